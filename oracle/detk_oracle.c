@@ -1,0 +1,187 @@
+/*
+ * detk_oracle.c -- plain CPU oracle for exact, bitwise-deterministic ragged top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU product path never
+ * calls it and shares no source, header or table with it.
+ *
+ * What it computes (the plain definition, written out):
+ *   SGLang PR #31115 "opt-in deterministic CuTe-DSL DSA top-k backend", PR summary
+ *   and "Modifications": the result is the canonical order -- score descending,
+ *   index ascending among bitwise-equal scores -- so the k-th boundary keeps the
+ *   smallest-index subset of its tie set; output is (B, topk) int32 local
+ *   indices, front-packed, padded with -1.
+ *   The same PR's hardening commit: the order is a bitwise total order on the
+ *   float bits (NaN is placed by its bits, not torch.topk's NaN-maximal rule),
+ *   and window clamps trust the row metadata.
+ *   docai.hu blog "Non-deterministic Qwen3.8-Flash-Next...", section "The price
+ *   of the fix": the exact result equals a full sort followed by truncation to k
+ *   and -1 padding when the row is shorter than k.
+ *
+ * Per row b:
+ *   n   = clamp(lengths[b], 0, max_len)        (lengths NULL: n = max_len)
+ *   s   = row_starts[b]                         (row_starts NULL: s = b * max_len)
+ *   key = the float's 32 bits mapped so that unsigned order is IEEE 754
+ *         totalOrder: a negative pattern (sign bit set) is complemented, a
+ *         positive pattern gets its sign bit set.
+ *   Sort positions 0..n-1 by (key descending, position ascending) with qsort --
+ *   sorting on that pair is exactly a stable sort on the key -- keep the first
+ *   m = min(k, n), write -1 / -inf after them.
+ *
+ * No floating-point operation ever touches a score: values are copied as bits.
+ * Rows are split over POSIX threads in contiguous blocks; each row is
+ * independent, so the thread count does not change the result.
+ */
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    uint32_t key;
+    int32_t pos;
+} oracle_item;
+
+/* IEEE 754 totalOrder as an unsigned key (see header). */
+static uint32_t oracle_total_order_key(uint32_t bits)
+{
+    if (bits & 0x80000000u)
+        return ~bits;
+    return bits | 0x80000000u;
+}
+
+/* (key descending, position ascending). */
+static int oracle_cmp(const void* pa, const void* pb)
+{
+    const oracle_item* a = (const oracle_item*)pa;
+    const oracle_item* b = (const oracle_item*)pb;
+    if (a->key != b->key)
+        return a->key > b->key ? -1 : 1;
+    if (a->pos != b->pos)
+        return a->pos < b->pos ? -1 : 1;
+    return 0;
+}
+
+typedef struct {
+    const uint32_t* scores;
+    const int32_t* row_starts;
+    const int32_t* lengths;
+    int32_t max_len;
+    int k;
+    int32_t* out_idx;
+    uint32_t* out_val;
+    int row_begin;
+    int row_end;
+    int status;
+} oracle_job;
+
+static void oracle_row(const oracle_job* job, int b, oracle_item* items)
+{
+    int64_t len = job->lengths ? job->lengths[b] : job->max_len;
+    if (len < 0)
+        len = 0;
+    if (len > job->max_len)
+        len = job->max_len;
+    int32_t n = (int32_t)len;
+    int64_t start = job->row_starts ? (int64_t)job->row_starts[b] : (int64_t)b * job->max_len;
+    const uint32_t* row = job->scores + start;
+
+    for (int32_t j = 0; j < n; ++j) {
+        items[j].key = oracle_total_order_key(row[j]);
+        items[j].pos = j;
+    }
+    qsort(items, (size_t)n, sizeof(oracle_item), oracle_cmp);
+
+    int32_t m = n < job->k ? n : job->k;
+    int32_t* oi = job->out_idx + (int64_t)b * job->k;
+    uint32_t* ov = job->out_val ? job->out_val + (int64_t)b * job->k : NULL;
+    for (int t = 0; t < job->k; ++t) {
+        if (t < m) {
+            oi[t] = items[t].pos;
+            if (ov)
+                ov[t] = row[items[t].pos];
+        } else {
+            oi[t] = -1;
+            if (ov)
+                ov[t] = 0xFF800000u; /* -inf in padded slots */
+        }
+    }
+}
+
+static void* oracle_worker(void* arg)
+{
+    oracle_job* job = (oracle_job*)arg;
+    if (job->row_begin >= job->row_end)
+        return NULL;
+    oracle_item* items = (oracle_item*)malloc(sizeof(oracle_item) * (size_t)(job->max_len > 0 ? job->max_len : 1));
+    if (!items) {
+        job->status = 1;
+        return NULL;
+    }
+    for (int b = job->row_begin; b < job->row_end; ++b)
+        oracle_row(job, b, items);
+    free(items);
+    return NULL;
+}
+
+/*
+ * Host pointers only.  scores: float32 bit patterns; out_val may be NULL.
+ * Returns 0 on success, 1 on bad arguments or allocation failure.
+ */
+int detk_oracle_topk_ragged(const uint32_t* scores, const int32_t* row_starts, const int32_t* lengths,
+                            int B, int32_t max_len, int k, int32_t* out_idx, uint32_t* out_val,
+                            int nthreads)
+{
+    if (B < 0 || k < 1 || max_len < 0 || !out_idx || (B > 0 && !scores))
+        return 1;
+    if (B == 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > B)
+        nthreads = B;
+
+    oracle_job* jobs = (oracle_job*)calloc((size_t)nthreads, sizeof(oracle_job));
+    pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return 1;
+    }
+    int per = B / nthreads, extra = B % nthreads, row = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        oracle_job* j = &jobs[t];
+        j->scores = scores;
+        j->row_starts = row_starts;
+        j->lengths = lengths;
+        j->max_len = max_len;
+        j->k = k;
+        j->out_idx = out_idx;
+        j->out_val = out_val;
+        j->row_begin = row;
+        row += per + (t < extra ? 1 : 0);
+        j->row_end = row;
+        j->status = 0;
+    }
+    int status = 0;
+    char* joined = (char*)calloc((size_t)nthreads, 1);
+    for (int t = 1; t < nthreads; ++t) {
+        if (joined && pthread_create(&tids[t], NULL, oracle_worker, &jobs[t]) == 0)
+            joined[t] = 1;
+        else
+            oracle_worker(&jobs[t]); /* could not start a thread: run the block here */
+    }
+    oracle_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t)
+        if (joined && joined[t])
+            pthread_join(tids[t], NULL);
+    for (int t = 0; t < nthreads; ++t)
+        status |= jobs[t].status;
+    free(joined);
+    free(jobs);
+    free(tids);
+    return status;
+}
+
+/* The key of one bit pattern, exported so tests can pin the mapping itself. */
+uint32_t detk_oracle_key(uint32_t bits) { return oracle_total_order_key(bits); }
