@@ -1,0 +1,155 @@
+"""Exact, bitwise-deterministic ragged top-k for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/detk.h`` (``libdetk.so``, built from
+``csrc/`` by :func:`deterministic_exact_top_amd.build.build_library`).  This module
+only marshals arguments: every step of the computation runs in the HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU fallback:
+if the library is missing or fails, calls raise.
+
+Operation: SGLang PR #31115 (PR summary, "Modifications", hardening commit) -- per
+row, the k highest scores in canonical order (score descending under the bitwise
+total order of the float bits, index ascending among bitwise-equal scores), local
+indices front-packed and padded with -1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "topk_ragged", "workspace_size", "can_implement", "status_string", "debug_set",
+    "workspace_error", "library_path", "load_library", "DETK_MAX_K", "DetkError",
+]
+
+DETK_MAX_K = 4096
+DETK_OK, DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, DETK_ERR_WORKSPACE, DETK_ERR_HIP = range(5)
+DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE = 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class DetkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s" % (what, status_string(status)))
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libdetk.so")
+
+
+def load_library():
+    """Load libdetk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError("libdetk.so is missing at %s; build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.detk_can_implement.argtypes = [ctypes.c_int, ctypes.c_int, i32]
+    lib.detk_can_implement.restype = ctypes.c_int
+    lib.detk_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32]
+    lib.detk_workspace_size.restype = sz
+    lib.detk_topk_ragged.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.detk_topk_ragged.restype = ctypes.c_int
+    lib.detk_status_string.argtypes = [ctypes.c_int]
+    lib.detk_status_string.restype = ctypes.c_char_p
+    lib.detk_workspace_error.argtypes = [vp, sz, vp]
+    lib.detk_workspace_error.restype = ctypes.c_int
+    lib.detk_debug_set.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.detk_debug_set.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().detk_status_string(int(status)).decode()
+
+
+def can_implement(k: int, max_len: int, device: int = 0) -> int:
+    return int(load_library().detk_can_implement(int(device), int(k), int(max_len)))
+
+
+def workspace_size(B: int, k: int, max_len: int, device: int = 0) -> int:
+    return int(load_library().detk_workspace_size(int(device), int(B), int(k), int(max_len)))
+
+
+def debug_set(what: int, value: int) -> None:
+    """Test-only overrides (see include/detk.h); they never change results."""
+    st = load_library().detk_debug_set(int(what), int(value))
+    if st != DETK_OK:
+        raise DetkError(st, "detk_debug_set")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_error(workspace, stream=None) -> int:
+    import torch
+    if workspace is None or workspace.numel() == 0:
+        return 0
+    s = stream if stream is not None else torch.cuda.current_stream(workspace.device)
+    return int(load_library().detk_workspace_error(_ptr(workspace), workspace.numel(), ctypes.c_void_p(s.cuda_stream)))
+
+
+def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: int | None = None,
+                out_idx=None, out_val=None, workspace=None, with_values: bool = True, B: int | None = None,
+                stream=None):
+    """Exact canonical top-k of each ragged row.
+
+    scores      float32 CUDA tensor, contiguous.  2-D (B, L): rows are the matrix rows
+                by default (row_starts None -> b * L, max_len defaults to L).  1-D:
+                a packed buffer; pass row_starts and max_len.
+    row_starts  int32 CUDA tensor (B,) of absolute element offsets, or None.
+    lengths     int32 CUDA tensor (B,), or None (every row max_len long).
+    k           1 <= k <= 4096.
+    max_len     host-known bound on every row length (never read from the device).
+    Returns (out_idx int32 (B, k), out_val float32 (B, k) or None).  All allocation
+    happens here, before the call, so a captured graph can reuse preallocated
+    out_idx / out_val / workspace passed in by the caller.
+    """
+    import torch
+    lib = load_library()
+    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 CUDA tensor")
+    if max_len is None:
+        if scores.dim() != 2:
+            raise ValueError("max_len is required unless scores is 2-D")
+        max_len = int(scores.shape[1])
+    if B is None:
+        if lengths is not None:
+            B = int(lengths.shape[0])
+        elif row_starts is not None:
+            B = int(row_starts.shape[0])
+        elif scores.dim() == 2:
+            B = int(scores.shape[0])
+        else:
+            raise ValueError("B cannot be inferred")
+    for name, t in (("row_starts", row_starts), ("lengths", lengths)):
+        if t is not None:
+            if t.dtype != torch.int32 or t.device != scores.device or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous int32 tensor on the scores' device" % name)
+            if t.shape[0] < B:
+                raise ValueError("%s has fewer than B entries" % name)
+    dev = scores.device
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if with_values and out_val is None:
+        out_val = torch.empty((B, k), dtype=torch.float32, device=dev)
+    need = lib.detk_workspace_size(dev.index if dev.index is not None else torch.cuda.current_device(),
+                                   int(B), int(k), int(max_len))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib.detk_topk_ragged(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len), int(k),
+                              _ptr(out_idx), _ptr(out_val) if with_values else None,
+                              _ptr(workspace) if need else None, int(workspace.numel()) if need else 0,
+                              ctypes.c_void_p(s.cuda_stream))
+    if st != DETK_OK:
+        raise DetkError(st, "detk_topk_ragged")
+    return out_idx, (out_val if with_values else None)

@@ -1,0 +1,314 @@
+// detk_api.hip -- host side of the C ABI declared in include/detk.h.
+//
+// Validates arguments on the host (nothing is launched on an error), picks the
+// launch shape from host-known sizes only (B, k, max_len, device properties) and
+// enqueues the kernels on the caller's stream.  No allocation, no synchronisation,
+// no device readback: a call can be captured into a HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "../../include/detk.h"
+#include "topk_device.hpp"
+
+namespace {
+
+using detk::Params;
+using detk::Smem;
+
+// Kernel shapes.  One-workgroup-per-row tiles (threads x elements per lane):
+//   4096 = 256 x 16, 8192 = 256 x 32, 16384 = 256 x 64, 32768 = 512 x 64.
+// Multi-workgroup rows use tiles of 4096 / 8192 / 16384 elements (256 threads).
+constexpr int kSingleMaxLen = 32768;
+
+struct DeviceInfo {
+    bool init = false;
+    bool gfx950 = false;
+    int cus = 0;
+    size_t max_lds = 0;
+    int multi_occ[3][2] = {};  // [tile index][kmax index] co-resident workgroups per CU
+};
+
+std::mutex g_mu;
+DeviceInfo g_dev[64];
+int g_force_path = 0;       // 0 auto, 1 single, 2 multi
+int g_stage_cap = -1;       // -1 default
+int g_multi_tile = 0;       // 0 default
+
+template <int NT, int EPT, int KMAX>
+constexpr size_t smem_bytes() {
+    return sizeof(Smem<NT, EPT, KMAX>);
+}
+
+template <int NT, int EPT, int KMAX, bool MULTI>
+hipError_t prepare_kernel() {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&detk::topk_ragged_kernel<NT, EPT, KMAX, MULTI>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_bytes<NT, EPT, KMAX>());
+}
+
+template <int NT, int EPT, int KMAX>
+int multi_occupancy() {
+    if (prepare_kernel<NT, EPT, KMAX, true>() != hipSuccess) return 0;
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void*>(&detk::topk_ragged_kernel<NT, EPT, KMAX, true>), NT,
+            smem_bytes<NT, EPT, KMAX>()) != hipSuccess)
+        return 0;
+    return blocks;
+}
+
+int device_info(int device, DeviceInfo* out) {
+    if (device < 0 || device >= 64) return DETK_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceInfo& d = g_dev[device];
+    if (!d.init) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return DETK_ERR_HIP;
+        if (cur != device && hipSetDevice(device) != hipSuccess) return DETK_ERR_HIP;
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, device);
+        if (e == hipSuccess) {
+            d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            d.cus = prop.multiProcessorCount;
+            d.max_lds = prop.sharedMemPerBlock;
+            d.multi_occ[0][0] = multi_occupancy<256, 16, 2048>();
+            d.multi_occ[0][1] = multi_occupancy<256, 16, 4096>();
+            d.multi_occ[1][0] = multi_occupancy<256, 32, 2048>();
+            d.multi_occ[1][1] = multi_occupancy<256, 32, 4096>();
+            d.multi_occ[2][0] = multi_occupancy<256, 64, 2048>();
+            d.multi_occ[2][1] = multi_occupancy<256, 64, 4096>();
+        }
+        if (cur != device) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return DETK_ERR_HIP;
+        d.init = true;
+    }
+    *out = d;
+    return DETK_OK;
+}
+
+struct Plan {
+    bool multi = false;
+    int tile = 0;         // elements per workgroup tile
+    int kmax = 2048;
+    int tiles_per_row = 1;
+    int grid = 0;
+    size_t lds = 0;
+    size_t ws_bytes = 0;
+    // workspace layout (bytes from the start)
+    size_t off_zero = 0, n_zero_words = 0, off_ecnt = 0, off_stage = 0;
+};
+
+size_t single_lds(int tile, int kmax) {
+    switch (tile) {
+    case 4096: return kmax == 2048 ? smem_bytes<256, 16, 2048>() : smem_bytes<256, 16, 4096>();
+    case 8192: return kmax == 2048 ? smem_bytes<256, 32, 2048>() : smem_bytes<256, 32, 4096>();
+    case 16384: return kmax == 2048 ? smem_bytes<256, 64, 2048>() : smem_bytes<256, 64, 4096>();
+    default: return kmax == 2048 ? smem_bytes<512, 64, 2048>() : smem_bytes<512, 64, 4096>();
+    }
+}
+
+int tile_index(int tile) { return tile == 4096 ? 0 : tile == 8192 ? 1 : 2; }
+
+// Decide the launch shape from host-known sizes only.
+int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
+    if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
+    if (k > DETK_MAX_K) return DETK_ERR_UNSUPPORTED;
+    if (!dev.gfx950) return DETK_ERR_UNSUPPORTED;
+    pl->kmax = k <= 2048 ? 2048 : 4096;
+    const int ki = pl->kmax == 2048 ? 0 : 1;
+
+    bool multi;
+    if (g_force_path == 1) {
+        if (max_len > kSingleMaxLen) return DETK_ERR_UNSUPPORTED;
+        multi = false;
+    } else if (g_force_path == 2) {
+        multi = true;
+    } else {
+        // One workgroup per row when the row fits a tile and the batch alone fills the
+        // chip; long rows, or few rows of moderate length, split over workgroups.
+        multi = max_len > kSingleMaxLen || (max_len > 8192 && (int64_t)B * 2 < dev.cus);
+    }
+    pl->multi = multi;
+    if (!multi) {
+        pl->tile = max_len <= 4096 ? 4096 : max_len <= 8192 ? 8192 : max_len <= 16384 ? 16384 : 32768;
+        pl->tiles_per_row = 1;
+        pl->grid = B;
+        pl->lds = single_lds(pl->tile, pl->kmax);
+        pl->ws_bytes = 0;
+    } else {
+        pl->tile = g_multi_tile ? g_multi_tile : 8192;
+        const int64_t tpr = max_len == 0 ? 1 : ((int64_t)max_len + pl->tile - 1) / pl->tile;
+        const int occ = dev.multi_occ[tile_index(pl->tile)][ki];
+        const int64_t capacity = (int64_t)occ * dev.cus;
+        if (occ <= 0 || tpr > capacity) return DETK_ERR_UNSUPPORTED;
+        pl->tiles_per_row = (int)tpr;
+        const int64_t items = (int64_t)B * tpr;
+        const int64_t rows_resident = capacity / tpr;
+        int64_t grid = rows_resident * tpr;
+        if (grid > items) grid = items;
+        pl->grid = (int)grid;
+        pl->lds = pl->tile == 4096   ? (ki ? smem_bytes<256, 16, 4096>() : smem_bytes<256, 16, 2048>())
+                  : pl->tile == 8192 ? (ki ? smem_bytes<256, 32, 4096>() : smem_bytes<256, 32, 2048>())
+                                     : (ki ? smem_bytes<256, 64, 4096>() : smem_bytes<256, 64, 2048>());
+        pl->n_zero_words = 1 + (size_t)B * detk::kRowZeroWords;
+        pl->off_zero = 0;
+        size_t off = pl->n_zero_words * 4;
+        off = (off + 255) & ~(size_t)255;
+        pl->off_ecnt = off;
+        off += (size_t)B * (size_t)tpr * 4;
+        off = (off + 255) & ~(size_t)255;
+        pl->off_stage = off;
+        off += (size_t)B * (size_t)k * 8;
+        pl->ws_bytes = off;
+    }
+    if (pl->lds > dev.max_lds) return DETK_ERR_UNSUPPORTED;
+    // int32 offsets: every window must be addressable with int32 row_starts + length.
+    if ((int64_t)B * k >= ((int64_t)1 << 31)) return DETK_ERR_UNSUPPORTED;
+    return DETK_OK;
+}
+
+template <int NT, int EPT, int KMAX, bool MULTI>
+hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
+    static bool attr_done = false;  // attribute set once per process (idempotent anyway)
+    if (!attr_done) {
+        hipError_t e = prepare_kernel<NT, EPT, KMAX, MULTI>();
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    hipLaunchKernelGGL((detk::topk_ragged_kernel<NT, EPT, KMAX, MULTI>), dim3(grid), dim3(NT), lds, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
+    const bool k2 = pl.kmax == 2048;
+    if (!pl.multi) {
+        switch (pl.tile) {
+        case 4096: return k2 ? launch<256, 16, 2048, false>(p, pl.grid, pl.lds, stream)
+                             : launch<256, 16, 4096, false>(p, pl.grid, pl.lds, stream);
+        case 8192: return k2 ? launch<256, 32, 2048, false>(p, pl.grid, pl.lds, stream)
+                             : launch<256, 32, 4096, false>(p, pl.grid, pl.lds, stream);
+        case 16384: return k2 ? launch<256, 64, 2048, false>(p, pl.grid, pl.lds, stream)
+                              : launch<256, 64, 4096, false>(p, pl.grid, pl.lds, stream);
+        default: return k2 ? launch<512, 64, 2048, false>(p, pl.grid, pl.lds, stream)
+                           : launch<512, 64, 4096, false>(p, pl.grid, pl.lds, stream);
+        }
+    }
+    switch (pl.tile) {
+    case 4096: return k2 ? launch<256, 16, 2048, true>(p, pl.grid, pl.lds, stream)
+                         : launch<256, 16, 4096, true>(p, pl.grid, pl.lds, stream);
+    case 8192: return k2 ? launch<256, 32, 2048, true>(p, pl.grid, pl.lds, stream)
+                         : launch<256, 32, 4096, true>(p, pl.grid, pl.lds, stream);
+    default: return k2 ? launch<256, 64, 2048, true>(p, pl.grid, pl.lds, stream)
+                       : launch<256, 64, 4096, true>(p, pl.grid, pl.lds, stream);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int detk_can_implement(int device, int k, int32_t max_len) {
+    DeviceInfo dev;
+    int st = device_info(device, &dev);
+    if (st != DETK_OK) return st;
+    Plan pl;
+    return make_plan(dev, 1, k, max_len, &pl);
+}
+
+size_t detk_workspace_size(int device, int B, int k, int32_t max_len) {
+    DeviceInfo dev;
+    if (device_info(device, &dev) != DETK_OK) return 0;
+    Plan pl;
+    if (make_plan(dev, B, k, max_len, &pl) != DETK_OK) return 0;
+    return B == 0 ? 0 : pl.ws_bytes;
+}
+
+int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
+                     int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
+                     size_t workspace_bytes, void* stream_ptr) {
+    if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
+    if (B > 0 && (!scores || !out_idx)) return DETK_ERR_INVALID_ARG;
+    if (k > DETK_MAX_K) return DETK_ERR_UNSUPPORTED;
+    if (B == 0) return DETK_OK;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return DETK_ERR_HIP;
+    DeviceInfo dev;
+    int st = device_info(device, &dev);
+    if (st != DETK_OK) return st;
+    Plan pl;
+    st = make_plan(dev, B, k, max_len, &pl);
+    if (st != DETK_OK) return st;
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return DETK_ERR_WORKSPACE;
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    Params p;
+    p.scores = reinterpret_cast<const uint32_t*>(scores);
+    p.row_starts = row_starts;
+    p.lengths = lengths;
+    p.B = B;
+    p.max_len = max_len;
+    p.k = k;
+    p.tiles_per_row = pl.tiles_per_row;
+    p.stage_cap = g_stage_cap < 0 ? detk::kStageCap : (g_stage_cap > detk::kStageCap ? detk::kStageCap : g_stage_cap);
+    p.out_idx = out_idx;
+    p.out_val = reinterpret_cast<uint32_t*>(out_val);
+    p.ws_zero = nullptr;
+    p.ws_ecnt = nullptr;
+    p.ws_stage = nullptr;
+    if (pl.multi) {
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        p.ws_zero = reinterpret_cast<uint32_t*>(ws + pl.off_zero);
+        p.ws_ecnt = reinterpret_cast<uint32_t*>(ws + pl.off_ecnt);
+        p.ws_stage = reinterpret_cast<uint64_t*>(ws + pl.off_stage);
+        const int64_t nz = (int64_t)pl.n_zero_words;
+        int zgrid = (int)((nz + 255) / 256);
+        if (zgrid > 1024) zgrid = 1024;
+        hipLaunchKernelGGL(detk::zero_words_kernel, dim3(zgrid), dim3(256), 0, stream, p.ws_zero, nz);
+        if (hipGetLastError() != hipSuccess) return DETK_ERR_HIP;
+    }
+    if (dispatch(pl, p, stream) != hipSuccess) return DETK_ERR_HIP;
+    return DETK_OK;
+}
+
+const char* detk_status_string(int status) {
+    switch (status) {
+    case DETK_OK: return "DETK_OK";
+    case DETK_ERR_INVALID_ARG: return "DETK_ERR_INVALID_ARG: null pointer, B < 0, k < 1 or max_len < 0";
+    case DETK_ERR_UNSUPPORTED:
+        return "DETK_ERR_UNSUPPORTED: k > 4096, device is not gfx950, or the row is too long for the "
+               "co-resident multi-workgroup path";
+    case DETK_ERR_WORKSPACE: return "DETK_ERR_WORKSPACE: workspace missing or smaller than detk_workspace_size()";
+    case DETK_ERR_HIP: return "DETK_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown detk status";
+    }
+}
+
+int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* stream_ptr) {
+    if (!workspace || workspace_bytes < 4) return 0;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    if (hipStreamSynchronize(stream) != hipSuccess) return -1;
+    uint32_t word = 0;
+    if (hipMemcpy(&word, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+    return (int)word;
+}
+
+int detk_debug_set(int what, int value) {
+    switch (what) {
+    case DETK_DEBUG_PATH:
+        if (value < 0 || value > 2) return DETK_ERR_INVALID_ARG;
+        g_force_path = value;
+        return DETK_OK;
+    case DETK_DEBUG_STAGING_CAP:
+        if (value < -1) return DETK_ERR_INVALID_ARG;
+        g_stage_cap = value;
+        return DETK_OK;
+    case DETK_DEBUG_MULTI_TILE:
+        if (value != 0 && value != 4096 && value != 8192 && value != 16384) return DETK_ERR_INVALID_ARG;
+        g_multi_tile = value;
+        return DETK_OK;
+    default: return DETK_ERR_INVALID_ARG;
+    }
+}
+
+}  // extern "C"

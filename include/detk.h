@@ -1,0 +1,127 @@
+/*
+ * detk.h -- exact, bitwise-deterministic ragged top-k on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (SGLang PR #31115 "opt-in deterministic CuTe-DSL DSA top-k backend":
+ * PR summary, "Modifications" and the hardening commit; docai.hu blog
+ * "Non-deterministic Qwen3.8-Flash-Next...", section "The price of the fix"):
+ *
+ *   For each row b of a ragged batch of float32 scores, return the k highest
+ *   entries of the row's window in one canonical order: score descending under
+ *   the bitwise total order of the float bits (IEEE 754 totalOrder: +NaN above
+ *   +inf, -0.0 below +0.0, -NaN below -inf; NaNs placed by their bits), then index
+ *   ascending among bitwise-equal scores.  At the k-th boundary the tie set
+ *   therefore contributes its smallest indices.  Indices are local to the window
+ *   (0 <= j < n_b), front-packed; slots past min(k, n_b) hold -1.  The result is a
+ *   pure function of the row's bits and k: identical across runs, streams, batch
+ *   compositions and graph replays.
+ *
+ * All entry points are plain C.  Pointers named "device" are HIP device pointers
+ * owned by the caller; the library never frees or retains them.
+ */
+#ifndef DETK_H
+#define DETK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+    DETK_OK = 0,
+    DETK_ERR_INVALID_ARG = 1, /* NULL required pointer, B < 0, k < 1, max_len < 0       */
+    DETK_ERR_UNSUPPORTED = 2, /* k > DETK_MAX_K, device not gfx950, row too long for the */
+                              /* co-resident multi-workgroup path, int32 offset overflow  */
+    DETK_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than detk_workspace_size()     */
+    DETK_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed               */
+} detk_status;
+
+/* Largest k supported.  The pages' deterministic backend envelope is topk <= 4096
+ * (SGLang PR #31115, "Modifications" and hardening commit). */
+#define DETK_MAX_K 4096
+
+/*
+ * detk_can_implement -- host-only capability query, no launch.
+ * Returns DETK_OK when a call with this k and max_len can run on `device`, else the
+ * status such a call would return.  Meant for construction time, so an unsupported
+ * configuration is found before the first batch (the failure mode reported in vLLM
+ * PR #55872's GB10 trace, where the check fired only inside warmup).
+ */
+int detk_can_implement(int device, int k, int32_t max_len);
+
+/*
+ * detk_workspace_size -- bytes of device workspace a call with these arguments needs
+ * (0 when every row fits one workgroup).  The same value for the same (device, B, k,
+ * max_len) in one process.
+ */
+size_t detk_workspace_size(int device, int B, int k, int32_t max_len);
+
+/*
+ * detk_topk_ragged -- the operation above, enqueued on `stream`.
+ *
+ *   scores      device, float32.  Row b's window is
+ *               scores[s_b .. s_b + n_b) with s_b = row_starts[b] (or b * max_len
+ *               when row_starts is NULL, i.e. a dense (B, max_len) matrix) and
+ *               n_b = clamp(lengths[b], 0, max_len) (max_len when lengths is NULL).
+ *               Metadata is trusted, as in the pages' backend: the windows must lie
+ *               inside the allocation; the library does not check them.
+ *   row_starts  device int32[B] absolute element offsets, or NULL.
+ *   lengths     device int32[B], or NULL.
+ *   B           rows (0 returns DETK_OK without launching anything).
+ *   max_len     host-known upper bound of every n_b; fixes the launch shape so the
+ *               call never reads device metadata on the host.
+ *   k           1 <= k <= DETK_MAX_K.
+ *   out_idx     device int32[B * k], row-major: local indices, -1 after min(k, n_b).
+ *   out_val     device float32[B * k] or NULL: the selected scores' exact bits
+ *               (NaN payloads and -0.0 preserved; no floating-point op touches them),
+ *               -inf in padded slots.
+ *   workspace   device, at least detk_workspace_size() bytes (may be NULL when that
+ *               is 0).  Scratch owned by the caller; contents need no initialisation
+ *               and are undefined after the call.  Calls that share one workspace
+ *               must be ordered (same stream, or synchronised).
+ *   stream      hipStream_t (NULL = default stream).
+ *
+ * The call allocates nothing, never synchronises and reads no device memory on the
+ * host, so it can be captured into a HIP graph.  Argument errors are detected on
+ * the host before any launch and leave every output untouched.
+ */
+int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
+                     int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* detk_status_string(int status);
+
+/*
+ * detk_workspace_error -- DEBUG.  Synchronises `stream` and returns the error word the
+ * last call on this workspace left behind: 0 when clean, non-zero when a
+ * multi-workgroup row barrier gave up after its bounded wait (outputs of that call
+ * are then undefined).  Not capturable.
+ */
+int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * detk_debug_set -- TEST-ONLY process-wide overrides (not thread-safe; set them before
+ * issuing calls).  Every override changes only how the result is computed, never the
+ * result.
+ *   what = DETK_DEBUG_PATH:        0 automatic, 1 one workgroup per row, 2 several
+ *                                  workgroups per row (co-operating through workspace).
+ *   what = DETK_DEBUG_STAGING_CAP: -1 default; else the largest threshold-bin
+ *                                  candidate count staged in LDS (0 forces every
+ *                                  refinement pass to rescan the register-resident row).
+ *   what = DETK_DEBUG_MULTI_TILE:  0 default; else elements per workgroup tile of the
+ *                                  multi-workgroup path (4096, 8192 or 16384).
+ * Returns DETK_OK or DETK_ERR_INVALID_ARG.
+ */
+#define DETK_DEBUG_PATH 1
+#define DETK_DEBUG_STAGING_CAP 2
+#define DETK_DEBUG_MULTI_TILE 3
+int detk_debug_set(int what, int value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETK_H */

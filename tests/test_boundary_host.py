@@ -1,0 +1,70 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports every
+symbol include/detk.h declares, and rejects bad arguments before touching HIP."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_exact_top_amd as detk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "detk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(detk_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(detk.library_path()):
+        from deterministic_exact_top_amd.build import build_library
+        build_library(force=True)
+    return detk.load_library()
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("detk_topk_ragged", "detk_workspace_size", "detk_can_implement", "detk_status_string",
+              "detk_workspace_error", "detk_debug_set"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(detk.library_path())
+    for name in _declared():
+        assert hasattr(raw, name), "libdetk.so does not export %s" % name
+
+
+def test_argument_errors_before_any_launch(lib):
+    vp = ctypes.c_void_p
+    dummy = vp(0x1000)  # never dereferenced: every case below fails (or returns) first
+    call = lambda scores, B, max_len, k, out: lib.detk_topk_ragged(scores, None, None, B, max_len, k, out, None,
+                                                                   None, 0, None)
+    assert call(dummy, -1, 10, 5, dummy) == detk.DETK_ERR_INVALID_ARG
+    assert call(dummy, 3, -1, 5, dummy) == detk.DETK_ERR_INVALID_ARG
+    assert call(dummy, 3, 10, 0, dummy) == detk.DETK_ERR_INVALID_ARG
+    assert call(None, 3, 10, 5, dummy) == detk.DETK_ERR_INVALID_ARG
+    assert call(dummy, 3, 10, 5, None) == detk.DETK_ERR_INVALID_ARG
+    assert call(dummy, 3, 10, 4097, dummy) == detk.DETK_ERR_UNSUPPORTED
+    assert call(None, 0, 10, 5, None) == detk.DETK_OK  # empty batch: nothing to do
+
+
+def test_status_strings_and_debug_overrides(lib):
+    for st in range(5):
+        assert detk.status_string(st).startswith("DETK_")
+    assert "unknown" in detk.status_string(99)
+    assert lib.detk_debug_set(1, 3) == detk.DETK_ERR_INVALID_ARG
+    assert lib.detk_debug_set(2, -2) == detk.DETK_ERR_INVALID_ARG
+    assert lib.detk_debug_set(3, 5000) == detk.DETK_ERR_INVALID_ARG
+    assert lib.detk_debug_set(42, 0) == detk.DETK_ERR_INVALID_ARG
+    for what, val in ((1, 2), (1, 0), (2, 0), (2, -1), (3, 4096), (3, 0)):
+        assert lib.detk_debug_set(what, val) == detk.DETK_OK
+
+
+def test_workspace_error_on_null_workspace(lib):
+    assert lib.detk_workspace_error(None, 0, None) == 0

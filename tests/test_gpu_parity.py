@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path against the CPU oracle, bit for bit (indices and value bits).
+
+Covers both launch shapes (one workgroup per row; several workgroups per row meeting
+through the workspace), the LDS-staged and the rescan (staging overflow) refinement,
+every named workload at full size (the 8192-row prefill workload on sampled rows plus
+whole-batch properties), edge rows, unaligned packed rows, the boundary's error codes.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import deterministic_exact_top_amd as detk
+import workloads as W
+from gpu_util import assert_same, debug_overrides, log, run_gpu, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    detk.load_library()
+    return torch.device("cuda:0")
+
+
+def _examples():
+    import test_oracle_pins as pins
+    return pins._examples()
+
+
+def test_worked_examples(dev):
+    import torch
+    for row, k, idx, val in _examples():
+        n = row.size
+        buf = torch.from_numpy((row if n else np.zeros(1, np.uint32)).view(np.float32)).to(dev)
+        rs = torch.zeros(1, dtype=torch.int32, device=dev)
+        ln = torch.full((1,), n, dtype=torch.int32, device=dev)
+        for path in (1, 2):
+            with debug_overrides(path=path, multi_tile=4096):
+                gi, gv = detk.topk_ragged(buf, rs, ln, k, max_len=max(n, 1))
+                torch.cuda.synchronize()
+            assert gi.cpu().numpy()[0].tolist() == idx, (row, k, path)
+            assert gv.cpu().numpy().view(np.uint32)[0].tolist() == val, (row, k, path)
+
+
+SMALL = {
+    "plateau": lambda: W.plateau_abs(B=6, L=4096, k=2048, name="gpu_plateau"),
+    "decode_ragged": lambda: W.decode_ragged(B=24, n_lo=1, n_hi=20000, k=2048, name="gpu_decode"),
+    "prefill_causal": lambda: W.prefill_causal(Q=160, ctx=9000, k=2048, name="gpu_prefill"),
+    "narrow": lambda: W.narrow_range(B=6, L=30000, k=4096, name="gpu_narrow"),
+    "long_context": lambda: W.long_context(B=5, L=40000, k=2048, short_n=1500, name="gpu_long"),
+    "small_k": lambda: W.decode_ragged(B=16, n_lo=1, n_hi=6000, k=7, name="gpu_smallk"),
+    "k_not_pow2": lambda: W.decode_ragged(B=16, n_lo=1, n_hi=12000, k=3000, name="gpu_k3000"),
+}
+_SMALL_CACHE = {}
+
+
+def _small(name):
+    if name not in _SMALL_CACHE:
+        _SMALL_CACHE[name] = SMALL[name]()
+    return _SMALL_CACHE[name]
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("shape", ["auto", "single", "multi4096", "multi8192", "single_rescan", "multi_rescan",
+                                   "multi_tinystage"])
+def test_small_workloads(dev, name, shape):
+    wl = _small(name)
+    if shape.startswith("single") and wl.max_len > 32768:
+        pytest.skip("row longer than one workgroup tile")
+    cfg = {
+        "auto": {},
+        "single": {"path": 1},
+        "multi4096": {"path": 2, "multi_tile": 4096},
+        "multi8192": {"path": 2, "multi_tile": 8192},
+        "single_rescan": {"path": 1, "stage_cap": 0},
+        "multi_rescan": {"path": 2, "multi_tile": 4096, "stage_cap": 0},
+        "multi_tinystage": {"path": 2, "multi_tile": 4096, "stage_cap": 3},
+    }[shape]
+    log("small workload %s shape %s B=%d max_len=%d k=%d" % (name, shape, wl.B, wl.max_len, wl.k))
+    with debug_overrides(**cfg):
+        gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, "%s/%s" % (name, shape))
+
+
+@pytest.mark.parametrize("name", ["plateau_4x4096", "decode_ragged_64", "narrow_128x65536", "long_context_8x262144"])
+def test_full_workload_exact(dev, name):
+    wl = W.full(name)
+    log("full workload %s B=%d max_len=%d k=%d" % (name, wl.B, wl.max_len, wl.k))
+    gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, name)
+
+
+@pytest.mark.parametrize("name", ["decode_ragged_64", "long_context_8x262144"])
+def test_full_workload_forced_rescan(dev, name):
+    wl = W.full(name)
+    log("full workload %s, staging disabled (every refinement pass rescans)" % name)
+    with debug_overrides(stage_cap=0):
+        gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, name + "/rescan")
+
+
+_PREFILL = {}
+
+
+def _prefill():
+    if "wl" not in _PREFILL:
+        _PREFILL["wl"] = W.full("prefill_causal_8192x16384")
+    return _PREFILL["wl"]
+
+
+def test_full_prefill_sampled_rows_and_batch_properties(dev):
+    """The 8192 x 16384 causal prefill workload in the benchmark's launch shape:
+    exact parity on sampled rows, plus properties of every row."""
+    wl = _prefill()
+    log("full prefill workload: GPU run")
+    gi, gv = run_gpu(wl, dev)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(wl.B - 32, wl.B),
+                                     rng.choice(wl.B, 192, replace=False)]))
+    log("full prefill workload: oracle on %d sampled rows" % rows.size)
+    oi, ov = run_oracle(wl, rows)
+    assert_same(gi[rows], gv[rows], oi, ov, "prefill sampled rows")
+    # Every row: indices inside the window, unique, values are the input bits.
+    n = wl.lengths.astype(np.int64)
+    assert np.all(gi >= 0) and np.all(gi < n[:, None])
+    srt = np.sort(gi, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])
+    u = wl.scores.view(np.uint32)
+    assert np.array_equal(u[wl.row_starts.astype(np.int64)[:, None] + gi], gv)
+    # Canonical order: keys non-increasing along every row.
+    key = np.where(gv >> 31 == 1, ~gv, gv | np.uint32(0x80000000)).astype(np.uint32)
+    assert np.all(key[:, 1:] <= key[:, :-1])
+
+
+def _edge_workload(L, k, lens, name):
+    rng = np.random.default_rng(W.seed_of(name))
+    B = len(lens)
+    buf = np.empty(B * L, np.float32)
+    for b in range(B):
+        buf[b * L:(b + 1) * L] = W.relu_sum_mixture(rng, L, 0.7)
+    return W.Workload(name, buf, (np.arange(B) * L).astype(np.int32), np.array(lens, np.int32), L, k)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_edge_lengths(dev, path):
+    k = 2048
+    L = 16384
+    lens = [0, 1, 2, k - 1, k, k + 1, 4095, 4096, 4097, 8191, 8192, 8193, 16383, 16384, -3, 99999]
+    wl = _edge_workload(L, k, lens, "edge")
+    log("edge lengths path %d" % path)
+    with debug_overrides(path=path, multi_tile=4096):
+        gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, "edge lengths path %d" % path)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_unaligned_packed_rows(dev, path):
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 9000, 40).astype(np.int32)
+    starts = (np.cumsum(np.concatenate([[3], lens[:-1] + rng.integers(0, 5, 39)]))).astype(np.int32)
+    total = int(starts[-1] + lens[-1] + 7)
+    buf = np.full(total, W.QNAN, np.uint32).view(np.float32)
+    for b in range(lens.size):
+        buf[starts[b]:starts[b] + lens[b]] = W.relu_sum_mixture(rng, int(lens[b]), 0.5)
+    wl = W.Workload("unaligned", buf, starts, lens, 9000, 1000)
+    log("unaligned packed rows path %d" % path)
+    with debug_overrides(path=path, multi_tile=4096):
+        gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, "unaligned path %d" % path)
+
+
+def test_default_metadata_and_no_values(dev):
+    import torch
+    wl = W.plateau_abs(B=5, L=3000, k=1000, name="dense_default")
+    m2 = torch.from_numpy(wl.scores.reshape(5, 3000)).to(dev)
+    gi, _ = detk.topk_ragged(m2, None, None, 1000, with_values=False)
+    gi2, gv2 = detk.topk_ragged(m2, None, None, 1000)
+    torch.cuda.synchronize()
+    oi, ov = run_oracle(wl)
+    assert np.array_equal(gi.cpu().numpy(), oi)
+    assert np.array_equal(gi2.cpu().numpy(), oi)
+    assert np.array_equal(gv2.cpu().numpy().view(np.uint32), ov)
+
+
+def test_many_rows_persistent_multi(dev):
+    """More (row, tile) items than co-resident workgroups: the multi-workgroup grid
+    loops over rounds of whole rows."""
+    wl = W.decode_ragged(B=1500, n_lo=1, n_hi=9000, k=512, name="gpu_many_rows")
+    log("many rows, multi path with 4096 tiles")
+    with debug_overrides(path=2, multi_tile=4096):
+        gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, "many rows multi")
+
+
+def test_error_codes(dev):
+    import torch
+    lib = detk.load_library()
+    x = torch.zeros(4, 100, device=dev)
+    idx = torch.empty(4, 10, dtype=torch.int32, device=dev)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = ctypes.c_void_p
+    call = lambda scores, B, max_len, k, out, ws=None, wsb=0: lib.detk_topk_ragged(
+        scores, None, None, B, max_len, k, out, None, ws, wsb, s)
+    assert call(p(x.data_ptr()), 4, 100, 0, p(idx.data_ptr())) == detk.DETK_ERR_INVALID_ARG
+    assert call(p(x.data_ptr()), -1, 100, 10, p(idx.data_ptr())) == detk.DETK_ERR_INVALID_ARG
+    assert call(p(x.data_ptr()), 4, -1, 10, p(idx.data_ptr())) == detk.DETK_ERR_INVALID_ARG
+    assert call(None, 4, 100, 10, p(idx.data_ptr())) == detk.DETK_ERR_INVALID_ARG
+    assert call(p(x.data_ptr()), 4, 100, 10, None) == detk.DETK_ERR_INVALID_ARG
+    assert call(p(x.data_ptr()), 4, 100, 4097, p(idx.data_ptr())) == detk.DETK_ERR_UNSUPPORTED
+    assert call(None, 0, 100, 10, None) == detk.DETK_OK
+    # a multi-workgroup shape needs workspace
+    big = torch.zeros(2, 300000, device=dev)
+    out = torch.empty(2, 16, dtype=torch.int32, device=dev)
+    need = detk.workspace_size(2, 16, 300000)
+    assert need > 0
+    assert lib.detk_topk_ragged(p(big.data_ptr()), None, None, 2, 300000, 16, p(out.data_ptr()), None, None, 0,
+                                s) == detk.DETK_ERR_WORKSPACE
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    assert lib.detk_topk_ragged(p(big.data_ptr()), None, None, 2, 300000, 16, p(out.data_ptr()), None,
+                                p(ws.data_ptr()), need - 1, s) == detk.DETK_ERR_WORKSPACE
+    assert lib.detk_topk_ragged(p(big.data_ptr()), None, None, 2, 300000, 16, p(out.data_ptr()), None,
+                                p(ws.data_ptr()), need, s) == detk.DETK_OK
+    torch.cuda.synchronize()
+    assert detk.workspace_error(ws) == 0
+    assert np.array_equal(out.cpu().numpy(), np.tile(np.arange(16, dtype=np.int32), (2, 1)))
+    assert detk.can_implement(2048, 262144) == detk.DETK_OK
+    assert detk.can_implement(4097, 10) == detk.DETK_ERR_UNSUPPORTED

@@ -1,0 +1,165 @@
+"""GPU determinism: byte-identical output across repeated runs, batch compositions,
+a busy sibling stream and HIP-graph replay.
+
+The pages find races by replaying identical input many times while other work
+perturbs scheduling (SGLang PR #31115, "Accuracy Tests": 30 repetitions with a busy
+sibling stream; review-thread tie-safety harness) and require graph replay to equal
+eager execution bitwise (PR "Modifications").  The selected set must be a pure
+function of the input across batch compositions (review thread).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import deterministic_exact_top_amd as detk
+import workloads as W
+from gpu_util import assert_same, debug_overrides, log, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    detk.load_library()
+    return torch.device("cuda:0")
+
+
+REPLAY = {
+    "plateau": lambda: W.full("plateau_4x4096"),
+    "decode_ragged": lambda: W.full("decode_ragged_64"),
+    "long_context": lambda: W.full("long_context_8x262144"),
+    "narrow_small": lambda: W.narrow_range(B=16, L=65536, k=4096, name="replay_narrow"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REPLAY))
+def test_twenty_runs_identical(dev, name):
+    import torch
+    wl = REPLAY[name]()
+    scores, rs, ln = to_dev(wl, dev)
+    log("replay x20: %s" % name)
+    ref = None
+    for _ in range(20):
+        gi, gv = detk.topk_ragged(scores, rs, ln, wl.k, max_len=wl.max_len)
+        torch.cuda.synchronize()
+        cur = (gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32))
+        if ref is None:
+            ref = cur
+            oi, ov = run_oracle(wl)
+            assert_same(cur[0], cur[1], oi, ov, name)
+        else:
+            assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
+
+
+def test_batch_composition_invariance(dev):
+    """A row's output does not depend on which other rows share the call, their
+    order, or the launch shape chosen for the batch."""
+    import torch
+    a = W.decode_ragged(B=24, n_lo=1, n_hi=30000, k=2048, name="comp_a")
+    bwl = W.long_context(B=3, L=300000, k=2048, short_n=1700, name="comp_b")
+    # One packed buffer holding both workloads' rows.
+    buf = np.concatenate([a.scores, bwl.scores])
+    starts = np.concatenate([a.row_starts.astype(np.int64), bwl.row_starts.astype(np.int64) + a.scores.size])
+    lens = np.concatenate([a.lengths, bwl.lengths]).astype(np.int32)
+    B = lens.size
+    d_buf = torch.from_numpy(buf).to(dev)
+    oi, ov = detk_oracle_rows(buf, starts, lens, 2048, 300000)
+
+    def run(order):
+        rs = torch.from_numpy(starts[order].astype(np.int32)).to(dev)
+        ln = torch.from_numpy(lens[order]).to(dev)
+        gi, gv = detk.topk_ragged(d_buf, rs, ln, 2048, max_len=300000)
+        torch.cuda.synchronize()
+        return gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32)
+
+    rng = np.random.default_rng(4)
+    orders = [np.arange(B), np.arange(B)[::-1].copy(), rng.permutation(B)]
+    for order in orders:
+        log("composition order %s" % order[:6])
+        gi, gv = run(order)
+        assert_same(gi, gv, oi[order], ov[order], "composition")
+    # each row alone, with the short-row launch shape where it fits one workgroup
+    for b in (0, 5, B - 3, B - 2, B - 1):
+        rs = torch.tensor([int(starts[b])], dtype=torch.int32, device=dev)
+        ln = torch.tensor([int(lens[b])], dtype=torch.int32, device=dev)
+        ml = int(max(lens[b], 1))
+        gi, gv = detk.topk_ragged(d_buf, rs, ln, 2048, max_len=ml)
+        torch.cuda.synchronize()
+        assert np.array_equal(gi.cpu().numpy()[0], oi[b]) and np.array_equal(
+            gv.cpu().numpy().view(np.uint32)[0], ov[b]), "row %d alone" % b
+
+
+def detk_oracle_rows(buf, starts, lens, k, max_len):
+    import oracle
+    return oracle.topk_ragged(buf, starts.astype(np.int32), lens, k, max_len)
+
+
+def test_busy_sibling_stream(dev):
+    """Replays while another stream runs large matmuls that compete for the CUs."""
+    import torch
+    wl = W.full("long_context_8x262144")
+    scores, rs, ln = to_dev(wl, dev)
+    oi, ov = run_oracle(wl)
+    side = torch.cuda.Stream()
+    a = torch.randn(2048, 2048, device=dev)
+    log("busy sibling stream replay")
+    for rep in range(10):
+        with torch.cuda.stream(side):
+            for _ in range(4):
+                a = (a @ a).clamp_(-1, 1)
+        gi, gv = detk.topk_ragged(scores, rs, ln, wl.k, max_len=wl.max_len)
+        torch.cuda.synchronize()
+        assert_same(gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32), oi, ov, "busy rep %d" % rep)
+
+
+@pytest.mark.parametrize("shape", ["single", "multi"])
+def test_hip_graph_replay_matches_eager(dev, shape):
+    """Capture one call into a HIP graph (through torch.cuda.graph), replay it on new
+    inputs copied into the captured buffers, and check every replay against an eager
+    call on the same input."""
+    import torch
+    if shape == "single":
+        mk = lambda i: W.decode_ragged(B=32, n_lo=3000, n_hi=16000, k=2048, name="graph_%d" % i)
+        max_len = 16000
+    else:
+        mk = lambda i: W.long_context(B=4, L=100000, k=2048, short_n=1234, name="graph_m%d" % i)
+        max_len = 100000
+    wls = [mk(i) for i in range(4)]
+    size = max(w.scores.size for w in wls)
+    B = wls[0].B
+    s_buf = torch.zeros(size, device=dev)
+    s_rs = torch.zeros(B, dtype=torch.int32, device=dev)
+    s_ln = torch.zeros(B, dtype=torch.int32, device=dev)
+    out_i = torch.empty(B, 2048, dtype=torch.int32, device=dev)
+    out_v = torch.empty(B, 2048, device=dev)
+    need = detk.workspace_size(B, 2048, max_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def load(w):
+        s_buf[:w.scores.size].copy_(torch.from_numpy(w.scores))
+        s_rs.copy_(torch.from_numpy(w.row_starts))
+        s_ln.copy_(torch.from_numpy(w.lengths))
+
+    load(wls[0])
+    # eager warmup on a side stream, then capture
+    detk.topk_ragged(s_buf, s_rs, s_ln, 2048, max_len=max_len, out_idx=out_i, out_val=out_v, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        detk.topk_ragged(s_buf, s_rs, s_ln, 2048, max_len=max_len, out_idx=out_i, out_val=out_v, workspace=ws)
+    torch.cuda.synchronize()
+    for rep, w in enumerate(wls + wls[::-1]):
+        load(w)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        gi, gv = out_i.cpu().numpy().copy(), out_v.cpu().numpy().view(np.uint32).copy()
+        ei, ev = detk.topk_ragged(s_buf, s_rs, s_ln, 2048, max_len=max_len)
+        torch.cuda.synchronize()
+        assert np.array_equal(gi, ei.cpu().numpy()), "replay %d idx" % rep
+        assert np.array_equal(gv, ev.cpu().numpy().view(np.uint32)), "replay %d val" % rep
+        oi, ov = run_oracle(w)
+        assert_same(gi, gv, oi, ov, "graph replay %d" % rep)
