@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark: exact, bitwise-deterministic ragged top-k on one MI355X.
+
+One step = one detk_topk_ragged call over the whole batch of the chosen synthetic
+workload (default: the chunked-prefill causal indexer, 8192 query rows over a 16384
+token context, row i window [0, 8192 + i], k = 2048, 0.0-plateau / ReLU-sum scores
+with plateau fraction 0.7).  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line with rows/s (value), score GB/s, the roofline object of the
+dominant kernel (algorithmic bytes / event-timed launch duration, against the 8 TB/s
+HBM peak) and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "ragged top-k rows/s and score GB/s (% of HBM peak), k=2048, 1 GPU"
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in ("detk_api.hip", "topk_device.hpp"):
+        with open(os.path.join(ROOT, "deterministic_exact_top_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def time_gpu(wl, steps, warmup, rotate):
+    import torch
+    import deterministic_exact_top_amd as detk
+
+    dev = torch.device("cuda:0")
+    copies = []
+    for _ in range(rotate):
+        copies.append(torch.from_numpy(wl.scores).to(dev))
+    rs = torch.from_numpy(wl.row_starts).to(dev)
+    ln = torch.from_numpy(wl.lengths).to(dev)
+    out_i = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
+    out_v = torch.empty((wl.B, wl.k), dtype=torch.float32, device=dev)
+    need = detk.workspace_size(wl.B, wl.k, wl.max_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        detk.topk_ragged(copies[i % rotate], rs, ln, wl.k, max_len=wl.max_len, out_idx=out_i, out_val=out_v,
+                         workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Per-launch durations, with events recorded on the stream the kernels run on.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, launch_ms, need
+
+
+def cpu_baseline(wl, budget_s: float = 15.0):
+    """The oracle as it stands, on the host cores, over rows of the same workload."""
+    import oracle
+    threads = cpu_threads()
+    # Calibrate on a small slice, then size the sample to ~budget_s of CPU work.
+    probe = min(wl.B, 64)
+    t0 = time.perf_counter()
+    oracle.topk_ragged(wl.scores, wl.row_starts[:probe], wl.lengths[:probe], wl.k, wl.max_len, threads=1)
+    per_row_cpu = (time.perf_counter() - t0) / probe
+    rows = int(min(wl.B, max(probe, budget_s / max(per_row_cpu, 1e-9))))
+    sel = np.linspace(0, wl.B - 1, rows).astype(np.int64) if rows < wl.B else np.arange(wl.B)
+    rs, ln = wl.row_starts[sel], wl.lengths[sel]
+    t0 = time.perf_counter()
+    oracle.topk_ragged(wl.scores, rs, ln, wl.k, wl.max_len, threads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": rows / dt,
+        "unit": "rows/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d rows (%s), qsort by (total-order key desc, index asc) + truncate, %d threads"
+                  % (rows, wl.B, "all" if rows == wl.B else "evenly spaced", threads),
+        "seconds": dt,
+    }
+
+
+def traffic_for(workload, algo_bytes):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(nbytes: int, reps: int) -> None:
+    """A plain device-to-device copy of known size, to calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_causal_8192x16384")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies cycled per step (0: enough to exceed the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the top-k rows are independent, so a multi-GPU "
+              "run would only shard rows; this build measures one GPU's share (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 5)
+        return
+
+    import workloads as W
+    log("generating %s" % args.workload)
+    wl = W.full(args.workload)
+    algo = wl.algorithmic_bytes()
+    rotate = args.rotate or max(1, -(-2 * MALL_BYTES // max(wl.scores.nbytes, 1)))
+    rotate = min(rotate, 200)
+    log("timing %d steps (+%d warmup), %d input copies" % (args.steps, args.warmup, rotate))
+    wall, launch_ms, ws_bytes = time_gpu(wl, args.steps, args.warmup, rotate)
+    ms_per_step = 1e3 * wall / args.steps
+    avg_launch_ms = float(np.mean(launch_ms))
+    achieved = algo / (avg_launch_ms * 1e-3) / 1e9
+    score_gbps = 4.0 * wl.sum_n / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": wl.B / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "B": wl.B, "max_len": wl.max_len, "k": wl.k, "sum_n": wl.sum_n,
+            "input_copies_rotated": rotate, "parallelism": "none (1 GPU)",
+        },
+        "score_gbps": score_gbps,
+        "score_frac_of_hbm_peak": score_gbps / HBM_PEAK_GBPS,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic_for(wl.name, algo),
+            "algorithmic_bytes_per_launch": algo,
+            "avg_launch_us": avg_launch_ms * 1e3,
+            "min_launch_us": float(np.min(launch_ms)) * 1e3,
+            "kernel": "topk_ragged_kernel",
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

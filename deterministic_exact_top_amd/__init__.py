@@ -23,7 +23,7 @@ __all__ = [
 
 DETK_MAX_K = 4096
 DETK_OK, DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, DETK_ERR_WORKSPACE, DETK_ERR_HIP = range(5)
-DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE = 1, 2, 3
+DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE, DETK_DEBUG_FAST = 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None

@@ -15,12 +15,31 @@
 namespace {
 
 using detk::Params;
-using detk::Smem;
+using detk::SmemAll;
 
-// Kernel shapes.  One-workgroup-per-row tiles (threads x elements per lane):
-//   4096 = 256 x 16, 8192 = 256 x 32, 16384 = 256 x 64, 32768 = 512 x 64.
-// Multi-workgroup rows use tiles of 4096 / 8192 / 16384 elements (256 threads).
+// Workgroup tile shapes (elements = threads x elements per lane).  Tiles keep the row in
+// VGPRs; MINW is the waves per SIMD their register allocation must allow.
+//   one workgroup per row: 4096 = 256 x 16, 8192 = 512 x 16, 16384 = 512 x 32,
+//                          32768 = 1024 x 32
+//   several per row:       4096 = 256 x 16, 8192 = 512 x 16, 16384 = 512 x 32
 constexpr int kSingleMaxLen = 32768;
+
+template <int TILE> struct Shape;
+template <> struct Shape<4096> { static constexpr int NT = 256, EPT = 16, MINW = 2; };
+template <> struct Shape<8192> { static constexpr int NT = 512, EPT = 16, MINW = 4; };
+template <> struct Shape<16384> { static constexpr int NT = 512, EPT = 32, MINW = 4; };
+template <> struct Shape<32768> { static constexpr int NT = 1024, EPT = 32, MINW = 4; };
+
+template <int TILE, int KMAX, bool MULTI>
+const void* kernel_ptr() {
+    using S = Shape<TILE>;
+    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>);
+}
+
+template <int TILE, int KMAX>
+constexpr size_t smem_bytes() {
+    return sizeof(SmemAll<Shape<TILE>::NT, Shape<TILE>::EPT, KMAX>);
+}
 
 struct DeviceInfo {
     bool init = false;
@@ -35,27 +54,29 @@ DeviceInfo g_dev[64];
 int g_force_path = 0;       // 0 auto, 1 single, 2 multi
 int g_stage_cap = -1;       // -1 default
 int g_multi_tile = 0;       // 0 default
+int g_fast = 1;             // 0 off, 1 on, 2 on with a pivot that always misses
 
-template <int NT, int EPT, int KMAX>
-constexpr size_t smem_bytes() {
-    return sizeof(Smem<NT, EPT, KMAX>);
-}
-
-template <int NT, int EPT, int KMAX, bool MULTI>
+template <int TILE, int KMAX, bool MULTI>
 hipError_t prepare_kernel() {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&detk::topk_ragged_kernel<NT, EPT, KMAX, MULTI>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_bytes<NT, EPT, KMAX>());
+    return hipFuncSetAttribute(kernel_ptr<TILE, KMAX, MULTI>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)smem_bytes<TILE, KMAX>());
 }
 
-template <int NT, int EPT, int KMAX>
+template <int TILE, int KMAX>
 int multi_occupancy() {
-    if (prepare_kernel<NT, EPT, KMAX, true>() != hipSuccess) return 0;
+    if (prepare_kernel<TILE, KMAX, true>() != hipSuccess) return 0;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&detk::topk_ragged_kernel<NT, EPT, KMAX, true>), NT,
-            smem_bytes<NT, EPT, KMAX>()) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel_ptr<TILE, KMAX, true>(), Shape<TILE>::NT,
+                                                     smem_bytes<TILE, KMAX>()) != hipSuccess)
         return 0;
     return blocks;
+}
+
+template <int TILE>
+void prepare_both(hipError_t* e) {
+    hipError_t r;
+    if ((r = prepare_kernel<TILE, 2048, false>()) != hipSuccess) *e = r;
+    if ((r = prepare_kernel<TILE, 4096, false>()) != hipSuccess) *e = r;
 }
 
 int device_info(int device, DeviceInfo* out) {
@@ -72,12 +93,16 @@ int device_info(int device, DeviceInfo* out) {
             d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
             d.cus = prop.multiProcessorCount;
             d.max_lds = prop.sharedMemPerBlock;
-            d.multi_occ[0][0] = multi_occupancy<256, 16, 2048>();
-            d.multi_occ[0][1] = multi_occupancy<256, 16, 4096>();
-            d.multi_occ[1][0] = multi_occupancy<256, 32, 2048>();
-            d.multi_occ[1][1] = multi_occupancy<256, 32, 4096>();
-            d.multi_occ[2][0] = multi_occupancy<256, 64, 2048>();
-            d.multi_occ[2][1] = multi_occupancy<256, 64, 4096>();
+            d.multi_occ[0][0] = multi_occupancy<4096, 2048>();
+            d.multi_occ[0][1] = multi_occupancy<4096, 4096>();
+            d.multi_occ[1][0] = multi_occupancy<8192, 2048>();
+            d.multi_occ[1][1] = multi_occupancy<8192, 4096>();
+            d.multi_occ[2][0] = multi_occupancy<16384, 2048>();
+            d.multi_occ[2][1] = multi_occupancy<16384, 4096>();
+            prepare_both<4096>(&e);
+            prepare_both<8192>(&e);
+            prepare_both<16384>(&e);
+            prepare_both<32768>(&e);
         }
         if (cur != device) (void)hipSetDevice(cur);
         if (e != hipSuccess) return DETK_ERR_HIP;
@@ -99,12 +124,13 @@ struct Plan {
     size_t off_zero = 0, n_zero_words = 0, off_ecnt = 0, off_stage = 0;
 };
 
-size_t single_lds(int tile, int kmax) {
+size_t lds_bytes(int tile, int kmax) {
+    const bool k2 = kmax == 2048;
     switch (tile) {
-    case 4096: return kmax == 2048 ? smem_bytes<256, 16, 2048>() : smem_bytes<256, 16, 4096>();
-    case 8192: return kmax == 2048 ? smem_bytes<256, 32, 2048>() : smem_bytes<256, 32, 4096>();
-    case 16384: return kmax == 2048 ? smem_bytes<256, 64, 2048>() : smem_bytes<256, 64, 4096>();
-    default: return kmax == 2048 ? smem_bytes<512, 64, 2048>() : smem_bytes<512, 64, 4096>();
+    case 4096: return k2 ? smem_bytes<4096, 2048>() : smem_bytes<4096, 4096>();
+    case 8192: return k2 ? smem_bytes<8192, 2048>() : smem_bytes<8192, 4096>();
+    case 16384: return k2 ? smem_bytes<16384, 2048>() : smem_bytes<16384, 4096>();
+    default: return k2 ? smem_bytes<32768, 2048>() : smem_bytes<32768, 4096>();
     }
 }
 
@@ -134,7 +160,6 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         pl->tile = max_len <= 4096 ? 4096 : max_len <= 8192 ? 8192 : max_len <= 16384 ? 16384 : 32768;
         pl->tiles_per_row = 1;
         pl->grid = B;
-        pl->lds = single_lds(pl->tile, pl->kmax);
         pl->ws_bytes = 0;
     } else {
         pl->tile = g_multi_tile ? g_multi_tile : 8192;
@@ -148,9 +173,6 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         int64_t grid = rows_resident * tpr;
         if (grid > items) grid = items;
         pl->grid = (int)grid;
-        pl->lds = pl->tile == 4096   ? (ki ? smem_bytes<256, 16, 4096>() : smem_bytes<256, 16, 2048>())
-                  : pl->tile == 8192 ? (ki ? smem_bytes<256, 32, 4096>() : smem_bytes<256, 32, 2048>())
-                                     : (ki ? smem_bytes<256, 64, 4096>() : smem_bytes<256, 64, 2048>());
         pl->n_zero_words = 1 + (size_t)B * detk::kRowZeroWords;
         pl->off_zero = 0;
         size_t off = pl->n_zero_words * 4;
@@ -162,21 +184,18 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         off += (size_t)B * (size_t)k * 8;
         pl->ws_bytes = off;
     }
+    pl->lds = lds_bytes(pl->tile, pl->kmax);
     if (pl->lds > dev.max_lds) return DETK_ERR_UNSUPPORTED;
     // int32 offsets: every window must be addressable with int32 row_starts + length.
     if ((int64_t)B * k >= ((int64_t)1 << 31)) return DETK_ERR_UNSUPPORTED;
     return DETK_OK;
 }
 
-template <int NT, int EPT, int KMAX, bool MULTI>
+template <int TILE, int KMAX, bool MULTI>
 hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
-    static bool attr_done = false;  // attribute set once per process (idempotent anyway)
-    if (!attr_done) {
-        hipError_t e = prepare_kernel<NT, EPT, KMAX, MULTI>();
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
-    hipLaunchKernelGGL((detk::topk_ragged_kernel<NT, EPT, KMAX, MULTI>), dim3(grid), dim3(NT), lds, stream, p);
+    using S = Shape<TILE>;
+    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>), dim3(grid), dim3(S::NT), lds,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -184,23 +203,23 @@ hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
     const bool k2 = pl.kmax == 2048;
     if (!pl.multi) {
         switch (pl.tile) {
-        case 4096: return k2 ? launch<256, 16, 2048, false>(p, pl.grid, pl.lds, stream)
-                             : launch<256, 16, 4096, false>(p, pl.grid, pl.lds, stream);
-        case 8192: return k2 ? launch<256, 32, 2048, false>(p, pl.grid, pl.lds, stream)
-                             : launch<256, 32, 4096, false>(p, pl.grid, pl.lds, stream);
-        case 16384: return k2 ? launch<256, 64, 2048, false>(p, pl.grid, pl.lds, stream)
-                              : launch<256, 64, 4096, false>(p, pl.grid, pl.lds, stream);
-        default: return k2 ? launch<512, 64, 2048, false>(p, pl.grid, pl.lds, stream)
-                           : launch<512, 64, 4096, false>(p, pl.grid, pl.lds, stream);
+        case 4096: return k2 ? launch<4096, 2048, false>(p, pl.grid, pl.lds, stream)
+                             : launch<4096, 4096, false>(p, pl.grid, pl.lds, stream);
+        case 8192: return k2 ? launch<8192, 2048, false>(p, pl.grid, pl.lds, stream)
+                             : launch<8192, 4096, false>(p, pl.grid, pl.lds, stream);
+        case 16384: return k2 ? launch<16384, 2048, false>(p, pl.grid, pl.lds, stream)
+                              : launch<16384, 4096, false>(p, pl.grid, pl.lds, stream);
+        default: return k2 ? launch<32768, 2048, false>(p, pl.grid, pl.lds, stream)
+                           : launch<32768, 4096, false>(p, pl.grid, pl.lds, stream);
         }
     }
     switch (pl.tile) {
-    case 4096: return k2 ? launch<256, 16, 2048, true>(p, pl.grid, pl.lds, stream)
-                         : launch<256, 16, 4096, true>(p, pl.grid, pl.lds, stream);
-    case 8192: return k2 ? launch<256, 32, 2048, true>(p, pl.grid, pl.lds, stream)
-                         : launch<256, 32, 4096, true>(p, pl.grid, pl.lds, stream);
-    default: return k2 ? launch<256, 64, 2048, true>(p, pl.grid, pl.lds, stream)
-                       : launch<256, 64, 4096, true>(p, pl.grid, pl.lds, stream);
+    case 4096: return k2 ? launch<4096, 2048, true>(p, pl.grid, pl.lds, stream)
+                         : launch<4096, 4096, true>(p, pl.grid, pl.lds, stream);
+    case 8192: return k2 ? launch<8192, 2048, true>(p, pl.grid, pl.lds, stream)
+                         : launch<8192, 4096, true>(p, pl.grid, pl.lds, stream);
+    default: return k2 ? launch<16384, 2048, true>(p, pl.grid, pl.lds, stream)
+                       : launch<16384, 4096, true>(p, pl.grid, pl.lds, stream);
     }
 }
 
@@ -251,6 +270,7 @@ int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32
     p.k = k;
     p.tiles_per_row = pl.tiles_per_row;
     p.stage_cap = g_stage_cap < 0 ? detk::kStageCap : (g_stage_cap > detk::kStageCap ? detk::kStageCap : g_stage_cap);
+    p.fast = g_fast;
     p.out_idx = out_idx;
     p.out_val = reinterpret_cast<uint32_t*>(out_val);
     p.ws_zero = nullptr;
@@ -306,6 +326,10 @@ int detk_debug_set(int what, int value) {
     case DETK_DEBUG_MULTI_TILE:
         if (value != 0 && value != 4096 && value != 8192 && value != 16384) return DETK_ERR_INVALID_ARG;
         g_multi_tile = value;
+        return DETK_OK;
+    case DETK_DEBUG_FAST:
+        if (value < 0 || value > 2) return DETK_ERR_INVALID_ARG;
+        g_fast = value;
         return DETK_OK;
     default: return DETK_ERR_INVALID_ARG;
     }

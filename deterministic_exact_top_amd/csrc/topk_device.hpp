@@ -1,39 +1,57 @@
 // topk_device.hpp -- gfx950 device code for exact, bitwise-deterministic ragged top-k.
 //
-// Method (SGLang PR #31115, "Modifications"): a coarse 8-bit radix histogram pass,
-// MSB-first refinement to the exact threshold key, smallest-index resolution of the
-// boundary tie set, and a sort of the unique (score, index) composites into the
-// canonical order (score descending under the bitwise total order, index ascending).
-// Threshold-bin overflow never drops a candidate: refinement rescans the row
-// (same PR, summary and hardening commit).
+// Result (SGLang PR #31115, PR summary and "Modifications"): per row, the k largest
+// scores in canonical order -- score descending under the bitwise total order of the
+// float bits, index ascending among bitwise-equal scores -- so the k-th boundary keeps
+// the smallest indices of its tie set.  The pages' method: a coarse 8-bit radix
+// histogram pass, MSB-first refinement to the exact threshold key, an index pass that
+// picks the smallest-index tie subset, a sort of unique (score, index) composites; a
+// threshold bin that overflows staging falls back to rescans, never dropping a
+// candidate (same PR, summary and hardening commit).
 //
 // MI355X layout of the work:
 //   * A workgroup owns a tile of up to NT*EPT consecutive elements of one row and keeps
-//     it in VGPRs for its whole life (EPT 32-bit keys per lane).  HBM is read once.
-//   * Histograms are per-wave LDS arrays of 256 u32 bins, merged by the workgroup;
-//     lanes that share the first active lane's bin are merged with one ballot and a
-//     single LDS add, which keeps 0.0-plateau rows from serialising on one bank.
-//   * After the first pass the threshold bin's candidates are compacted into LDS when
-//     they fit (`stage_cap`); otherwise every later pass rescans the registers.
-//   * Boundary ties (key == T) are ranked in index order with an LDS bitmap over the
-//     tile's positions plus a prefix over words; the first `need` are kept.
-//   * Selected elements above T are sorted in LDS as u64 composites
-//     (key << 32 | ~index), which are unique, so the order is total.
-//   * Rows longer than one tile are split over several co-resident workgroups that
-//     add their integer histograms into the workspace with atomics (order-independent,
-//     hence deterministic) and meet at per-row counters between passes.
+//     it in VGPRs for its whole life: HBM is read once, with every buffer load of the
+//     tile in flight together (out-of-range lanes read 0 from the buffer unit).
+//   * Fast path (rows that fit one tile): a pivot P is taken from a 1024-element
+//     sample (its r-th largest key, r set a few standard deviations above the expected
+//     share of the top k).  One register pass sends keys > P to per-wave LDS candidate
+//     regions and marks keys == P in an LDS bitmap of positions.  If at least min(k, n)
+//     keys are >= P, the top k lie among them: candidates are bucketed by key (a
+//     linear bucket index over [min candidate, max sample]), buckets get exclusive
+//     offsets from an integer suffix scan, and each candidate's slot is its bucket
+//     offset plus the number of bucket members with a larger (key, ~index) composite.
+//     That one step both selects (slots >= k are dropped) and sorts.  Ties at P, when
+//     needed, take the smallest positions from the bitmap.
+//   * Exact path (pivot miss, oversized bucket, and rows split over several
+//     workgroups): 8-bit MSD radix passes with per-wave LDS histograms merged into one
+//     (lanes sharing the first active lane's bin are merged with one ballot and one
+//     LDS add); threshold-bin candidates are staged in LDS when they fit, otherwise each
+//     pass rescans the registers; boundary ties are ranked in index order with the
+//     position bitmap; elements above the threshold are sorted as composites in LDS.
+//   * Rows longer than one tile are split over co-resident workgroups that add their
+//     integer histograms into the workspace with atomics (order-independent, hence
+//     deterministic) and meet at per-row counters between passes.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace detk {
 
 constexpr int kRadix = 256;
-constexpr int kStageCap = 4096;          // LDS threshold-bin staging capacity (entries)
+constexpr int kStageCap = 4096;                 // exact path: LDS threshold-bin staging (entries)
+constexpr int kCandCap = 4096;                  // fast path: LDS candidate capacity (entries)
+constexpr int kBuckets = 4096;                  // fast path: buckets over the candidate key range
+constexpr int kBucketBits = 12;
+constexpr int kBucketLimit = 256;               // fast path: largest bucket ranked by comparisons
+constexpr int kSamplesPerLane = 4;
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 constexpr int kRowZeroWords = 4 * kRadix + 4;   // per-row words zeroed before a multi launch
 constexpr uint32_t kSpinLimit = 1u << 21;       // bounded wait (polls, ~1 us each) at row barriers
+constexpr int kBufferWord3 = 0x00020000;        // raw buffer resource, gfx9-family data format
 
 struct Params {
     const uint32_t* scores;
@@ -44,6 +62,7 @@ struct Params {
     int32_t k;
     int32_t tiles_per_row;      // multi path only
     int32_t stage_cap;          // <= kStageCap
+    int32_t fast;               // 1: try the pivot fast path on single-tile rows
     int32_t* out_idx;
     uint32_t* out_val;          // nullable
     uint32_t* ws_zero;          // [0] error word, then B * kRowZeroWords (zeroed per call)
@@ -64,6 +83,14 @@ __device__ __forceinline__ uint32_t bits_of(uint32_t key) {
 
 // ----------------------------------------------------------------------------- wave helpers
 
+// threadIdx.x behind an empty asm: values derived from it are recomputed where they are
+// used instead of being hoisted out of the persistent item loop into (spilled) registers.
+__device__ __forceinline__ int opaque_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
@@ -75,6 +102,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
         const uint32_t y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
     }
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor(x, o, 64));
     return x;
 }
 
@@ -108,10 +147,40 @@ __device__ __forceinline__ uint32_t claim_slot(bool pred, uint32_t* counter) {
     return base + lanes_below(m);
 }
 
+// ----------------------------------------------------------------------------- loads
+
+// Load one tile's raw bits: slot (v, c) of lane t holds window position
+// (v * NT + t) * 4 + c.  All loads are issued before any use.  The buffer resource
+// covers exactly the tile's valid bytes, so slots past the window read 0 (callers mask
+// them by position).  A 16-byte aligned tile uses 16-byte loads (a partially valid one
+// never leaves the 16-byte chunk holding valid data); otherwise 4-byte loads.
+template <int NT, int EPT>
+__device__ __forceinline__ void load_tile(uint32_t (&u)[EPT], const uint32_t* src, int nt) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src), (short)0, nt * 4, kBufferWord3);
+    const int tid = opaque_tid();
+    if ((((uintptr_t)src) & 15u) == 0) {
+#pragma unroll
+        for (int v = 0; v < EPT / 4; ++v) {
+            const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (v * NT + tid) * 16, 0, 0);
+            u[4 * v + 0] = q[0];
+            u[4 * v + 1] = q[1];
+            u[4 * v + 2] = q[2];
+            u[4 * v + 3] = q[3];
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < EPT / 4; ++v)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, ((v * NT + tid) * 4 + c) * 4, 0, 0);
+    }
+}
+
 // ----------------------------------------------------------------------------- shared memory
 
 template <int NT, int EPT, int KMAX>
-struct Smem {
+struct ExactSmem {
     static constexpr int NW = NT / 64;
     static constexpr int TILE = NT * EPT;
     static constexpr int BWORDS = TILE / 32;
@@ -126,6 +195,40 @@ struct Smem {
     uint32_t skey[kStageCap];     // staged candidate keys
     uint32_t sidx[kStageCap];     // staged candidate row indices
     uint64_t A[KMAX];             // composites of selected elements above T
+};
+
+template <int NT, int EPT, int KMAX>
+struct FastSmem {
+    static constexpr int NW = NT / 64;
+    static constexpr int TILE = NT * EPT;
+    static constexpr int BWORDS = TILE / 32;
+    static constexpr int CAPW = kCandCap / NW;   // candidate entries per wave region
+    static constexpr int SCAP = KMAX + kBucketLimit;
+    uint32_t ctl[16];             // [0] pivot, [1] sample max, [2] candidate min, [3] b_t,
+                                  // [4] kept, [5] max bucket
+    uint32_t wsum[32];
+    uint32_t sel[4];
+    uint32_t wcnt[NW][4];         // per wave: candidates (> P), ties (== P)
+    uint32_t hist[kRadix];        // sample radix select
+    uint32_t bitmap[BWORDS];      // positions with key == P
+    uint32_t bucket[kBuckets];    // counts, then cursors / bucket ends
+    uint64_t S[SCAP];             // kept candidates as composites, grouped by bucket
+    union {
+        struct {
+            uint32_t key[kCandCap];
+            uint16_t idx[kCandCap];
+        } cand;
+        struct {
+            uint32_t idx[KMAX];
+            uint32_t val[KMAX];
+        } out;
+    } u;
+};
+
+template <int NT, int EPT, int KMAX>
+union SmemAll {
+    ExactSmem<NT, EPT, KMAX> exact;
+    FastSmem<NT, EPT, KMAX> fast;
 };
 
 // ----------------------------------------------------------------------------- block helpers
@@ -206,6 +309,15 @@ __device__ __forceinline__ void bitonic_desc(uint64_t* A, int count) {
     }
 }
 
+// Write the padding slots [m, k) of one output row.
+template <int NT>
+__device__ __forceinline__ void write_padding(int32_t* oidx, uint32_t* oval, int m, int k) {
+    for (int q = m + (int)threadIdx.x; q < k; q += NT) {
+        oidx[q] = -1;
+        if (oval) oval[q] = kNegInfBits;
+    }
+}
+
 // ----------------------------------------------------------------------------- row barrier
 
 __device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
@@ -226,82 +338,326 @@ __device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint
     __threadfence();
 }
 
-// ----------------------------------------------------------------------------- the tile
+// ----------------------------------------------------------------------------- row context
+
+struct RowCtx {
+    int b, tile, ntiles;
+    int32_t n, m, k, nt, j0;
+    int64_t base;
+    bool multi;
+    int32_t* oidx;
+    uint32_t* oval;
+};
+
+// ----------------------------------------------------------------------------- fast path
+
+// Try the pivot + bucket-rank path on a single-tile row (raw bits in u[]).  Returns
+// false, with LDS left dirty but registers untouched, when the row needs the exact path.
+template <int NT, int EPT, int KMAX>
+__device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMAX>& s, const uint32_t (&u)[EPT],
+                                          int fast_mode) {
+    using FS = FastSmem<NT, EPT, KMAX>;
+    constexpr int G4 = EPT / 4;
+    constexpr int NW = FS::NW;
+    constexpr int BW = FS::BWORDS;
+    constexpr int CAPW = FS::CAPW;
+    constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
+    const int tid = opaque_tid();
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int32_t nt = r.nt;
+    const int32_t m = r.m;
+
+    // ------------------------------------------------ clear LDS state
+    for (int i = tid; i < kBuckets; i += NT) s.bucket[i] = 0;
+    for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
+    if (tid < 16) s.ctl[tid] = tid == 2 ? 0xFFFFFFFFu : 0u;
+
+    // ------------------------------------------------ sample -> pivot
+    // Samples: slots i * EPT / 4 (i < 4) of every lane, spread over the tile.
+    uint32_t sk[kSamplesPerLane];
+    int nsamp = 0;  // valid samples in the whole workgroup (uniform)
+    uint32_t smax = 0;
+#pragma unroll
+    for (int i = 0; i < kSamplesPerLane; ++i) {
+        constexpr int step = EPT / kSamplesPerLane;
+        const int slot = i * step;
+        const int v = slot / 4, c = slot % 4;
+        const int pos = (v * NT + tid) * 4 + c;
+        const bool ok = pos < nt;
+        sk[i] = ok ? key_of(u[slot]) : 0u;
+        smax = max(smax, sk[i]);
+        const int lim = nt - v * NT * 4 - c;  // lanes of this sample row that are valid
+        nsamp += min(max((lim + 3) / 4, 0), NT);
+    }
+    smax = wave_max(smax);
+    __syncthreads();
+    if (lane == 0) __hip_atomic_fetch_max(&s.ctl[1], smax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+
+    // r-th largest sample, r = expected share of the top m plus ~3.5 standard deviations.
+    uint32_t P = 0;
+    {
+        const float expct = (float)nsamp * (float)m / (float)nt;
+        // (r.fast == 2, a test setting, takes the largest sample: the pivot misses.)
+        const int rr = fast_mode == 2 ? 1 : (int)ceilf(expct + 3.5f * sqrtf(expct) + 4.0f);
+        if (m < nt && rr < nsamp) {
+            uint32_t prefix = 0, r_rem = (uint32_t)rr;
+#pragma unroll 1
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+                if (tid < kRadix) s.hist[tid] = 0;
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < kSamplesPerLane; ++i) {
+                    const uint32_t kk = sk[i];
+                    const bool match = pass == 0 || (kk >> (shift + 8)) == prefix;
+                    if (match) hist_add(s.hist, (kk >> shift) & 0xFFu);
+                }
+                __syncthreads();
+                select_digit<NT>(s.hist, r_rem, s.wsum, s.sel);
+                prefix = (prefix << 8) | s.sel[0];
+                r_rem -= s.sel[1];
+                __syncthreads();
+            }
+            P = prefix;
+        }
+    }
+    // Compare on raw bits when P is a non-negative float's key (the common case).
+    const int32_t pr = (int32_t)(P & 0x7FFFFFFFu);
+
+    // ------------------------------------------------ one register pass: > P to the
+    // wave's candidate region, == P into the position bitmap.
+    uint32_t off = 0;        // wave-uniform fill of this wave's region
+    uint32_t neq = 0;        // this lane's count of keys == P
+    uint32_t cmin = 0xFFFFFFFFu;
+    uint32_t* ckey = s.u.cand.key + wave * CAPW;
+    uint16_t* cidx = s.u.cand.idx + wave * CAPW;
+    const int tid4 = tid * 4;
+    auto pass = [&](auto pos_tag) {
+        constexpr bool POS = decltype(pos_tag)::value;
+#pragma unroll
+        for (int v = 0; v < G4; ++v) {
+            const int lim = nt - v * NT * 4;
+            if (lim <= 0) break;
+            const int llim = lim - tid4;  // valid slots of this lane in group v (may be <= 0 or > 4)
+            uint32_t nib = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t x = u[4 * v + c];
+                bool gt, eq;
+                if constexpr (POS) {
+                    gt = (int32_t)x > pr;
+                    eq = x == (uint32_t)pr;
+                } else {
+                    const uint32_t kx = key_of(x);
+                    gt = kx > P;
+                    eq = kx == P;
+                }
+                const bool ok = c < llim;
+                gt = gt && ok;
+                eq = eq && ok;
+                nib |= (eq ? 1u : 0u) << c;
+                const uint64_t bal = __ballot(gt);
+                if (bal) {
+                    const uint32_t slot = off + lanes_below(bal);
+                    if (gt && slot < (uint32_t)CAPW) {
+                        const uint32_t kx = key_of(x);
+                        ckey[slot] = kx;
+                        cidx[slot] = (uint16_t)(tid4 + (v * NT * 4 + c));
+                        cmin = min(cmin, kx);
+                    }
+                    off += (uint32_t)__popcll(bal);
+                }
+            }
+            if (__ballot(nib != 0)) {
+                if (nib) {
+                    const int p0 = tid4 + v * NT * 4;
+                    __hip_atomic_fetch_or(&s.bitmap[p0 >> 5], nib << (p0 & 31), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+                    neq += (uint32_t)__popc(nib);
+                }
+            }
+        }
+    };
+    if (P >= 0x80000000u)
+        pass(std::true_type{});
+    else
+        pass(std::false_type{});
+    {
+        neq = wave_incl_scan(neq);  // lane 63 holds the wave total
+        cmin = wave_min(cmin);
+        if (lane == 63) {
+            s.wcnt[wave][0] = off;
+            s.wcnt[wave][1] = neq;
+        }
+        if (lane == 0) __hip_atomic_fetch_min(&s.ctl[2], cmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    uint32_t c_gt = 0, c_eq = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        c_gt += s.wcnt[w][0];
+        c_eq += s.wcnt[w][1];
+        overflow |= s.wcnt[w][0] > (uint32_t)CAPW;
+    }
+    if (overflow || c_gt + c_eq < (uint32_t)m) return false;  // uniform
+    const uint32_t mlim = min((uint32_t)m, c_gt);             // slots filled by candidates
+
+    // ------------------------------------------------ bucket counts
+    const uint32_t L = s.ctl[2];
+    const uint32_t U = max(s.ctl[1], L);
+    const uint32_t span = U - L;
+    const int sh = max(0, (32 - __clz(span)) - kBucketBits);
+    auto bucket_of = [&](uint32_t kx) -> uint32_t { return min((kx - L) >> sh, (uint32_t)(kBuckets - 1)); };
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t cnt = s.wcnt[w][0];
+        for (uint32_t j = tid; j < cnt; j += NT) lds_add(&s.bucket[bucket_of(s.u.cand.key[w * CAPW + j])], 1u);
+    }
+    __syncthreads();
+
+    // ------------------------------------------------ suffix scan: bucket starts
+    // Thread t owns buckets [kBuckets - (t + 1) * BPT, kBuckets - t * BPT), scanned from
+    // the top, so rank offsets grow with t.
+    uint32_t cnts[BPT];
+    uint32_t tsum = 0;
+    const int btop = kBuckets - tid * BPT - 1;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        cnts[i] = s.bucket[btop - i];
+        tsum += cnts[i];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan<NT>(tsum, s.wsum, &total);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const uint32_t st = run;
+        s.bucket[btop - i] = st;  // cursor starts at the bucket's first slot
+        if (c_gt >= (uint32_t)m && st < (uint32_t)m && st + cnts[i] >= (uint32_t)m) {
+            s.ctl[3] = (uint32_t)(btop - i);  // threshold bucket
+            s.ctl[4] = st + cnts[i];          // kept candidates (slots of buckets >= b_t)
+        }
+        run += cnts[i];
+    }
+    __syncthreads();
+    const uint32_t bt = c_gt >= (uint32_t)m ? s.ctl[3] : 0u;
+    const uint32_t kept = c_gt >= (uint32_t)m ? s.ctl[4] : c_gt;
+    {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i)
+            if ((uint32_t)(btop - i) >= bt) mx = max(mx, cnts[i]);
+        mx = wave_max(mx);
+        if (lane == 0) __hip_atomic_fetch_max(&s.ctl[5], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (kept > (uint32_t)FS::SCAP || s.ctl[5] > (uint32_t)kBucketLimit) return false;  // uniform
+
+    // ------------------------------------------------ scatter kept candidates by bucket
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t cnt = s.wcnt[w][0];
+        for (uint32_t j = tid; j < cnt; j += NT) {
+            const uint32_t kx = s.u.cand.key[w * CAPW + j];
+            const uint32_t bk = bucket_of(kx);
+            if (bk >= bt) {
+                const uint32_t pos = __hip_atomic_fetch_add(&s.bucket[bk], 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (pos < (uint32_t)FS::SCAP)
+                    s.S[pos] = ((uint64_t)kx << 32) | (uint32_t)~(uint32_t)s.u.cand.idx[w * CAPW + j];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------ rank inside buckets -> final slot
+    // s.bucket[b] now holds the end of bucket b; its start is the end of bucket b + 1.
+    for (uint32_t q = tid; q < kept; q += NT) {
+        const uint64_t c = s.S[q];
+        const uint32_t bk = bucket_of((uint32_t)(c >> 32));
+        const uint32_t e = min(s.bucket[bk], kept);
+        const uint32_t st = bk == (uint32_t)(kBuckets - 1) ? 0u : s.bucket[bk + 1];
+        uint32_t rank = 0;
+        for (uint32_t f = st; f < e; ++f) rank += s.S[f] > c ? 1u : 0u;
+        const uint32_t slot = st + rank;
+        if (slot < mlim) {
+            s.u.out.idx[slot] = ~(uint32_t)c;
+            s.u.out.val[slot] = bits_of((uint32_t)(c >> 32));
+        }
+    }
+
+    // ------------------------------------------------ ties at P: smallest positions
+    if (c_gt < (uint32_t)m) {
+        const uint32_t need = (uint32_t)m - c_gt;
+        constexpr int WPT = (BW + NT - 1) / NT;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            const int w = tid * WPT + q;
+            if (w < BW) cnt += (uint32_t)__popc(s.bitmap[w]);
+        }
+        uint32_t tot;
+        uint32_t rr = block_excl_scan<NT>(cnt, s.wsum, &tot);
+        const uint32_t vP = bits_of(P);
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            const int w = tid * WPT + q;
+            if (w < BW) {
+                uint32_t word = s.bitmap[w];
+                while (word && rr < need) {
+                    const int bit = __ffs(word) - 1;
+                    word &= word - 1;
+                    s.u.out.idx[c_gt + rr] = (uint32_t)(w * 32 + bit);
+                    s.u.out.val[c_gt + rr] = vP;
+                    ++rr;
+                }
+                rr += (uint32_t)__popc(word);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------ store the row
+    for (int q = tid; q < m; q += NT) {
+        r.oidx[q] = (int32_t)s.u.out.idx[q];
+        if (r.oval) r.oval[q] = s.u.out.val[q];
+    }
+    write_padding<NT>(r.oidx, r.oval, m, r.k);
+    return true;
+}
+
+// ----------------------------------------------------------------------------- exact path
 
 template <int NT, int EPT, int KMAX, bool MULTI>
-__device__ __forceinline__ void process_tile(const Params& p, Smem<NT, EPT, KMAX>& s, int b, int tile) {
-    constexpr int TILE = NT * EPT;
-    constexpr int G4 = EPT / 4;  // float4 groups per lane
-    constexpr int BW = Smem<NT, EPT, KMAX>::BWORDS;
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ExactSmem<NT, EPT, KMAX>& s,
+                                           const uint32_t (&key)[EPT]) {
+    constexpr int G4 = EPT / 4;
+    constexpr int BW = ExactSmem<NT, EPT, KMAX>::BWORDS;
+    constexpr int NW = ExactSmem<NT, EPT, KMAX>::NW;
+    const int tid = opaque_tid();
     const int wave = tid >> 6;
-
-    const int32_t len = p.lengths ? p.lengths[b] : p.max_len;
-    const int32_t n = min(max(len, 0), p.max_len);
-    const int64_t base = p.row_starts ? (int64_t)p.row_starts[b] : (int64_t)b * p.max_len;
-    const int32_t k = p.k;
-    const int32_t m = min(k, n);
-    const int ntiles = MULTI ? max(1, (n + TILE - 1) / TILE) : 1;
-    if (tile >= ntiles) return;
-    const bool multi = MULTI && ntiles > 1;
-    int32_t* oidx = p.out_idx + (int64_t)b * k;
-    uint32_t* oval = p.out_val ? p.out_val + (int64_t)b * k : nullptr;
-
-    __syncthreads();  // previous item of a persistent workgroup is done with LDS
-
-    if (m == 0) {  // empty window: every slot is padding (single tile by construction)
-        for (int q = tid; q < k; q += NT) {
-            oidx[q] = -1;
-            if (oval) oval[q] = kNegInfBits;
-        }
-        return;
-    }
+    const bool multi = MULTI && r.multi;
+    const int b = r.b, tile = r.tile, ntiles = r.ntiles;
+    const int32_t m = r.m, k = r.k, nt = r.nt, j0 = r.j0;
+    int32_t* oidx = r.oidx;
+    uint32_t* oval = r.oval;
 
     uint32_t* rw = multi ? p.ws_zero + 1 + (int64_t)b * kRowZeroWords : nullptr;  // row words
     uint32_t* err = p.ws_zero;
     uint32_t bar_target = 0;
 
-    const int32_t j0 = tile * TILE;
-    const int32_t nt = min(TILE, n - j0);  // >= 1
-
-    // ---------------------------------------------------------------- load (HBM, once)
-    uint32_t key[EPT];
-    {
-        const uint32_t* src = p.scores + base + j0;
-        const bool aligned = (((uintptr_t)src) & 15u) == 0;
-#pragma unroll
-        for (int v = 0; v < G4; ++v) {
-            const int jl = (v * NT + tid) * 4;
-            uint32_t u0 = 0, u1 = 0, u2 = 0, u3 = 0;
-            if (jl < nt) {
-                if (aligned) {
-                    const uint4 q = *reinterpret_cast<const uint4*>(src + jl);
-                    u0 = q.x; u1 = q.y; u2 = q.z; u3 = q.w;
-                } else {
-                    u0 = src[jl];
-                    if (jl + 1 < nt) u1 = src[jl + 1];
-                    if (jl + 2 < nt) u2 = src[jl + 2];
-                    if (jl + 3 < nt) u3 = src[jl + 3];
-                }
-            }
-            key[4 * v + 0] = key_of(u0);
-            key[4 * v + 1] = key_of(u1);
-            key[4 * v + 2] = key_of(u2);
-            key[4 * v + 3] = key_of(u3);
-        }
-    }
-
+    const int tid4 = tid * 4;
     // Visit every valid register element: f(key, local index).
     auto for_each = [&](auto&& f) {
 #pragma unroll
         for (int v = 0; v < G4; ++v) {
             const int lim = nt - v * NT * 4;
             if (lim <= 0) break;
+            const int llim = lim - tid4;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int jl = (v * NT + tid) * 4 + c;
-                if (tid * 4 + c < lim) f(key[4 * v + c], jl);
-            }
+            for (int c = 0; c < 4; ++c)
+                if (c < llim) f(key[4 * v + c], tid4 + (v * NT * 4 + c));
         }
     };
     // Same, but every lane of the wave calls f (valid flag passed) -- for ballots.
@@ -310,17 +666,15 @@ __device__ __forceinline__ void process_tile(const Params& p, Smem<NT, EPT, KMAX
         for (int v = 0; v < G4; ++v) {
             const int lim = nt - v * NT * 4;
             if (lim <= 0) break;
+            const int llim = lim - tid4;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int jl = (v * NT + tid) * 4 + c;
-                f(key[4 * v + c], jl, tid * 4 + c < lim);
-            }
+            for (int c = 0; c < 4; ++c) f(key[4 * v + c], tid4 + (v * NT * 4 + c), c < llim);
         }
     };
 
     auto zero_whist = [&]() {
         uint32_t* w = &s.whist[0][0];
-        for (int i = tid; i < Smem<NT, EPT, KMAX>::NW * kRadix; i += NT) w[i] = 0;
+        for (int i = tid; i < NW * kRadix; i += NT) w[i] = 0;
     };
 
     // Merge per-wave histograms; in multi mode also add into the row's global histogram
@@ -330,7 +684,7 @@ __device__ __forceinline__ void process_tile(const Params& p, Smem<NT, EPT, KMAX
         if (tid < kRadix) {
             uint32_t h = 0;
 #pragma unroll
-            for (int w = 0; w < Smem<NT, EPT, KMAX>::NW; ++w) h += s.whist[w][tid];
+            for (int w = 0; w < NW; ++w) h += s.whist[w][tid];
             s.lhist[tid] = h;
             s.hist[tid] = h;
             if (multi && h) atomicAdd(&rw[pass * kRadix + tid], h);
@@ -399,9 +753,9 @@ __device__ __forceinline__ void process_tile(const Params& p, Smem<NT, EPT, KMAX
         k_rem -= s.sel[1];
         __syncthreads();
     }
-    const uint32_t T = prefix;                    // exact threshold key
-    const uint32_t need = min(k_rem, (uint32_t)m); // ties at T to keep (>= 1)
-    const uint32_t cnt_gt = (uint32_t)m - need;   // selected elements strictly above T
+    const uint32_t T = prefix;                      // exact threshold key
+    const uint32_t need = min(k_rem, (uint32_t)m);  // ties at T to keep (>= 1)
+    const uint32_t cnt_gt = (uint32_t)m - need;     // selected elements strictly above T
     const uint32_t vT = bits_of(T);
 
     // ---------------------------------------------------------------- the rest of G
@@ -478,14 +832,14 @@ __device__ __forceinline__ void process_tile(const Params& p, Smem<NT, EPT, KMAX
     if (tie_off < need) {
         for (int w = tid; w < BW; w += NT) {
             uint32_t word = s.bitmap[w];
-            uint32_t r = tie_off + s.wpre[w];
-            while (word && r < need) {
+            uint32_t rr = tie_off + s.wpre[w];
+            while (word && rr < need) {
                 const int bit = __ffs(word) - 1;
                 word &= word - 1;
                 const int32_t j = j0 + w * 32 + bit;
-                oidx[cnt_gt + r] = j;
-                if (oval) oval[cnt_gt + r] = vT;
-                ++r;
+                oidx[cnt_gt + rr] = j;
+                if (oval) oval[cnt_gt + rr] = vT;
+                ++rr;
             }
         }
     }
@@ -500,10 +854,7 @@ __device__ __forceinline__ void process_tile(const Params& p, Smem<NT, EPT, KMAX
             oidx[q] = (int32_t)~(uint32_t)c;
             if (oval) oval[q] = bits_of((uint32_t)(c >> 32));
         }
-        for (int q = m + tid; q < k; q += NT) {
-            oidx[q] = -1;
-            if (oval) oval[q] = kNegInfBits;
-        }
+        write_padding<NT>(oidx, oval, m, k);
         return;
     }
 
@@ -538,16 +889,55 @@ __device__ __forceinline__ void process_tile(const Params& p, Smem<NT, EPT, KMAX
         oidx[q] = (int32_t)~(uint32_t)c;
         if (oval) oval[q] = bits_of((uint32_t)(c >> 32));
     }
-    for (int q = m + tid; q < k; q += NT) {
-        oidx[q] = -1;
-        if (oval) oval[q] = kNegInfBits;
-    }
+    write_padding<NT>(oidx, oval, m, k);
 }
 
+// ----------------------------------------------------------------------------- one item
+
 template <int NT, int EPT, int KMAX, bool MULTI>
-__global__ __launch_bounds__(NT) void topk_ragged_kernel(Params p) {
+__device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX>& s, int b, int tile) {
+    constexpr int TILE = NT * EPT;
+    RowCtx r;
+    const int32_t len = p.lengths ? p.lengths[b] : p.max_len;
+    r.b = b;
+    r.tile = tile;
+    r.n = min(max(len, 0), p.max_len);
+    r.base = p.row_starts ? (int64_t)p.row_starts[b] : (int64_t)b * p.max_len;
+    r.k = p.k;
+    r.m = min(r.k, r.n);
+    r.ntiles = MULTI ? max(1, (r.n + TILE - 1) / TILE) : 1;
+    if (tile >= r.ntiles) return;
+    r.multi = MULTI && r.ntiles > 1;
+    r.oidx = p.out_idx + (int64_t)b * r.k;
+    r.oval = p.out_val ? p.out_val + (int64_t)b * r.k : nullptr;
+    r.j0 = tile * TILE;
+    r.nt = min(TILE, r.n - r.j0);
+
+    __syncthreads();  // previous item of a persistent workgroup is done with LDS
+
+    if (r.m == 0) {  // empty window: every slot is padding (single tile by construction)
+        write_padding<NT>(r.oidx, r.oval, 0, r.k);
+        return;
+    }
+
+    uint32_t u[EPT];
+    load_tile<NT, EPT>(u, p.scores + r.base + r.j0, r.nt);
+
+    if (!r.multi && p.fast) {
+        if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
+        __syncthreads();  // fall back to the exact path on the same registers
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
+    exact_tile<NT, EPT, KMAX, MULTI>(p, r, s.exact, u);
+}
+
+// MINW: waves per SIMD the register allocation must allow (the LDS footprint fixes
+// how many workgroups share a CU, so more registers per wave would buy nothing).
+template <int NT, int EPT, int KMAX, bool MULTI, int MINW>
+__global__ __launch_bounds__(NT, MINW) void topk_ragged_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    auto& s = *reinterpret_cast<Smem<NT, EPT, KMAX>*>(smem_raw);
+    auto& s = *reinterpret_cast<SmemAll<NT, EPT, KMAX>*>(smem_raw);
     const int64_t items = MULTI ? (int64_t)p.B * p.tiles_per_row : (int64_t)p.B;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int b = MULTI ? (int)(it / p.tiles_per_row) : (int)it;

@@ -55,8 +55,10 @@ def assert_same(gi, gv, oi, ov, what: str) -> None:
 
 
 @contextlib.contextmanager
-def debug_overrides(path=None, stage_cap=None, multi_tile=None):
+def debug_overrides(path=None, stage_cap=None, multi_tile=None, fast=None):
     try:
+        if fast is not None:
+            detk.debug_set(detk.DETK_DEBUG_FAST, fast)
         if path is not None:
             detk.debug_set(detk.DETK_DEBUG_PATH, path)
         if stage_cap is not None:
@@ -68,3 +70,4 @@ def debug_overrides(path=None, stage_cap=None, multi_tile=None):
         detk.debug_set(detk.DETK_DEBUG_PATH, 0)
         detk.debug_set(detk.DETK_DEBUG_STAGING_CAP, -1)
         detk.debug_set(detk.DETK_DEBUG_MULTI_TILE, 0)
+        detk.debug_set(detk.DETK_DEBUG_FAST, 1)

@@ -46,7 +46,45 @@ def test_worked_examples(dev):
             assert gv.cpu().numpy().view(np.uint32)[0].tolist() == val, (row, k, path)
 
 
+def _quantized(B=12, L=12000, k=2048, name="gpu_quantized"):
+    """Few distinct values (multiples of 0.25 in [0, 4)): buckets full of equal keys."""
+    buf = np.empty(B * L, np.float32)
+    for b in range(B):
+        rng = W.row_rng(W.seed_of(name), b)
+        buf[b * L:(b + 1) * L] = (rng.integers(0, 16, L) * 0.25).astype(np.float32)
+    return W.Workload(name, buf, (np.arange(B) * L).astype(np.int32), np.full(B, L, np.int32), L, k)
+
+
+def _outliers(B=12, L=15000, k=2048, name="gpu_outliers"):
+    """ReLU-sum rows with a few huge values, infinities and NaNs of both signs."""
+    buf = np.empty(B * L, np.float32)
+    specials = np.array([0x7FC00000, 0x7F800000, 0x7F7FFFFF, 0x7F800001, 0xFFC00000, 0xFF800000, 0x80000000,
+                         0x00000001], np.uint32)
+    for b in range(B):
+        rng = W.row_rng(W.seed_of(name), b)
+        row = W.relu_sum_mixture(rng, L, 0.5).view(np.uint32)
+        pos = rng.choice(L, size=3 * b + 1, replace=False)
+        row[pos] = specials[rng.integers(0, specials.size, pos.size)]
+        buf[b * L:(b + 1) * L] = row.view(np.float32)
+    return W.Workload(name, buf, (np.arange(B) * L).astype(np.int32), np.full(B, L, np.int32), L, k)
+
+
+def _negative(B=8, L=9000, k=1500, name="gpu_negative"):
+    """All-negative rows (pivot below every non-negative key) with -0.0 and -inf mixed in."""
+    buf = np.empty(B * L, np.float32)
+    for b in range(B):
+        rng = W.row_rng(W.seed_of(name), b)
+        row = -np.abs(rng.standard_normal(L)).astype(np.float32)
+        row[rng.random(L) < 0.3] = -0.0
+        row[rng.random(L) < 0.05] = -np.inf
+        buf[b * L:(b + 1) * L] = row
+    return W.Workload(name, buf, (np.arange(B) * L).astype(np.int32), np.full(B, L, np.int32), L, k)
+
+
 SMALL = {
+    "quantized": _quantized,
+    "outliers": _outliers,
+    "negative": _negative,
     "plateau": lambda: W.plateau_abs(B=6, L=4096, k=2048, name="gpu_plateau"),
     "decode_ragged": lambda: W.decode_ragged(B=24, n_lo=1, n_hi=20000, k=2048, name="gpu_decode"),
     "prefill_causal": lambda: W.prefill_causal(Q=160, ctx=9000, k=2048, name="gpu_prefill"),
@@ -65,8 +103,8 @@ def _small(name):
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
-@pytest.mark.parametrize("shape", ["auto", "single", "multi4096", "multi8192", "single_rescan", "multi_rescan",
-                                   "multi_tinystage"])
+@pytest.mark.parametrize("shape", ["auto", "single", "single_exact", "single_pivot_miss", "multi4096", "multi8192",
+                                   "single_rescan", "multi_rescan", "multi_tinystage"])
 def test_small_workloads(dev, name, shape):
     wl = _small(name)
     if shape.startswith("single") and wl.max_len > 32768:
@@ -74,9 +112,11 @@ def test_small_workloads(dev, name, shape):
     cfg = {
         "auto": {},
         "single": {"path": 1},
+        "single_exact": {"path": 1, "fast": 0},
+        "single_pivot_miss": {"path": 1, "fast": 2},
         "multi4096": {"path": 2, "multi_tile": 4096},
         "multi8192": {"path": 2, "multi_tile": 8192},
-        "single_rescan": {"path": 1, "stage_cap": 0},
+        "single_rescan": {"path": 1, "stage_cap": 0, "fast": 0},
         "multi_rescan": {"path": 2, "multi_tile": 4096, "stage_cap": 0},
         "multi_tinystage": {"path": 2, "multi_tile": 4096, "stage_cap": 3},
     }[shape]
@@ -148,14 +188,14 @@ def _edge_workload(L, k, lens, name):
     return W.Workload(name, buf, (np.arange(B) * L).astype(np.int32), np.array(lens, np.int32), L, k)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 def test_edge_lengths(dev, path):
     k = 2048
     L = 16384
     lens = [0, 1, 2, k - 1, k, k + 1, 4095, 4096, 4097, 8191, 8192, 8193, 16383, 16384, -3, 99999]
     wl = _edge_workload(L, k, lens, "edge")
     log("edge lengths path %d" % path)
-    with debug_overrides(path=path, multi_tile=4096):
+    with debug_overrides(path=min(path, 2), multi_tile=4096, fast=0 if path == 3 else 1):
         gi, gv = run_gpu(wl, dev)
     oi, ov = run_oracle(wl)
     assert_same(gi, gv, oi, ov, "edge lengths path %d" % path)
