@@ -36,9 +36,9 @@ const void* kernel_ptr() {
     return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>);
 }
 
-template <int TILE, int KMAX>
+template <int TILE, int KMAX, bool MULTI>
 constexpr size_t smem_bytes() {
-    return sizeof(SmemAll<Shape<TILE>::NT, Shape<TILE>::EPT, KMAX>);
+    return sizeof(SmemAll<Shape<TILE>::NT, Shape<TILE>::EPT, KMAX, MULTI>);
 }
 
 struct DeviceInfo {
@@ -59,7 +59,7 @@ int g_fast = 1;             // 0 off, 1 on, 2 on with a pivot that always misses
 template <int TILE, int KMAX, bool MULTI>
 hipError_t prepare_kernel() {
     return hipFuncSetAttribute(kernel_ptr<TILE, KMAX, MULTI>(), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)smem_bytes<TILE, KMAX>());
+                               (int)smem_bytes<TILE, KMAX, MULTI>());
 }
 
 template <int TILE, int KMAX>
@@ -67,7 +67,7 @@ int multi_occupancy() {
     if (prepare_kernel<TILE, KMAX, true>() != hipSuccess) return 0;
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel_ptr<TILE, KMAX, true>(), Shape<TILE>::NT,
-                                                     smem_bytes<TILE, KMAX>()) != hipSuccess)
+                                                     smem_bytes<TILE, KMAX, true>()) != hipSuccess)
         return 0;
     return blocks;
 }
@@ -124,15 +124,17 @@ struct Plan {
     size_t off_zero = 0, n_zero_words = 0, off_ecnt = 0, off_stage = 0;
 };
 
-size_t lds_bytes(int tile, int kmax) {
+template <bool MULTI>
+size_t lds_bytes_t(int tile, int kmax) {
     const bool k2 = kmax == 2048;
     switch (tile) {
-    case 4096: return k2 ? smem_bytes<4096, 2048>() : smem_bytes<4096, 4096>();
-    case 8192: return k2 ? smem_bytes<8192, 2048>() : smem_bytes<8192, 4096>();
-    case 16384: return k2 ? smem_bytes<16384, 2048>() : smem_bytes<16384, 4096>();
-    default: return k2 ? smem_bytes<32768, 2048>() : smem_bytes<32768, 4096>();
+    case 4096: return k2 ? smem_bytes<4096, 2048, MULTI>() : smem_bytes<4096, 4096, MULTI>();
+    case 8192: return k2 ? smem_bytes<8192, 2048, MULTI>() : smem_bytes<8192, 4096, MULTI>();
+    case 16384: return k2 ? smem_bytes<16384, 2048, MULTI>() : smem_bytes<16384, 4096, MULTI>();
+    default: return k2 ? smem_bytes<32768, 2048, MULTI>() : smem_bytes<32768, 4096, MULTI>();
     }
 }
+size_t lds_bytes(int tile, int kmax, bool multi) { return multi ? lds_bytes_t<true>(tile, kmax) : lds_bytes_t<false>(tile, kmax); }
 
 int tile_index(int tile) { return tile == 4096 ? 0 : tile == 8192 ? 1 : 2; }
 
@@ -184,7 +186,7 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         off += (size_t)B * (size_t)k * 8;
         pl->ws_bytes = off;
     }
-    pl->lds = lds_bytes(pl->tile, pl->kmax);
+    pl->lds = lds_bytes(pl->tile, pl->kmax, pl->multi);
     if (pl->lds > dev.max_lds) return DETK_ERR_UNSUPPORTED;
     // int32 offsets: every window must be addressable with int32 row_starts + length.
     if ((int64_t)B * k >= ((int64_t)1 << 31)) return DETK_ERR_UNSUPPORTED;

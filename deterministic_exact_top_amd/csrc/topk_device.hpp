@@ -47,7 +47,8 @@ constexpr int kCandCap = 4096;                  // fast path: LDS candidate capa
 constexpr int kBuckets = 4096;                  // fast path: buckets over the candidate key range
 constexpr int kBucketBits = 12;
 constexpr int kBucketLimit = 256;               // fast path: largest bucket ranked by comparisons
-constexpr int kSamplesPerLane = 4;
+static_assert(kBuckets / 2 >= 256, "the packed bucket array doubles as the sample histogram");
+constexpr int kSamplesPerLane = 2;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 constexpr int kRowZeroWords = 4 * kRadix + 4;   // per-row words zeroed before a multi launch
 constexpr uint32_t kSpinLimit = 1u << 21;       // bounded wait (polls, ~1 us each) at row barriers
@@ -83,6 +84,28 @@ __device__ __forceinline__ uint32_t bits_of(uint32_t key) {
 
 // ----------------------------------------------------------------------------- wave helpers
 
+// A list of (key, position) pairs kept as two separate LDS arrays: a pair is never one
+// 64-bit store, which would make the register allocator pair every register-resident key
+// with a spare register.  pos passes through an empty asm so it is formed only where the
+// store happens.
+struct PairList {
+    uint32_t* key;
+    uint32_t* pos;
+    __device__ __forceinline__ void put(uint32_t i, uint32_t k, uint32_t p) const {
+        asm volatile("" : "+v"(p));
+        key[i] = k;
+        pos[i] = p;
+    }
+    // Composite (key << 32) | ~pos: unique, and its descending order is the canonical order.
+    __device__ __forceinline__ uint64_t composite(uint32_t i) const {
+        return ((uint64_t)key[i] << 32) | (uint32_t)~pos[i];
+    }
+    __device__ __forceinline__ void set_composite(uint32_t i, uint64_t c) const {
+        key[i] = (uint32_t)(c >> 32);
+        pos[i] = ~(uint32_t)c;
+    }
+};
+
 // threadIdx.x behind an empty asm: values derived from it are recomputed where they are
 // used instead of being hoisted out of the persistent item loop into (spilled) registers.
 __device__ __forceinline__ int opaque_tid() {
@@ -95,26 +118,39 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// DPP lane moves (gfx9 encodings): row_shr:n shifts within 16-lane rows, row_bcast:15 /
+// row_bcast:31 carry the last lane of a row / of the lower half into the next rows.
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele within rows, then row carries).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    x += dpp<kRowShr1, 0xF, true>(0, x);
+    x += dpp<kRowShr2, 0xF, true>(0, x);
+    x += dpp<kRowShr4, 0xF, true>(0, x);
+    x += dpp<kRowShr8, 0xF, true>(0, x);
+    x += dpp<kRowBcast15, 0xA, false>(0, x);
+    x += dpp<kRowBcast31, 0xC, false>(0, x);
     return x;
 }
 
+// Wave-wide max / min, returned to every lane.
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor(x, o, 64));
-    return x;
+    x = max(x, dpp<kRowShr1, 0xF, true>(0, x));
+    x = max(x, dpp<kRowShr2, 0xF, true>(0, x));
+    x = max(x, dpp<kRowShr4, 0xF, true>(0, x));
+    x = max(x, dpp<kRowShr8, 0xF, true>(0, x));
+    x = max(x, dpp<kRowBcast15, 0xA, false>(0, x));
+    x = max(x, dpp<kRowBcast31, 0xC, false>(0, x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
-
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor(x, o, 64));
-    return x;
+    const uint32_t y = ~x;  // min(x) = ~max(~x); zero-filled lanes stay neutral
+    return ~wave_max(y);
 }
 
 __device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
@@ -159,15 +195,20 @@ __device__ __forceinline__ void load_tile(uint32_t (&u)[EPT], const uint32_t* sr
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src), (short)0, nt * 4, kBufferWord3);
     const int tid = opaque_tid();
+    constexpr int G4 = EPT / 4;
+    constexpr int SG = G4 >= kSamplesPerLane ? G4 / kSamplesPerLane : 1;  // pivot-sample groups first
     if ((((uintptr_t)src) & 15u) == 0) {
 #pragma unroll
-        for (int v = 0; v < EPT / 4; ++v) {
-            const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (v * NT + tid) * 16, 0, 0);
-            u[4 * v + 0] = q[0];
-            u[4 * v + 1] = q[1];
-            u[4 * v + 2] = q[2];
-            u[4 * v + 3] = q[3];
-        }
+        for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+            for (int v = 0; v < G4; ++v) {
+                if ((v % SG == 0) != (pass == 0)) continue;
+                const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (v * NT + tid) * 16, 0, 0);
+                u[4 * v + 0] = q[0];
+                u[4 * v + 1] = q[1];
+                u[4 * v + 2] = q[2];
+                u[4 * v + 3] = q[3];
+            }
     } else {
 #pragma unroll
         for (int v = 0; v < EPT / 4; ++v)
@@ -179,11 +220,12 @@ __device__ __forceinline__ void load_tile(uint32_t (&u)[EPT], const uint32_t* sr
 
 // ----------------------------------------------------------------------------- shared memory
 
-template <int NT, int EPT, int KMAX>
+template <int NT, int EPT, int KMAX, int STAGE>
 struct ExactSmem {
     static constexpr int NW = NT / 64;
     static constexpr int TILE = NT * EPT;
     static constexpr int BWORDS = TILE / 32;
+    static constexpr int STAGE_CAP = STAGE;
     uint32_t whist[NW][kRadix];   // per-wave histograms
     uint32_t hist[kRadix];        // merged histogram of the current pass (row-global)
     uint32_t lhist[kRadix];       // this tile's own merged histogram
@@ -192,9 +234,10 @@ struct ExactSmem {
     uint32_t ctr[8];              // [0] staged, [1] A fill, [2] bcast, [3] bcast
     uint32_t bitmap[BWORDS];      // tie positions of this tile
     uint32_t wpre[BWORDS];        // exclusive prefix of popcounts over bitmap words
-    uint32_t skey[kStageCap];     // staged candidate keys
-    uint32_t sidx[kStageCap];     // staged candidate row indices
-    uint64_t A[KMAX];             // composites of selected elements above T
+    uint32_t skey[STAGE];         // staged candidate keys
+    uint32_t sidx[STAGE];         // staged candidate row indices
+    uint32_t akey[KMAX];          // selected elements above T: keys
+    uint32_t apos[KMAX];          //   and positions
 };
 
 template <int NT, int EPT, int KMAX>
@@ -202,22 +245,16 @@ struct FastSmem {
     static constexpr int NW = NT / 64;
     static constexpr int TILE = NT * EPT;
     static constexpr int BWORDS = TILE / 32;
-    static constexpr int CAPW = kCandCap / NW;   // candidate entries per wave region
     static constexpr int SCAP = KMAX + kBucketLimit;
-    uint32_t ctl[16];             // [0] pivot, [1] sample max, [2] candidate min, [3] b_t,
-                                  // [4] kept, [5] max bucket
+    uint32_t ctl[16];             // [1] sample max, [2] least sample above P, [3] b_t, [4] kept,
+                                  // [5] max bucket, [6..8] sample bin / above / count, [9] ties
     uint32_t wsum[32];
-    uint32_t sel[4];
-    uint32_t wcnt[NW][4];         // per wave: candidates (> P), ties (== P)
-    uint32_t hist[kRadix];        // sample radix select
     uint32_t bitmap[BWORDS];      // positions with key == P
-    uint32_t bucket[kBuckets];    // counts, then cursors / bucket ends
+    uint32_t bucket[kBuckets / 2];  // 16-bit bucket counters, cursors and ends, two per word;
+                                    // while choosing P, a 256-bin 32-bit sample histogram
     uint64_t S[SCAP];             // kept candidates as composites, grouped by bucket
     union {
-        struct {
-            uint32_t key[kCandCap];
-            uint16_t idx[kCandCap];
-        } cand;
+        uint2 cand[kCandCap];     // candidates: (raw bits, position)
         struct {
             uint32_t idx[KMAX];
             uint32_t val[KMAX];
@@ -225,14 +262,21 @@ struct FastSmem {
     } u;
 };
 
-template <int NT, int EPT, int KMAX>
+// Exact-path staging: smaller in one-workgroup-per-row kernels so that the LDS footprint
+// lets three rows share a CU.
+template <bool MULTI>
+constexpr int stage_entries() { return MULTI ? kStageCap : 2560; }
+
+template <int NT, int EPT, int KMAX, bool MULTI>
 union SmemAll {
-    ExactSmem<NT, EPT, KMAX> exact;
+    ExactSmem<NT, EPT, KMAX, stage_entries<MULTI>()> exact;
     FastSmem<NT, EPT, KMAX> fast;
 };
 
 // ----------------------------------------------------------------------------- block helpers
 
+// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.  One
+// barrier: `wsum` must not be written again before the caller's next barrier.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
     const int tid = threadIdx.x;
@@ -247,7 +291,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, 
         tot += v;
     }
     *total = tot;
-    __syncthreads();
     return off + incl - x;
 }
 
@@ -284,24 +327,25 @@ __device__ __forceinline__ void select_digit(const uint32_t* hist, uint32_t k_re
     __syncthreads();
 }
 
-// Descending bitonic sort of A[0..count) (count <= KMAX, KMAX a power of two).
+// Descending bitonic sort of the composites of A[0..count) (count <= KMAX, a power of
+// two).  Padding entries get composite 0, which no real element has (~pos != 0).
 template <int NT>
-__device__ __forceinline__ void bitonic_desc(uint64_t* A, int count) {
+__device__ __forceinline__ void bitonic_desc(const PairList& A, int count) {
     const int tid = threadIdx.x;
     int P = 1;
     while (P < count) P <<= 1;
-    for (int i = count + tid; i < P; i += NT) A[i] = 0;  // 0 is never a real composite
+    for (int i = count + tid; i < P; i += NT) A.set_composite(i, 0);
     __syncthreads();
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int i = tid; i < (P >> 1); i += NT) {
                 const int lo = 2 * i - (i & (stride - 1));
                 const int hi = lo + stride;
-                const uint64_t a = A[lo], b = A[hi];
+                const uint64_t a = A.composite(lo), b = A.composite(hi);
                 const bool desc = (lo & size) == 0;
                 if ((a < b) == desc) {
-                    A[lo] = b;
-                    A[hi] = a;
+                    A.set_composite(lo, b);
+                    A.set_composite(hi, a);
                 }
             }
             __syncthreads();
@@ -351,6 +395,8 @@ struct RowCtx {
 
 // ----------------------------------------------------------------------------- fast path
 
+constexpr uint32_t kRefineAbove = 24;  // pivot: resolve a third sample digit past this bin count
+
 // Try the pivot + bucket-rank path on a single-tile row (raw bits in u[]).  Returns
 // false, with LDS left dirty but registers untouched, when the row needs the exact path.
 template <int NT, int EPT, int KMAX>
@@ -358,247 +404,288 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
                                           int fast_mode) {
     using FS = FastSmem<NT, EPT, KMAX>;
     constexpr int G4 = EPT / 4;
-    constexpr int NW = FS::NW;
     constexpr int BW = FS::BWORDS;
-    constexpr int CAPW = FS::CAPW;
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     const int tid = opaque_tid();
-    const int wave = tid >> 6;
     const int lane = tid & 63;
     const int32_t nt = r.nt;
     const int32_t m = r.m;
 
     // ------------------------------------------------ clear LDS state
-    for (int i = tid; i < kBuckets; i += NT) s.bucket[i] = 0;
+    if (tid < kRadix) s.bucket[tid] = 0;
     for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
     if (tid < 16) s.ctl[tid] = tid == 2 ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot
-    // Samples: slots i * EPT / 4 (i < 4) of every lane, spread over the tile.
+    // Samples: slots i * EPT / kSamplesPerLane of every lane, spread over the tile.
     uint32_t sk[kSamplesPerLane];
     int nsamp = 0;  // valid samples in the whole workgroup (uniform)
     uint32_t smax = 0;
+    {
+        const int t4 = tid * 4;
 #pragma unroll
-    for (int i = 0; i < kSamplesPerLane; ++i) {
-        constexpr int step = EPT / kSamplesPerLane;
-        const int slot = i * step;
-        const int v = slot / 4, c = slot % 4;
-        const int pos = (v * NT + tid) * 4 + c;
-        const bool ok = pos < nt;
-        sk[i] = ok ? key_of(u[slot]) : 0u;
-        smax = max(smax, sk[i]);
-        const int lim = nt - v * NT * 4 - c;  // lanes of this sample row that are valid
-        nsamp += min(max((lim + 3) / 4, 0), NT);
+        for (int i = 0; i < kSamplesPerLane; ++i) {
+            constexpr int step = EPT / kSamplesPerLane;
+            const int slot = i * step;
+            const int v = slot / 4, c = slot % 4;
+            const bool ok = t4 + (v * NT * 4 + c) < nt;
+            sk[i] = ok ? key_of(u[slot]) : 0u;
+            smax = max(smax, sk[i]);
+            const int lim = nt - v * NT * 4 - c;  // lanes of this sample row that are valid
+            nsamp += min(max((lim + 3) / 4, 0), NT);
+        }
     }
     smax = wave_max(smax);
     __syncthreads();
     if (lane == 0) __hip_atomic_fetch_max(&s.ctl[1], smax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 
-    // r-th largest sample, r = expected share of the top m plus ~3.5 standard deviations.
+    // P: the low end of the 16-bit (or, for a crowded bin, 24-bit) key prefix holding the
+    // rr-th largest sample, rr = the expected share of the top m plus ~3.5 standard
+    // deviations, found with MSB-first 8-bit digit passes over the samples.
     uint32_t P = 0;
     {
         const float expct = (float)nsamp * (float)m / (float)nt;
-        // (r.fast == 2, a test setting, takes the largest sample: the pivot misses.)
+        // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
         const int rr = fast_mode == 2 ? 1 : (int)ceilf(expct + 3.5f * sqrtf(expct) + 4.0f);
         if (m < nt && rr < nsamp) {
             uint32_t prefix = 0, r_rem = (uint32_t)rr;
 #pragma unroll 1
-            for (int pass = 0; pass < 4; ++pass) {
+            for (int pass = 0; pass < 3; ++pass) {
                 const int shift = 24 - 8 * pass;
-                if (tid < kRadix) s.hist[tid] = 0;
+                if (pass == 2 && s.ctl[8] <= kRefineAbove) break;  // uniform: bin resolved
+                if (pass > 0 && tid < kRadix) s.bucket[tid] = 0;
                 __syncthreads();
 #pragma unroll
-                for (int i = 0; i < kSamplesPerLane; ++i) {
-                    const uint32_t kk = sk[i];
-                    const bool match = pass == 0 || (kk >> (shift + 8)) == prefix;
-                    if (match) hist_add(s.hist, (kk >> shift) & 0xFFu);
-                }
+                for (int i = 0; i < kSamplesPerLane; ++i)
+                    if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(s.bucket, (sk[i] >> shift) & 0xFFu);
                 __syncthreads();
-                select_digit<NT>(s.hist, r_rem, s.wsum, s.sel);
-                prefix = (prefix << 8) | s.sel[0];
-                r_rem -= s.sel[1];
-                __syncthreads();
+                select_digit<NT>(s.bucket, r_rem, s.wsum, s.ctl + 6);
+                prefix = (prefix << 8) | s.ctl[6];
+                r_rem -= s.ctl[7];
+                P = prefix << shift;
             }
-            P = prefix;
         }
     }
-    // Compare on raw bits when P is a non-negative float's key (the common case).
-    const int32_t pr = (int32_t)(P & 0x7FFFFFFFu);
+    const int32_t pr = (int32_t)(P & 0x7FFFFFFFu);  // P's float bits when P >= key(+0.0)
+    {  // smallest sample above P: the low end of the bucket range
+        uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < kSamplesPerLane; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
+        lo = wave_min(lo);
+        if (lane == 0) __hip_atomic_fetch_min(&s.ctl[2], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();  // sample extremes published; sample histogram no longer read
+    // Buckets: linear in the key over [L, U], L the smallest sample above P and U the
+    // largest sample; keys in (P, L) share bucket 0 and keys above U the top bucket.
+    // Starting at L rather than P keeps the resolution where the kept keys are when P
+    // sits on a plateau of equal scores far below them.
+    const uint32_t U = max(s.ctl[1], P);
+    const uint32_t L = min(s.ctl[2], U);
+    const int sh = max(0, (32 - __clz(U - L)) - kBucketBits);
+    auto bucket_of = [&](uint32_t kx) -> uint32_t {
+        return min((max(kx, L) - L) >> sh, (uint32_t)(kBuckets - 1));
+    };
+    for (int i = tid; i < kBuckets / 2; i += NT) s.bucket[i] = 0;
+    // 16-bit halves: bucket b lives in word b / 2, bits 16 * (b % 2) and up.
+    auto half_of = [](uint32_t word, uint32_t b) -> uint32_t { return (word >> ((b & 1u) << 4)) & 0xFFFFu; };
 
-    // ------------------------------------------------ one register pass: > P to the
-    // wave's candidate region, == P into the position bitmap.
-    uint32_t off = 0;        // wave-uniform fill of this wave's region
-    uint32_t neq = 0;        // this lane's count of keys == P
-    uint32_t cmin = 0xFFFFFFFFu;
-    uint32_t* ckey = s.u.cand.key + wave * CAPW;
-    uint16_t* cidx = s.u.cand.idx + wave * CAPW;
-    const int tid4 = tid * 4;
-    auto pass = [&](auto pos_tag) {
-        constexpr bool POS = decltype(pos_tag)::value;
+    // Visit register slots: f(x, slot constant c, group v, valid, 4 * thread).  Full groups
+    // skip the per-lane bound check.
+    auto slots = [&](auto&& f) {
+        const int t4 = opaque_tid() * 4;
 #pragma unroll
         for (int v = 0; v < G4; ++v) {
             const int lim = nt - v * NT * 4;
             if (lim <= 0) break;
-            const int llim = lim - tid4;  // valid slots of this lane in group v (may be <= 0 or > 4)
-            uint32_t nib = 0;
+            if (lim >= NT * 4) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t x = u[4 * v + c];
-                bool gt, eq;
-                if constexpr (POS) {
-                    gt = (int32_t)x > pr;
-                    eq = x == (uint32_t)pr;
-                } else {
-                    const uint32_t kx = key_of(x);
-                    gt = kx > P;
-                    eq = kx == P;
-                }
-                const bool ok = c < llim;
-                gt = gt && ok;
-                eq = eq && ok;
-                nib |= (eq ? 1u : 0u) << c;
-                const uint64_t bal = __ballot(gt);
-                if (bal) {
-                    const uint32_t slot = off + lanes_below(bal);
-                    if (gt && slot < (uint32_t)CAPW) {
-                        const uint32_t kx = key_of(x);
-                        ckey[slot] = kx;
-                        cidx[slot] = (uint16_t)(tid4 + (v * NT * 4 + c));
-                        cmin = min(cmin, kx);
-                    }
-                    off += (uint32_t)__popcll(bal);
-                }
-            }
-            if (__ballot(nib != 0)) {
-                if (nib) {
-                    const int p0 = tid4 + v * NT * 4;
-                    __hip_atomic_fetch_or(&s.bitmap[p0 >> 5], nib << (p0 & 31), __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_WORKGROUP);
-                    neq += (uint32_t)__popc(nib);
-                }
+                for (int c = 0; c < 4; ++c) f(u[4 * v + c], c, v, true, t4);
+            } else {
+                const int llim = lim - t4;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) f(u[4 * v + c], c, v, c < llim, t4);
             }
         }
     };
+
+    // ------------------------------------------------ count pass: keys > P per lane
+    uint32_t cnt = 0;
     if (P >= 0x80000000u)
-        pass(std::true_type{});
+        slots([&](uint32_t x, int, int, bool ok, int) { cnt += ((int32_t)x > pr && ok) ? 1u : 0u; });
     else
-        pass(std::false_type{});
-    {
-        neq = wave_incl_scan(neq);  // lane 63 holds the wave total
-        cmin = wave_min(cmin);
-        if (lane == 63) {
-            s.wcnt[wave][0] = off;
-            s.wcnt[wave][1] = neq;
-        }
-        if (lane == 0) __hip_atomic_fetch_min(&s.ctl[2], cmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        slots([&](uint32_t x, int, int, bool ok, int) { cnt += (key_of(x) > P && ok) ? 1u : 0u; });
+    uint32_t c_gt;
+    uint32_t o = block_excl_scan<NT>(cnt, s.wsum, &c_gt);
+    if (c_gt > (uint32_t)kCandCap) return false;  // uniform
+    const bool ties = c_gt < (uint32_t)m;           // uniform: keys == P fill the tail
+
+    // ------------------------------------------------ write pass: (bits, position) of the
+    // candidates to LDS; keys == P into the position bitmap when the tail needs them.
+    uint32_t neq = 0;
+    auto write_pass = [&](auto pos_tag, auto eq_tag) {
+        constexpr bool POS = decltype(pos_tag)::value;
+        constexpr bool EQ = decltype(eq_tag)::value;
+        uint32_t nib = 0;
+        slots([&](uint32_t x, int c, int v, bool ok, int t4) {
+            const bool gt = POS ? (int32_t)x > pr : key_of(x) > P;
+            if (gt && ok) {
+                s.u.cand[o] = make_uint2(x, (uint32_t)(t4 + (v * NT * 4 + c)));
+                ++o;
+            }
+            if (EQ) {
+                const bool eq = POS ? x == (uint32_t)pr : key_of(x) == P;
+                nib |= (eq && ok ? 1u : 0u) << c;
+                if (c == 3) {
+                    if (nib) {
+                        const int p0 = t4 + v * NT * 4;
+                        __hip_atomic_fetch_or(&s.bitmap[p0 >> 5], nib << (p0 & 31), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_WORKGROUP);
+                        neq += (uint32_t)__popc(nib);
+                    }
+                    nib = 0;
+                }
+            }
+        });
+    };
+    if (P >= 0x80000000u) {
+        if (ties) write_pass(std::true_type{}, std::true_type{});
+        else write_pass(std::true_type{}, std::false_type{});
+    } else {
+        if (ties) write_pass(std::false_type{}, std::true_type{});
+        else write_pass(std::false_type{}, std::false_type{});
+    }
+    if (ties) {
+        neq = wave_incl_scan(neq);
+        if (lane == 63) lds_add(&s.ctl[9], neq);
     }
     __syncthreads();
-    uint32_t c_gt = 0, c_eq = 0;
-    bool overflow = false;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        c_gt += s.wcnt[w][0];
-        c_eq += s.wcnt[w][1];
-        overflow |= s.wcnt[w][0] > (uint32_t)CAPW;
-    }
-    if (overflow || c_gt + c_eq < (uint32_t)m) return false;  // uniform
+    if (ties && c_gt + s.ctl[9] < (uint32_t)m) return false;  // uniform: pivot missed
     const uint32_t mlim = min((uint32_t)m, c_gt);             // slots filled by candidates
 
-    // ------------------------------------------------ bucket counts
-    const uint32_t L = s.ctl[2];
-    const uint32_t U = max(s.ctl[1], L);
-    const uint32_t span = U - L;
-    const int sh = max(0, (32 - __clz(span)) - kBucketBits);
-    auto bucket_of = [&](uint32_t kx) -> uint32_t { return min((kx - L) >> sh, (uint32_t)(kBuckets - 1)); };
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t cnt = s.wcnt[w][0];
-        for (uint32_t j = tid; j < cnt; j += NT) lds_add(&s.bucket[bucket_of(s.u.cand.key[w * CAPW + j])], 1u);
+    // ------------------------------------------------ bucket counts (dense over candidates)
+    for (uint32_t j = tid; j < c_gt; j += NT) {
+        const uint32_t bk = bucket_of(key_of(s.u.cand[j].x));
+        lds_add(&s.bucket[bk >> 1], 1u << ((bk & 1u) << 4));
     }
     __syncthreads();
 
     // ------------------------------------------------ suffix scan: bucket starts
     // Thread t owns buckets [kBuckets - (t + 1) * BPT, kBuckets - t * BPT), scanned from
-    // the top, so rank offsets grow with t.
+    // the top, so rank offsets grow with t.  Kept buckets are those starting below m.
+    static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     uint32_t cnts[BPT];
     uint32_t tsum = 0;
-    const int btop = kBuckets - tid * BPT - 1;
+    const int btop = kBuckets - tid * BPT - 1;  // odd: the high half of word btop / 2
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-        cnts[i] = s.bucket[btop - i];
-        tsum += cnts[i];
+    for (int i = 0; i < BPT; i += 2) {
+        const uint32_t w = s.bucket[(btop - i) >> 1];
+        cnts[i] = w >> 16;           // bucket btop - i
+        cnts[i + 1] = w & 0xFFFFu;   // bucket btop - i - 1
+        tsum += cnts[i] + cnts[i + 1];
     }
     uint32_t total;
-    uint32_t run = block_excl_scan<NT>(tsum, s.wsum, &total);
+    uint32_t run = block_excl_scan<NT>(tsum, s.wsum + 16, &total);
+    uint32_t mx = 0;
+    uint32_t hi_start = 0;
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
         const uint32_t st = run;
-        s.bucket[btop - i] = st;  // cursor starts at the bucket's first slot
-        if (c_gt >= (uint32_t)m && st < (uint32_t)m && st + cnts[i] >= (uint32_t)m) {
+        if ((i & 1) == 0) {
+            hi_start = st;
+        } else {
+            s.bucket[(btop - i) >> 1] = (hi_start << 16) | st;  // cursors start at first slots
+        }
+        if (ties || st < (uint32_t)m) mx = max(mx, cnts[i]);
+        if (!ties && st < (uint32_t)m && st + cnts[i] >= (uint32_t)m) {
             s.ctl[3] = (uint32_t)(btop - i);  // threshold bucket
             s.ctl[4] = st + cnts[i];          // kept candidates (slots of buckets >= b_t)
         }
         run += cnts[i];
     }
+    mx = wave_max(mx);
+    if (lane == 0) __hip_atomic_fetch_max(&s.ctl[5], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __syncthreads();
-    const uint32_t bt = c_gt >= (uint32_t)m ? s.ctl[3] : 0u;
-    const uint32_t kept = c_gt >= (uint32_t)m ? s.ctl[4] : c_gt;
-    {
-        uint32_t mx = 0;
-#pragma unroll
-        for (int i = 0; i < BPT; ++i)
-            if ((uint32_t)(btop - i) >= bt) mx = max(mx, cnts[i]);
-        mx = wave_max(mx);
-        if (lane == 0) __hip_atomic_fetch_max(&s.ctl[5], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    __syncthreads();
+    const uint32_t bt = ties ? 0u : s.ctl[3];
+    const uint32_t kept = ties ? c_gt : s.ctl[4];
     if (kept > (uint32_t)FS::SCAP || s.ctl[5] > (uint32_t)kBucketLimit) return false;  // uniform
 
     // ------------------------------------------------ scatter kept candidates by bucket
+    constexpr int SUNR = 2;
+    for (uint32_t j0 = 0; j0 < c_gt; j0 += SUNR * NT) {
+        uint2 cv[SUNR];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t cnt = s.wcnt[w][0];
-        for (uint32_t j = tid; j < cnt; j += NT) {
-            const uint32_t kx = s.u.cand.key[w * CAPW + j];
-            const uint32_t bk = bucket_of(kx);
-            if (bk >= bt) {
-                const uint32_t pos = __hip_atomic_fetch_add(&s.bucket[bk], 1u, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_WORKGROUP);
-                if (pos < (uint32_t)FS::SCAP)
-                    s.S[pos] = ((uint64_t)kx << 32) | (uint32_t)~(uint32_t)s.u.cand.idx[w * CAPW + j];
-            }
+        for (int i = 0; i < SUNR; ++i) {
+            const uint32_t j = j0 + i * NT + tid;
+            cv[i] = j < c_gt ? s.u.cand[j] : make_uint2(0u, 0u);
         }
+        uint32_t pos[SUNR], kk[SUNR];
+#pragma unroll
+        for (int i = 0; i < SUNR; ++i) {
+            kk[i] = key_of(cv[i].x);
+            const uint32_t bk = bucket_of(kk[i]);
+            pos[i] = 0xFFFFFFFFu;
+            if (j0 + i * NT + tid < c_gt && bk >= bt)
+                pos[i] = half_of(__hip_atomic_fetch_add(&s.bucket[bk >> 1], 1u << ((bk & 1u) << 4), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_WORKGROUP),
+                                 bk);
+        }
+#pragma unroll
+        for (int i = 0; i < SUNR; ++i)
+            if (pos[i] < (uint32_t)FS::SCAP) s.S[pos[i]] = ((uint64_t)kk[i] << 32) | (uint32_t)~cv[i].y;
     }
     __syncthreads();
 
     // ------------------------------------------------ rank inside buckets -> final slot
-    // s.bucket[b] now holds the end of bucket b; its start is the end of bucket b + 1.
-    for (uint32_t q = tid; q < kept; q += NT) {
-        const uint64_t c = s.S[q];
-        const uint32_t bk = bucket_of((uint32_t)(c >> 32));
-        const uint32_t e = min(s.bucket[bk], kept);
-        const uint32_t st = bk == (uint32_t)(kBuckets - 1) ? 0u : s.bucket[bk + 1];
-        uint32_t rank = 0;
-        for (uint32_t f = st; f < e; ++f) rank += s.S[f] > c ? 1u : 0u;
-        const uint32_t slot = st + rank;
-        if (slot < mlim) {
-            s.u.out.idx[slot] = ~(uint32_t)c;
-            s.u.out.val[slot] = bits_of((uint32_t)(c >> 32));
+    // Bucket b's counter now holds its end; its start is the end of bucket b + 1.  Each
+    // lane ranks RUNR elements at once; the comparison loop runs the wave's largest
+    // bucket length, uniformly.
+    constexpr int RUNR = 2;
+    for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
+        uint64_t cc[RUNR];
+        uint32_t st[RUNR], len[RUNR], rank[RUNR];
+        uint32_t lmax = 0;
+#pragma unroll
+        for (int i = 0; i < RUNR; ++i) {
+            const uint32_t q = q0 + i * NT + tid;
+            const bool in = q < kept;
+            cc[i] = in ? s.S[q] : 0ull;
+            const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
+            const uint32_t en = in ? min(half_of(s.bucket[bk >> 1], bk), kept) : 0u;
+            st[i] = bk == (uint32_t)(kBuckets - 1) ? 0u : half_of(s.bucket[(bk + 1) >> 1], bk + 1);
+            len[i] = en > st[i] ? en - st[i] : 0u;
+            lmax = max(lmax, len[i]);
+            rank[i] = 0;
+        }
+        lmax = wave_max(lmax);
+        for (uint32_t f = 0; f < lmax; ++f) {
+#pragma unroll
+            for (int i = 0; i < RUNR; ++i) {
+                const uint64_t other = s.S[f < len[i] ? st[i] + f : 0u];
+                rank[i] += (f < len[i] && other > cc[i]) ? 1u : 0u;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RUNR; ++i) {
+            const uint32_t slot = st[i] + rank[i];
+            if (q0 + i * NT + tid < kept && slot < mlim) {
+                s.u.out.idx[slot] = ~(uint32_t)cc[i];
+                s.u.out.val[slot] = bits_of((uint32_t)(cc[i] >> 32));
+            }
         }
     }
 
     // ------------------------------------------------ ties at P: smallest positions
-    if (c_gt < (uint32_t)m) {
+    if (ties) {
         const uint32_t need = (uint32_t)m - c_gt;
         constexpr int WPT = (BW + NT - 1) / NT;
-        uint32_t cnt = 0;
+        uint32_t tc = 0;
 #pragma unroll
         for (int q = 0; q < WPT; ++q) {
             const int w = tid * WPT + q;
-            if (w < BW) cnt += (uint32_t)__popc(s.bitmap[w]);
+            if (w < BW) tc += (uint32_t)__popc(s.bitmap[w]);
         }
         uint32_t tot;
-        uint32_t rr = block_excl_scan<NT>(cnt, s.wsum, &tot);
+        uint32_t rr = block_excl_scan<NT>(tc, s.wsum, &tot);
         const uint32_t vP = bits_of(P);
 #pragma unroll
         for (int q = 0; q < WPT; ++q) {
@@ -629,12 +716,12 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
 
 // ----------------------------------------------------------------------------- exact path
 
-template <int NT, int EPT, int KMAX, bool MULTI>
-__device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ExactSmem<NT, EPT, KMAX>& s,
-                                           const uint32_t (&key)[EPT]) {
+template <int NT, int EPT, int KMAX, bool MULTI, typename ES>
+__device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES& s, const uint32_t (&key)[EPT]) {
     constexpr int G4 = EPT / 4;
-    constexpr int BW = ExactSmem<NT, EPT, KMAX>::BWORDS;
-    constexpr int NW = ExactSmem<NT, EPT, KMAX>::NW;
+    constexpr int BW = ES::BWORDS;
+    constexpr int NW = ES::NW;
+    constexpr int SCAPX = ES::STAGE_CAP;
     const int tid = opaque_tid();
     const int wave = tid >> 6;
     const bool multi = MULTI && r.multi;
@@ -646,29 +733,33 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
     uint32_t* rw = multi ? p.ws_zero + 1 + (int64_t)b * kRowZeroWords : nullptr;  // row words
     uint32_t* err = p.ws_zero;
     uint32_t bar_target = 0;
+    const PairList A{s.akey, s.apos};
 
-    const int tid4 = tid * 4;
     // Visit every valid register element: f(key, local index).
+    // (Each visit re-reads the thread index so per-slot positions are not kept live
+    // across passes.)
     auto for_each = [&](auto&& f) {
+        const int t4 = opaque_tid() * 4;
 #pragma unroll
         for (int v = 0; v < G4; ++v) {
             const int lim = nt - v * NT * 4;
             if (lim <= 0) break;
-            const int llim = lim - tid4;
+            const int llim = lim - t4;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (c < llim) f(key[4 * v + c], tid4 + (v * NT * 4 + c));
+                if (c < llim) f(key[4 * v + c], t4 + (v * NT * 4 + c));
         }
     };
     // Same, but every lane of the wave calls f (valid flag passed) -- for ballots.
     auto for_each_conv = [&](auto&& f) {
+        const int t4 = opaque_tid() * 4;
 #pragma unroll
         for (int v = 0; v < G4; ++v) {
             const int lim = nt - v * NT * 4;
             if (lim <= 0) break;
-            const int llim = lim - tid4;
+            const int llim = lim - t4;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) f(key[4 * v + c], tid4 + (v * NT * 4 + c), c < llim);
+            for (int c = 0; c < 4; ++c) f(key[4 * v + c], t4 + (v * NT * 4 + c), c < llim);
         }
     };
 
@@ -709,7 +800,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
     uint32_t prefix = s.sel[0];
     uint32_t k_rem = (uint32_t)m - s.sel[1];
     const uint32_t d0 = prefix;
-    const bool staged = s.lhist[d0] <= (uint32_t)p.stage_cap;
+    const bool staged = s.lhist[d0] <= (uint32_t)min(p.stage_cap, SCAPX);
     __syncthreads();
 
     // Collect: digit > d0 are selected outright (into A); digit == d0 are candidates
@@ -718,18 +809,20 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
         const uint32_t d = kk >> 24;
         const bool g = ok && d > d0;
         const uint32_t sa = claim_slot(g, &s.ctr[1]);
-        if (g && sa < (uint32_t)KMAX) s.A[sa] = ((uint64_t)kk << 32) | (uint32_t)~(uint32_t)(j0 + jl);
+        if (g && sa < (uint32_t)KMAX) A.put(sa, kk, (uint32_t)(j0 + jl));
         if (staged) {
             const bool cnd = ok && d == d0;
             const uint32_t sc = claim_slot(cnd, &s.ctr[0]);
-            if (cnd && sc < (uint32_t)kStageCap) {
+            if (cnd && sc < (uint32_t)SCAPX) {
+                uint32_t j = (uint32_t)(j0 + jl);
+                asm volatile("" : "+v"(j));
                 s.skey[sc] = kk;
-                s.sidx[sc] = (uint32_t)(j0 + jl);
+                s.sidx[sc] = j;
             }
         }
     });
     __syncthreads();
-    const uint32_t nstaged = staged ? min(s.ctr[0], (uint32_t)kStageCap) : 0u;
+    const uint32_t nstaged = staged ? min(s.ctr[0], (uint32_t)SCAPX) : 0u;
 
     // ---------------------------------------------------------------- passes 1..3: refine
 #pragma unroll 1
@@ -765,13 +858,13 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
             const uint32_t kk = i < nstaged ? s.skey[i] : 0u;
             const bool g = i < nstaged && kk > T;
             const uint32_t sa = claim_slot(g, &s.ctr[1]);
-            if (g && sa < (uint32_t)KMAX) s.A[sa] = ((uint64_t)kk << 32) | (uint32_t)~s.sidx[i];
+            if (g && sa < (uint32_t)KMAX) A.put(sa, kk, s.sidx[i]);
         }
     } else {
         for_each_conv([&](uint32_t kk, int jl, bool ok) {
             const bool g = ok && (kk >> 24) == d0 && kk > T;
             const uint32_t sa = claim_slot(g, &s.ctr[1]);
-            if (g && sa < (uint32_t)KMAX) s.A[sa] = ((uint64_t)kk << 32) | (uint32_t)~(uint32_t)(j0 + jl);
+            if (g && sa < (uint32_t)KMAX) A.put(sa, kk, (uint32_t)(j0 + jl));
         });
     }
 
@@ -848,11 +941,10 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
     // ---------------------------------------------------------------- sort G and store
     const uint32_t nA = min(s.ctr[1], cnt_gt);
     if (!multi) {
-        bitonic_desc<NT>(s.A, (int)nA);
+        bitonic_desc<NT>(A, (int)nA);
         for (uint32_t q = tid; q < nA; q += NT) {
-            const uint64_t c = s.A[q];
-            oidx[q] = (int32_t)~(uint32_t)c;
-            if (oval) oval[q] = bits_of((uint32_t)(c >> 32));
+            oidx[q] = (int32_t)s.apos[q];
+            if (oval) oval[q] = bits_of(s.akey[q]);
         }
         write_padding<NT>(oidx, oval, m, k);
         return;
@@ -865,7 +957,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
         uint64_t* st = p.ws_stage + (int64_t)b * k;
         const uint32_t gb = s.ctr[2];
         for (uint32_t q = tid; q < nA; q += NT)
-            if (gb + q < cnt_gt) st[gb + q] = s.A[q];
+            if (gb + q < cnt_gt) st[gb + q] = A.composite(q);
     }
     __threadfence();
     __syncthreads();
@@ -880,14 +972,13 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
     {
         const uint64_t* st = p.ws_stage + (int64_t)b * k;
         for (uint32_t q = tid; q < cnt_gt; q += NT)
-            s.A[q] = __hip_atomic_load(&st[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            A.set_composite(q, __hip_atomic_load(&st[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     }
     __syncthreads();
-    bitonic_desc<NT>(s.A, (int)cnt_gt);
+    bitonic_desc<NT>(A, (int)cnt_gt);
     for (uint32_t q = tid; q < cnt_gt; q += NT) {
-        const uint64_t c = s.A[q];
-        oidx[q] = (int32_t)~(uint32_t)c;
-        if (oval) oval[q] = bits_of((uint32_t)(c >> 32));
+        oidx[q] = (int32_t)s.apos[q];
+        if (oval) oval[q] = bits_of(s.akey[q]);
     }
     write_padding<NT>(oidx, oval, m, k);
 }
@@ -895,7 +986,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, Exa
 // ----------------------------------------------------------------------------- one item
 
 template <int NT, int EPT, int KMAX, bool MULTI>
-__device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX>& s, int b, int tile) {
+__device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, int b, int tile) {
     constexpr int TILE = NT * EPT;
     RowCtx r;
     const int32_t len = p.lengths ? p.lengths[b] : p.max_len;
@@ -937,7 +1028,7 @@ __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, K
 template <int NT, int EPT, int KMAX, bool MULTI, int MINW>
 __global__ __launch_bounds__(NT, MINW) void topk_ragged_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    auto& s = *reinterpret_cast<SmemAll<NT, EPT, KMAX>*>(smem_raw);
+    auto& s = *reinterpret_cast<SmemAll<NT, EPT, KMAX, MULTI>*>(smem_raw);
     const int64_t items = MULTI ? (int64_t)p.B * p.tiles_per_row : (int64_t)p.B;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int b = MULTI ? (int)(it / p.tiles_per_row) : (int)it;
