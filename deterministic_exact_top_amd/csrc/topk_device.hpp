@@ -364,22 +364,35 @@ __device__ __forceinline__ void write_padding(int32_t* oidx, uint32_t* oval, int
 
 // ----------------------------------------------------------------------------- row barrier
 
+// Wait until this wave's outstanding global stores and atomics have completed (reached
+// the L2, or memory for device-scope atomics), so that a release issued afterwards by
+// another wave of the workgroup covers them.  A workgroup barrier alone does not wait
+// for them.
+__device__ __forceinline__ void wait_global_writes() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Arrive at a row barrier and wait until `target` arrivals are counted.  Every wave
+// first waits for its own global writes; then one thread per workgroup talks to the
+// counter: a release add (one L2 write-back) makes the workgroup's global writes
+// visible device-wide, the wait polls with relaxed coherent loads (an acquire per poll
+// would invalidate the L2 each time), and one acquire fence after the wait makes the
+// other workgroups' writes visible.  The wait is bounded: past kSpinLimit polls it flags
+// `err` and returns.
 __device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
-    __threadfence();
+    wait_global_writes();
     __syncthreads();
     if (threadIdx.x == 0) {
         __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(2);
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
                 __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
-    __threadfence();
 }
 
 // ----------------------------------------------------------------------------- row context
@@ -959,16 +972,15 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
         for (uint32_t q = tid; q < nA; q += NT)
             if (gb + q < cnt_gt) st[gb + q] = A.composite(q);
     }
-    __threadfence();
+    wait_global_writes();
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0) {  // release this tile's stage writes; the last arriver acquires all of them
         const uint32_t old = __hip_atomic_fetch_add(&rw[4 * kRadix + 1], 1u, __ATOMIC_ACQ_REL,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         s.ctr[3] = (old == (uint32_t)ntiles - 1u) ? 1u : 0u;
     }
     __syncthreads();
     if (s.ctr[3] == 0) return;
-    __threadfence();
     {
         const uint64_t* st = p.ws_stage + (int64_t)b * k;
         for (uint32_t q = tid; q < cnt_gt; q += NT)
