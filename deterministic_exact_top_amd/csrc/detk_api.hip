@@ -121,7 +121,7 @@ struct Plan {
     size_t lds = 0;
     size_t ws_bytes = 0;
     // workspace layout (bytes from the start)
-    size_t off_zero = 0, n_zero_words = 0, off_ecnt = 0, off_stage = 0;
+    size_t off_zero = 0, n_zero_words = 0, off_ecnt = 0, off_stage = 0, off_cand = 0;
 };
 
 template <bool MULTI>
@@ -184,6 +184,9 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         off = (off + 255) & ~(size_t)255;
         pl->off_stage = off;
         off += (size_t)B * (size_t)k * 8;
+        off = (off + 255) & ~(size_t)255;
+        pl->off_cand = off;
+        off += (size_t)B * (size_t)(pl->kmax == 2048 ? detk::cand_cap<2048>() : detk::cand_cap<4096>()) * 8;
         pl->ws_bytes = off;
     }
     pl->lds = lds_bytes(pl->tile, pl->kmax, pl->multi);
@@ -278,11 +281,13 @@ int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32
     p.ws_zero = nullptr;
     p.ws_ecnt = nullptr;
     p.ws_stage = nullptr;
+    p.ws_cand = nullptr;
     if (pl.multi) {
         unsigned char* ws = static_cast<unsigned char*>(workspace);
         p.ws_zero = reinterpret_cast<uint32_t*>(ws + pl.off_zero);
         p.ws_ecnt = reinterpret_cast<uint32_t*>(ws + pl.off_ecnt);
         p.ws_stage = reinterpret_cast<uint64_t*>(ws + pl.off_stage);
+        p.ws_cand = reinterpret_cast<uint2*>(ws + pl.off_cand);
         const int64_t nz = (int64_t)pl.n_zero_words;
         int zgrid = (int)((nz + 255) / 256);
         if (zgrid > 1024) zgrid = 1024;

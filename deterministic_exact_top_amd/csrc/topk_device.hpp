@@ -43,14 +43,26 @@ namespace detk {
 
 constexpr int kRadix = 256;
 constexpr int kStageCap = 4096;                 // exact path: LDS threshold-bin staging (entries)
-constexpr int kCandCap = 4096;                  // fast path: LDS candidate capacity (entries)
 constexpr int kBuckets = 4096;                  // fast path: buckets over the candidate key range
 constexpr int kBucketBits = 12;
 constexpr int kBucketLimit = 256;               // fast path: largest bucket ranked by comparisons
 static_assert(kBuckets / 2 >= 256, "the packed bucket array doubles as the sample histogram");
 constexpr int kSamplesPerLane = 2;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
-constexpr int kRowZeroWords = 4 * kRadix + 4;   // per-row words zeroed before a multi launch
+// Per-row workspace words of the multi-workgroup path, zeroed before each launch.
+constexpr int kRowHist = 0;                     // exact path: 4 pass histograms
+constexpr int kRowBar = 4 * kRadix;             // row barrier counter (both paths)
+constexpr int kRowArrive = kRowBar + 1;         // exact path: arrivals after staging
+constexpr int kRowStage = kRowBar + 2;          // exact path: staged composites
+constexpr int kRowSampHist = kRowBar + 4;       // pivot path: 4 sample-digit histograms
+constexpr int kRowFast = kRowSampHist + 4 * kRadix;  // pivot path control words:
+constexpr int kRowCgt = kRowFast + 0;           //   keys above P (claims candidate space)
+constexpr int kRowEq = kRowFast + 1;            //   keys equal to P
+constexpr int kRowNotLo = kRowFast + 2;         //   ~(least sample above P), by max
+constexpr int kRowUAll = kRowFast + 3;          //   largest sample
+constexpr int kRowUFin = kRowFast + 4;          //   largest sample below key(+inf)
+constexpr int kRowFastArrive = kRowFast + 5;    //   arrivals after writing candidates
+constexpr int kRowZeroWords = kRowFast + 12;
 constexpr uint32_t kSpinLimit = 1u << 21;       // bounded wait (polls, ~1 us each) at row barriers
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer resource, gfx9-family data format
 
@@ -69,6 +81,7 @@ struct Params {
     uint32_t* ws_zero;          // [0] error word, then B * kRowZeroWords (zeroed per call)
     uint32_t* ws_ecnt;          // B * tiles_per_row
     uint64_t* ws_stage;         // B * k
+    uint2* ws_cand;             // B * cand_cap(KMAX): pivot-path candidates (bits, position)
 };
 
 // ----------------------------------------------------------------------------- bits
@@ -240,27 +253,48 @@ struct ExactSmem {
     uint32_t apos[KMAX];          //   and positions
 };
 
+// Candidate capacity of the pivot paths: keys above the pivot, at most twice KMAX.
+template <int KMAX>
+constexpr int cand_cap() { return 2 * KMAX; }
+
 template <int NT, int EPT, int KMAX>
 struct FastSmem {
     static constexpr int NW = NT / 64;
     static constexpr int TILE = NT * EPT;
     static constexpr int BWORDS = TILE / 32;
+    static constexpr int CCAP = cand_cap<KMAX>();
     static constexpr int SCAP = KMAX + kBucketLimit;
-    uint32_t ctl[16];             // [1] sample max, [2] least sample above P, [3] b_t, [4] kept,
-                                  // [5] max bucket, [6..8] sample bin / above / count, [9] ties
+    uint32_t ctl[16];             // control words, kCtl* below
     uint32_t wsum[32];
     uint32_t bitmap[BWORDS];      // positions with key == P
     uint32_t bucket[kBuckets / 2];  // 16-bit bucket counters, cursors and ends, two per word;
                                     // while choosing P, a 256-bin 32-bit sample histogram
     uint64_t S[SCAP];             // kept candidates as composites, grouped by bucket
     union {
-        uint2 cand[kCandCap];     // candidates: (raw bits, position)
+        uint2 cand[CCAP];         // candidates: (raw bits, position)
         struct {
             uint32_t idx[KMAX];
             uint32_t val[KMAX];
         } out;
     } u;
 };
+
+// Pivot path of a row split over several workgroups: candidates live in the workspace,
+// so LDS holds only the tile's tie bitmap, the buckets and the kept composites (the last
+// workgroup of the row ranks every candidate, so S takes the whole capacity).
+template <int NT, int EPT, int KMAX>
+struct MultiFastSmem {
+    static constexpr int TILE = NT * EPT;
+    static constexpr int BWORDS = TILE / 32;
+    static constexpr int SCAP = cand_cap<KMAX>();
+    uint32_t ctl[16];
+    uint32_t wsum[32];
+    uint32_t bitmap[BWORDS];
+    uint32_t bucket[kBuckets / 2];
+    uint64_t S[SCAP];
+};
+
+struct NoSmem {};
 
 // Exact-path staging: smaller in one-workgroup-per-row kernels so that the LDS footprint
 // lets three rows share a CU.
@@ -271,6 +305,7 @@ template <int NT, int EPT, int KMAX, bool MULTI>
 union SmemAll {
     ExactSmem<NT, EPT, KMAX, stage_entries<MULTI>()> exact;
     FastSmem<NT, EPT, KMAX> fast;
+    typename std::conditional<MULTI, MultiFastSmem<NT, EPT, KMAX>, NoSmem>::type mfast;
 };
 
 // ----------------------------------------------------------------------------- block helpers
@@ -408,129 +443,331 @@ struct RowCtx {
 
 // ----------------------------------------------------------------------------- fast path
 
-constexpr uint32_t kRefineAbove = 24;  // pivot: resolve a third sample digit past this bin count
+constexpr uint32_t kRefineAbove = 24;         // pivot: resolve one more sample digit past this bin count
+constexpr uint32_t kKeyPosInf = 0xFF800000u;  // key of +inf; keys at or above it are +inf and +NaN
 
-// Try the pivot + bucket-rank path on a single-tile row (raw bits in u[]).  Returns
-// false, with LDS left dirty but registers untouched, when the row needs the exact path.
+// Fast-path LDS control words.
+enum : int {
+    kCtlSmaxAll = 1,    // largest sample key
+    kCtlLo = 2,         // least sample key above P (all ones when there is none)
+    kCtlBt = 3,         // threshold bucket
+    kCtlKept = 4,       // kept candidates
+    kCtlMaxBucket = 5,  // longest kept bucket
+    kCtlSel = 6,        // [6..8] sample digit select: digit, count above, bin count
+    kCtlEq = 9,         // keys equal to P
+    kCtlSmaxFin = 10,   // largest sample key below key(+inf)
+    kCtlBase = 11,      // several workgroups: this tile's first candidate slot in the row
+    kCtlLast = 12,      // several workgroups: this tile arrived last
+    kCtlTieOff = 13,    // several workgroups: keys equal to P in earlier tiles
+};
+
+// Real samples among a tile's nt elements (uniform): slot i * EPT / kSamplesPerLane of
+// each lane, for the lanes whose slot lies inside the tile.
+template <int NT, int EPT>
+__device__ __forceinline__ int tile_samples(int32_t nt) {
+    int ns = 0;
+#pragma unroll
+    for (int i = 0; i < kSamplesPerLane; ++i) {
+        const int slot = i * (EPT / kSamplesPerLane);
+        const int lim = nt - (slot / 4) * NT * 4 - slot % 4;
+        ns += min(max((lim + 3) / 4, 0), NT);
+    }
+    return ns;
+}
+
+// This lane's samples: register slots i * EPT / kSamplesPerLane (the groups load_tile
+// issues first).  Slots past the tile give key 0, the least key, which never outranks a
+// real sample at the ranks asked for.
+template <int NT, int EPT>
+__device__ __forceinline__ void take_samples(const uint32_t (&u)[EPT], int32_t nt, uint32_t (&sk)[kSamplesPerLane]) {
+    const int t4 = opaque_tid() * 4;
+#pragma unroll
+    for (int i = 0; i < kSamplesPerLane; ++i) {
+        const int slot = i * (EPT / kSamplesPerLane);
+        sk[i] = t4 + ((slot / 4) * NT * 4 + slot % 4) < nt ? key_of(u[slot]) : 0u;
+    }
+}
+
+// Sample rank whose key bounds the m-th largest of n keys from below with high
+// probability: the expected rank of that key among nsamp samples plus 3.5 standard
+// deviations plus 4.
+__device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) {
+    const float expct = (float)nsamp * (float)m / (float)n;
+    return (uint32_t)ceilf(expct + 3.5f * sqrtf(expct) + 4.0f);
+}
+
+// P = the key prefix of the rr-th largest sample, MSB first, one 8-bit digit per pass;
+// a pass runs past the second only while the selected bin still holds more than
+// kRefineAbove samples, so after four passes P is that sample's key itself.  `hist` is
+// 256 LDS words; merge(pass, hist) turns this workgroup's histogram into the one the
+// select reads (nothing to do for a single workgroup, a device-wide sum over the row's
+// tiles otherwise).  Every workgroup of a row takes the same decisions.
+template <int NT, class Merge>
+__device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist,
+                                                 uint32_t* wsum, uint32_t* sel, Merge&& merge) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, r_rem = rr, P = 0;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        if (pass >= 2 && sel[2] <= kRefineAbove) break;  // uniform: bin resolved
+        if (tid < kRadix) hist[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSamplesPerLane; ++i)
+            if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(hist, (sk[i] >> shift) & 0xFFu);
+        __syncthreads();
+        merge(pass, hist);
+        select_digit<NT>(hist, r_rem, wsum, sel);
+        prefix = (prefix << 8) | sel[0];
+        r_rem -= sel[1];
+        P = prefix << shift;
+    }
+    return P;
+}
+
+// Visit the tile's register slots: f(x, slot constant c, group v, valid, 4 * thread).
+// Full groups skip the per-lane bound check.
+template <int NT, int EPT, class F>
+__device__ __forceinline__ void visit_slots(const uint32_t (&u)[EPT], int32_t nt, F&& f) {
+    const int t4 = opaque_tid() * 4;
+#pragma unroll
+    for (int v = 0; v < EPT / 4; ++v) {
+        const int lim = nt - v * NT * 4;
+        if (lim <= 0) break;
+        if (lim >= NT * 4) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) f(u[4 * v + c], c, v, true, t4);
+        } else {
+            const int llim = lim - t4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) f(u[4 * v + c], c, v, c < llim, t4);
+        }
+    }
+}
+
+// Keys above P, compared on the raw bits when P >= key(+0.0) (then only non-negative
+// patterns qualify and their signed order is the key order).
+struct AboveP {
+    uint32_t P;
+    int32_t pr;  // P's float bits when P >= key(+0.0)
+    __device__ explicit AboveP(uint32_t p) : P(p), pr((int32_t)(p & 0x7FFFFFFFu)) {}
+    template <bool POS>
+    __device__ __forceinline__ bool gt(uint32_t x) const { return POS ? (int32_t)x > pr : key_of(x) > P; }
+    template <bool POS>
+    __device__ __forceinline__ bool eq(uint32_t x) const { return POS ? x == (uint32_t)pr : key_of(x) == P; }
+};
+
+// Order the candidates: the m largest of the c_gt candidates (all of them when
+// c_gt <= m) go to slots [0, min(m, c_gt)) in canonical order through
+// emit(slot, position, bits).  cand(j) gives candidate j as (raw bits, position).
+// Buckets are linear in the key over [L, U] (keys below L share bucket 0, keys above U
+// the top bucket), counted with 16-bit LDS counters, two per word.  The bucket holding
+// the m-th largest is the threshold; kept candidates (buckets at or above it) go to S
+// grouped by bucket as composites (key << 32 | ~position), which are unique and whose
+// descending order is the canonical order; a kept candidate's slot is its bucket's start
+// plus the number of larger composites in its bucket.
+// LIMITED: returns false, having emitted nothing, when more than SCAP candidates are kept
+// or a kept bucket holds more than kBucketLimit; otherwise c_gt <= SCAP is the caller's.
+// On entry the bucket array and ctl[kCtlBt..kCtlMaxBucket] are zero, a barrier behind.
+template <int NT, int SCAP, bool LIMITED, class Cand, class Emit>
+__device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Cand&& cand,
+                                            uint32_t c_gt, uint32_t m, bool ties, uint32_t L, uint32_t U, Emit&& emit) {
+    constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
+    static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int sh = max(0, (32 - __clz(U - L)) - kBucketBits);
+    auto bucket_of = [&](uint32_t kx) -> uint32_t { return min((max(kx, L) - L) >> sh, (uint32_t)(kBuckets - 1)); };
+    // bucket b lives in word b / 2, bits 16 * (b % 2) and up
+    auto half_of = [](uint32_t word, uint32_t b) -> uint32_t { return (word >> ((b & 1u) << 4)) & 0xFFFFu; };
+    const uint32_t mlim = min(m, c_gt);  // slots the candidates fill
+
+    // ---- counts
+    for (uint32_t j = tid; j < c_gt; j += NT) {
+        const uint32_t bk = bucket_of(key_of(cand(j).x));
+        lds_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4));
+    }
+    __syncthreads();
+
+    // ---- suffix scan: bucket starts.  Thread t owns buckets [kBuckets - (t + 1) * BPT,
+    // kBuckets - t * BPT), scanned from the top, so slot offsets grow with t.
+    uint32_t cnts[BPT];
+    uint32_t tsum = 0;
+    const int btop = kBuckets - tid * BPT - 1;  // odd: the high half of word btop / 2
+#pragma unroll
+    for (int i = 0; i < BPT; i += 2) {
+        const uint32_t w = bucket[(btop - i) >> 1];
+        cnts[i] = w >> 16;          // bucket btop - i
+        cnts[i + 1] = w & 0xFFFFu;  // bucket btop - i - 1
+        tsum += cnts[i] + cnts[i + 1];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan<NT>(tsum, wsum + 16, &total);
+    uint32_t mx = 0;
+    uint32_t hi_start = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const uint32_t st = run;
+        if ((i & 1) == 0) {
+            hi_start = st;
+        } else {
+            bucket[(btop - i) >> 1] = (hi_start << 16) | st;  // cursors start at first slots
+        }
+        if (ties || st < m) mx = max(mx, cnts[i]);
+        if (!ties && st < m && st + cnts[i] >= m) {
+            ctl[kCtlBt] = (uint32_t)(btop - i);  // threshold bucket
+            ctl[kCtlKept] = st + cnts[i];        // kept candidates (slots of buckets >= b_t)
+        }
+        run += cnts[i];
+    }
+    if (LIMITED) {
+        mx = wave_max(mx);
+        if (lane == 0) __hip_atomic_fetch_max(&ctl[kCtlMaxBucket], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    const uint32_t bt = ties ? 0u : ctl[kCtlBt];
+    const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
+    if (LIMITED && (kept > (uint32_t)SCAP || ctl[kCtlMaxBucket] > (uint32_t)kBucketLimit)) return false;  // uniform
+
+    // ---- scatter kept candidates by bucket
+    constexpr int SUNR = 2;
+    for (uint32_t j0 = 0; j0 < c_gt; j0 += SUNR * NT) {
+        uint2 cv[SUNR];
+#pragma unroll
+        for (int i = 0; i < SUNR; ++i) {
+            const uint32_t j = j0 + i * NT + tid;
+            cv[i] = j < c_gt ? cand(j) : make_uint2(0u, 0u);
+        }
+        uint32_t pos[SUNR], kk[SUNR];
+#pragma unroll
+        for (int i = 0; i < SUNR; ++i) {
+            kk[i] = key_of(cv[i].x);
+            const uint32_t bk = bucket_of(kk[i]);
+            pos[i] = 0xFFFFFFFFu;
+            if (j0 + i * NT + tid < c_gt && bk >= bt)
+                pos[i] = half_of(__hip_atomic_fetch_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_WORKGROUP),
+                                 bk);
+        }
+#pragma unroll
+        for (int i = 0; i < SUNR; ++i)
+            if (pos[i] < (uint32_t)SCAP) S[pos[i]] = ((uint64_t)kk[i] << 32) | (uint32_t)~cv[i].y;
+    }
+    __syncthreads();
+
+    // ---- rank inside buckets -> final slot.  Bucket b's counter now holds its end; its
+    // start is the end of bucket b + 1.  Each lane ranks RUNR elements at once; the
+    // comparison loop runs the wave's longest bucket, uniformly.
+    constexpr int RUNR = 2;
+    for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
+        uint64_t cc[RUNR];
+        uint32_t st[RUNR], len[RUNR], rank[RUNR];
+        uint32_t lmax = 0;
+#pragma unroll
+        for (int i = 0; i < RUNR; ++i) {
+            const uint32_t q = q0 + i * NT + tid;
+            const bool in = q < kept;
+            cc[i] = in ? S[q] : 0ull;
+            const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
+            const uint32_t en = in ? min(half_of(bucket[bk >> 1], bk), kept) : 0u;
+            st[i] = bk == (uint32_t)(kBuckets - 1) ? 0u : half_of(bucket[(bk + 1) >> 1], bk + 1);
+            len[i] = en > st[i] ? en - st[i] : 0u;
+            lmax = max(lmax, len[i]);
+            rank[i] = 0;
+        }
+        lmax = wave_max(lmax);
+        for (uint32_t f = 0; f < lmax; ++f) {
+#pragma unroll
+            for (int i = 0; i < RUNR; ++i) {
+                const uint64_t other = S[f < len[i] ? st[i] + f : 0u];
+                rank[i] += (f < len[i] && other > cc[i]) ? 1u : 0u;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RUNR; ++i) {
+            const uint32_t slot = st[i] + rank[i];
+            if (q0 + i * NT + tid < kept && slot < mlim) emit(slot, ~(uint32_t)cc[i], bits_of((uint32_t)(cc[i] >> 32)));
+        }
+    }
+    return true;
+}
+
+// Bucket range [L, U]: L is the least sample above P, U the largest sample below
+// key(+inf) (the largest sample when P itself is +inf or +NaN), so neither a pivot on a
+// plateau of equal scores far below the kept keys nor a few +inf / NaN scores stretch
+// the range away from where the kept keys are.
+__device__ __forceinline__ void bucket_range(uint32_t P, uint32_t lo, uint32_t smax_all, uint32_t smax_fin, uint32_t* L,
+                                             uint32_t* U) {
+    *U = max(P, P >= kKeyPosInf ? smax_all : smax_fin);
+    *L = min(lo, *U);
+}
+
+// Pivot path of a row that fits one workgroup (raw bits in u[]).  Returns false, with LDS
+// left dirty but registers untouched, when the row needs the exact path.
 template <int NT, int EPT, int KMAX>
 __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMAX>& s, const uint32_t (&u)[EPT],
                                           int fast_mode) {
     using FS = FastSmem<NT, EPT, KMAX>;
-    constexpr int G4 = EPT / 4;
     constexpr int BW = FS::BWORDS;
-    constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     const int tid = opaque_tid();
     const int lane = tid & 63;
     const int32_t nt = r.nt;
     const int32_t m = r.m;
 
     // ------------------------------------------------ clear LDS state
-    if (tid < kRadix) s.bucket[tid] = 0;
     for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
-    if (tid < 16) s.ctl[tid] = tid == 2 ? 0xFFFFFFFFu : 0u;
+    if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot
-    // Samples: slots i * EPT / kSamplesPerLane of every lane, spread over the tile.
     uint32_t sk[kSamplesPerLane];
-    int nsamp = 0;  // valid samples in the whole workgroup (uniform)
-    uint32_t smax = 0;
+    take_samples<NT, EPT>(u, nt, sk);
+    const int nsamp = tile_samples<NT, EPT>(nt);
     {
-        const int t4 = tid * 4;
+        uint32_t sa = 0, sf = 0;
 #pragma unroll
         for (int i = 0; i < kSamplesPerLane; ++i) {
-            constexpr int step = EPT / kSamplesPerLane;
-            const int slot = i * step;
-            const int v = slot / 4, c = slot % 4;
-            const bool ok = t4 + (v * NT * 4 + c) < nt;
-            sk[i] = ok ? key_of(u[slot]) : 0u;
-            smax = max(smax, sk[i]);
-            const int lim = nt - v * NT * 4 - c;  // lanes of this sample row that are valid
-            nsamp += min(max((lim + 3) / 4, 0), NT);
+            sa = max(sa, sk[i]);
+            sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
+        }
+        sa = wave_max(sa);
+        sf = wave_max(sf);
+        __syncthreads();
+        if (lane == 0) {
+            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxAll], sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     }
-    smax = wave_max(smax);
-    __syncthreads();
-    if (lane == 0) __hip_atomic_fetch_max(&s.ctl[1], smax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-
-    // P: the low end of the 16-bit (or, for a crowded bin, 24-bit) key prefix holding the
-    // rr-th largest sample, rr = the expected share of the top m plus ~3.5 standard
-    // deviations, found with MSB-first 8-bit digit passes over the samples.
     uint32_t P = 0;
     {
-        const float expct = (float)nsamp * (float)m / (float)nt;
         // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
-        const int rr = fast_mode == 2 ? 1 : (int)ceilf(expct + 3.5f * sqrtf(expct) + 4.0f);
-        if (m < nt && rr < nsamp) {
-            uint32_t prefix = 0, r_rem = (uint32_t)rr;
-#pragma unroll 1
-            for (int pass = 0; pass < 3; ++pass) {
-                const int shift = 24 - 8 * pass;
-                if (pass == 2 && s.ctl[8] <= kRefineAbove) break;  // uniform: bin resolved
-                if (pass > 0 && tid < kRadix) s.bucket[tid] = 0;
-                __syncthreads();
-#pragma unroll
-                for (int i = 0; i < kSamplesPerLane; ++i)
-                    if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(s.bucket, (sk[i] >> shift) & 0xFFu);
-                __syncthreads();
-                select_digit<NT>(s.bucket, r_rem, s.wsum, s.ctl + 6);
-                prefix = (prefix << 8) | s.ctl[6];
-                r_rem -= s.ctl[7];
-                P = prefix << shift;
-            }
-        }
+        const uint32_t rr = fast_mode == 2 ? 1u : pivot_rank(nsamp, m, nt);
+        if (m < nt && rr < (uint32_t)nsamp)
+            P = pivot_passes<NT>(sk, rr, s.bucket, s.wsum, s.ctl + kCtlSel, [](int, uint32_t*) {});
     }
-    const int32_t pr = (int32_t)(P & 0x7FFFFFFFu);  // P's float bits when P >= key(+0.0)
-    {  // smallest sample above P: the low end of the bucket range
+    {
         uint32_t lo = 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < kSamplesPerLane; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
         lo = wave_min(lo);
-        if (lane == 0) __hip_atomic_fetch_min(&s.ctl[2], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (lane == 0) __hip_atomic_fetch_min(&s.ctl[kCtlLo], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();  // sample extremes published; sample histogram no longer read
-    // Buckets: linear in the key over [L, U], L the smallest sample above P and U the
-    // largest sample; keys in (P, L) share bucket 0 and keys above U the top bucket.
-    // Starting at L rather than P keeps the resolution where the kept keys are when P
-    // sits on a plateau of equal scores far below them.
-    const uint32_t U = max(s.ctl[1], P);
-    const uint32_t L = min(s.ctl[2], U);
-    const int sh = max(0, (32 - __clz(U - L)) - kBucketBits);
-    auto bucket_of = [&](uint32_t kx) -> uint32_t {
-        return min((max(kx, L) - L) >> sh, (uint32_t)(kBuckets - 1));
-    };
+    uint32_t L, U;
+    bucket_range(P, s.ctl[kCtlLo], s.ctl[kCtlSmaxAll], s.ctl[kCtlSmaxFin], &L, &U);
     for (int i = tid; i < kBuckets / 2; i += NT) s.bucket[i] = 0;
-    // 16-bit halves: bucket b lives in word b / 2, bits 16 * (b % 2) and up.
-    auto half_of = [](uint32_t word, uint32_t b) -> uint32_t { return (word >> ((b & 1u) << 4)) & 0xFFFFu; };
-
-    // Visit register slots: f(x, slot constant c, group v, valid, 4 * thread).  Full groups
-    // skip the per-lane bound check.
-    auto slots = [&](auto&& f) {
-        const int t4 = opaque_tid() * 4;
-#pragma unroll
-        for (int v = 0; v < G4; ++v) {
-            const int lim = nt - v * NT * 4;
-            if (lim <= 0) break;
-            if (lim >= NT * 4) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) f(u[4 * v + c], c, v, true, t4);
-            } else {
-                const int llim = lim - t4;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) f(u[4 * v + c], c, v, c < llim, t4);
-            }
-        }
-    };
+    const AboveP ap(P);
 
     // ------------------------------------------------ count pass: keys > P per lane
     uint32_t cnt = 0;
     if (P >= 0x80000000u)
-        slots([&](uint32_t x, int, int, bool ok, int) { cnt += ((int32_t)x > pr && ok) ? 1u : 0u; });
+        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) { cnt += (ap.gt<true>(x) && ok) ? 1u : 0u; });
     else
-        slots([&](uint32_t x, int, int, bool ok, int) { cnt += (key_of(x) > P && ok) ? 1u : 0u; });
+        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) { cnt += (ap.gt<false>(x) && ok) ? 1u : 0u; });
     uint32_t c_gt;
     uint32_t o = block_excl_scan<NT>(cnt, s.wsum, &c_gt);
-    if (c_gt > (uint32_t)kCandCap) return false;  // uniform
-    const bool ties = c_gt < (uint32_t)m;           // uniform: keys == P fill the tail
+    if (c_gt > (uint32_t)FS::CCAP) return false;  // uniform
+    const bool ties = c_gt < (uint32_t)m;          // uniform: keys == P fill the tail
 
     // ------------------------------------------------ write pass: (bits, position) of the
     // candidates to LDS; keys == P into the position bitmap when the tail needs them.
@@ -539,15 +776,13 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         constexpr bool POS = decltype(pos_tag)::value;
         constexpr bool EQ = decltype(eq_tag)::value;
         uint32_t nib = 0;
-        slots([&](uint32_t x, int c, int v, bool ok, int t4) {
-            const bool gt = POS ? (int32_t)x > pr : key_of(x) > P;
-            if (gt && ok) {
+        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int c, int v, bool ok, int t4) {
+            if (ap.gt<POS>(x) && ok) {
                 s.u.cand[o] = make_uint2(x, (uint32_t)(t4 + (v * NT * 4 + c)));
                 ++o;
             }
             if (EQ) {
-                const bool eq = POS ? x == (uint32_t)pr : key_of(x) == P;
-                nib |= (eq && ok ? 1u : 0u) << c;
+                nib |= (ap.eq<POS>(x) && ok ? 1u : 0u) << c;
                 if (c == 3) {
                     if (nib) {
                         const int p0 = t4 + v * NT * 4;
@@ -569,123 +804,19 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     }
     if (ties) {
         neq = wave_incl_scan(neq);
-        if (lane == 63) lds_add(&s.ctl[9], neq);
+        if (lane == 63) lds_add(&s.ctl[kCtlEq], neq);
     }
     __syncthreads();
-    if (ties && c_gt + s.ctl[9] < (uint32_t)m) return false;  // uniform: pivot missed
-    const uint32_t mlim = min((uint32_t)m, c_gt);             // slots filled by candidates
+    if (ties && c_gt + s.ctl[kCtlEq] < (uint32_t)m) return false;  // uniform: pivot missed
 
-    // ------------------------------------------------ bucket counts (dense over candidates)
-    for (uint32_t j = tid; j < c_gt; j += NT) {
-        const uint32_t bk = bucket_of(key_of(s.u.cand[j].x));
-        lds_add(&s.bucket[bk >> 1], 1u << ((bk & 1u) << 4));
-    }
-    __syncthreads();
-
-    // ------------------------------------------------ suffix scan: bucket starts
-    // Thread t owns buckets [kBuckets - (t + 1) * BPT, kBuckets - t * BPT), scanned from
-    // the top, so rank offsets grow with t.  Kept buckets are those starting below m.
-    static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
-    uint32_t cnts[BPT];
-    uint32_t tsum = 0;
-    const int btop = kBuckets - tid * BPT - 1;  // odd: the high half of word btop / 2
-#pragma unroll
-    for (int i = 0; i < BPT; i += 2) {
-        const uint32_t w = s.bucket[(btop - i) >> 1];
-        cnts[i] = w >> 16;           // bucket btop - i
-        cnts[i + 1] = w & 0xFFFFu;   // bucket btop - i - 1
-        tsum += cnts[i] + cnts[i + 1];
-    }
-    uint32_t total;
-    uint32_t run = block_excl_scan<NT>(tsum, s.wsum + 16, &total);
-    uint32_t mx = 0;
-    uint32_t hi_start = 0;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-        const uint32_t st = run;
-        if ((i & 1) == 0) {
-            hi_start = st;
-        } else {
-            s.bucket[(btop - i) >> 1] = (hi_start << 16) | st;  // cursors start at first slots
-        }
-        if (ties || st < (uint32_t)m) mx = max(mx, cnts[i]);
-        if (!ties && st < (uint32_t)m && st + cnts[i] >= (uint32_t)m) {
-            s.ctl[3] = (uint32_t)(btop - i);  // threshold bucket
-            s.ctl[4] = st + cnts[i];          // kept candidates (slots of buckets >= b_t)
-        }
-        run += cnts[i];
-    }
-    mx = wave_max(mx);
-    if (lane == 0) __hip_atomic_fetch_max(&s.ctl[5], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __syncthreads();
-    const uint32_t bt = ties ? 0u : s.ctl[3];
-    const uint32_t kept = ties ? c_gt : s.ctl[4];
-    if (kept > (uint32_t)FS::SCAP || s.ctl[5] > (uint32_t)kBucketLimit) return false;  // uniform
-
-    // ------------------------------------------------ scatter kept candidates by bucket
-    constexpr int SUNR = 2;
-    for (uint32_t j0 = 0; j0 < c_gt; j0 += SUNR * NT) {
-        uint2 cv[SUNR];
-#pragma unroll
-        for (int i = 0; i < SUNR; ++i) {
-            const uint32_t j = j0 + i * NT + tid;
-            cv[i] = j < c_gt ? s.u.cand[j] : make_uint2(0u, 0u);
-        }
-        uint32_t pos[SUNR], kk[SUNR];
-#pragma unroll
-        for (int i = 0; i < SUNR; ++i) {
-            kk[i] = key_of(cv[i].x);
-            const uint32_t bk = bucket_of(kk[i]);
-            pos[i] = 0xFFFFFFFFu;
-            if (j0 + i * NT + tid < c_gt && bk >= bt)
-                pos[i] = half_of(__hip_atomic_fetch_add(&s.bucket[bk >> 1], 1u << ((bk & 1u) << 4), __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_WORKGROUP),
-                                 bk);
-        }
-#pragma unroll
-        for (int i = 0; i < SUNR; ++i)
-            if (pos[i] < (uint32_t)FS::SCAP) s.S[pos[i]] = ((uint64_t)kk[i] << 32) | (uint32_t)~cv[i].y;
-    }
-    __syncthreads();
-
-    // ------------------------------------------------ rank inside buckets -> final slot
-    // Bucket b's counter now holds its end; its start is the end of bucket b + 1.  Each
-    // lane ranks RUNR elements at once; the comparison loop runs the wave's largest
-    // bucket length, uniformly.
-    constexpr int RUNR = 2;
-    for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
-        uint64_t cc[RUNR];
-        uint32_t st[RUNR], len[RUNR], rank[RUNR];
-        uint32_t lmax = 0;
-#pragma unroll
-        for (int i = 0; i < RUNR; ++i) {
-            const uint32_t q = q0 + i * NT + tid;
-            const bool in = q < kept;
-            cc[i] = in ? s.S[q] : 0ull;
-            const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
-            const uint32_t en = in ? min(half_of(s.bucket[bk >> 1], bk), kept) : 0u;
-            st[i] = bk == (uint32_t)(kBuckets - 1) ? 0u : half_of(s.bucket[(bk + 1) >> 1], bk + 1);
-            len[i] = en > st[i] ? en - st[i] : 0u;
-            lmax = max(lmax, len[i]);
-            rank[i] = 0;
-        }
-        lmax = wave_max(lmax);
-        for (uint32_t f = 0; f < lmax; ++f) {
-#pragma unroll
-            for (int i = 0; i < RUNR; ++i) {
-                const uint64_t other = s.S[f < len[i] ? st[i] + f : 0u];
-                rank[i] += (f < len[i] && other > cc[i]) ? 1u : 0u;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < RUNR; ++i) {
-            const uint32_t slot = st[i] + rank[i];
-            if (q0 + i * NT + tid < kept && slot < mlim) {
-                s.u.out.idx[slot] = ~(uint32_t)cc[i];
-                s.u.out.val[slot] = bits_of((uint32_t)(cc[i] >> 32));
-            }
-        }
-    }
+    // ------------------------------------------------ order the candidates
+    if (!bucket_rank<NT, FS::SCAP, true>(
+            s.bucket, s.S, s.wsum, s.ctl, [&](uint32_t j) { return s.u.cand[j]; }, c_gt, (uint32_t)m, ties, L, U,
+            [&](uint32_t slot, uint32_t pos, uint32_t bits) {
+                s.u.out.idx[slot] = pos;
+                s.u.out.val[slot] = bits;
+            }))
+        return false;
 
     // ------------------------------------------------ ties at P: smallest positions
     if (ties) {
@@ -727,10 +858,221 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     return true;
 }
 
+// Pivot path of a row split over several workgroups, one tile each (raw bits in u[]).
+// The tiles of a row meet at row barriers (bar_target counts them):
+//   - per sample digit, each tile adds its sample histogram into the row's and all tiles
+//     select the same digit, so every tile derives the same pivot P;
+//   - each tile counts its keys above and equal to P, claims space for its candidates in
+//     the row's workspace list and publishes its counts and sample extremes; after the
+//     barrier all tiles see the row's totals and take the same decision: fall back
+//     (returns false, registers untouched) when the list would overflow or fewer than m
+//     keys are >= P;
+//   - each tile writes its candidates (bits, row position) and, when keys equal to P
+//     fill the tail, the smallest-position ones straight to their output slots (its rank
+//     among them offset by the earlier tiles' counts);
+//   - the last tile to arrive orders the row's candidates (bucket_rank) into slots
+//     [0, min(m, candidates)).
+template <int NT, int EPT, int KMAX>
+__device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r, MultiFastSmem<NT, EPT, KMAX>& s,
+                                                const uint32_t (&u)[EPT], uint32_t& bar_target) {
+    using MS = MultiFastSmem<NT, EPT, KMAX>;
+    constexpr int BW = MS::BWORDS;
+    constexpr int TILE = MS::TILE;
+    constexpr uint32_t CAP = (uint32_t)MS::SCAP;
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int b = r.b, tile = r.tile, ntiles = r.ntiles;
+    const int32_t nt = r.nt, m = r.m, n = r.n, j0 = r.j0;
+    uint32_t* rw = p.ws_zero + 1 + (int64_t)b * kRowZeroWords;
+    uint32_t* err = p.ws_zero;
+
+    // ------------------------------------------------ clear LDS state
+    for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
+    if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
+
+    // ------------------------------------------------ sample -> pivot (row-wide)
+    uint32_t sk[kSamplesPerLane];
+    take_samples<NT, EPT>(u, nt, sk);
+    const int nsamp = (ntiles - 1) * tile_samples<NT, EPT>(TILE) + tile_samples<NT, EPT>(n - (ntiles - 1) * TILE);
+    {
+        uint32_t sa = 0, sf = 0;
+#pragma unroll
+        for (int i = 0; i < kSamplesPerLane; ++i) {
+            sa = max(sa, sk[i]);
+            sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
+        }
+        sa = wave_max(sa);
+        sf = wave_max(sf);
+        __syncthreads();
+        if (lane == 0) {
+            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxAll], sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    uint32_t P = 0;
+    {
+        const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
+        if (rr < (uint32_t)nsamp) {
+            uint32_t* gsamp = rw + kRowSampHist;
+            P = pivot_passes<NT>(sk, rr, s.bucket, s.wsum, s.ctl + kCtlSel, [&](int pass, uint32_t* h) {
+                if (tid < kRadix) {
+                    const uint32_t c = h[tid];
+                    if (c) atomicAdd(&gsamp[pass * kRadix + tid], c);
+                }
+                bar_target += (uint32_t)ntiles;
+                row_barrier(&rw[kRowBar], bar_target, err);
+                if (tid < kRadix)
+                    h[tid] = __hip_atomic_load(&gsamp[pass * kRadix + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+            });
+        }
+    }
+    {
+        uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < kSamplesPerLane; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
+        lo = wave_min(lo);
+        if (lane == 0) __hip_atomic_fetch_min(&s.ctl[kCtlLo], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    const AboveP ap(P);
+
+    // ------------------------------------------------ count, claim, publish
+    uint32_t cgt = 0, ceq = 0;
+    if (P >= 0x80000000u)
+        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
+            cgt += (ap.gt<true>(x) && ok) ? 1u : 0u;
+            ceq += (ap.eq<true>(x) && ok) ? 1u : 0u;
+        });
+    else
+        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
+            cgt += (ap.gt<false>(x) && ok) ? 1u : 0u;
+            ceq += (ap.eq<false>(x) && ok) ? 1u : 0u;
+        });
+    uint32_t c_tile, e_tile;
+    uint32_t o = block_excl_scan<NT>(cgt, s.wsum, &c_tile);
+    (void)block_excl_scan<NT>(ceq, s.wsum + 16, &e_tile);
+    if (tid == 0) {
+        s.ctl[kCtlBase] = c_tile ? atomicAdd(&rw[kRowCgt], c_tile) : 0u;
+        if (e_tile) atomicAdd(&rw[kRowEq], e_tile);
+        __hip_atomic_store(&p.ws_ecnt[(int64_t)b * p.tiles_per_row + tile], e_tile, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        atomicMax(&rw[kRowNotLo], ~s.ctl[kCtlLo]);
+        atomicMax(&rw[kRowUAll], s.ctl[kCtlSmaxAll]);
+        atomicMax(&rw[kRowUFin], s.ctl[kCtlSmaxFin]);
+    }
+    bar_target += (uint32_t)ntiles;
+    row_barrier(&rw[kRowBar], bar_target, err);
+    const uint32_t c_gt = __hip_atomic_load(&rw[kRowCgt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t n_eq = __hip_atomic_load(&rw[kRowEq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c_gt > CAP || c_gt + n_eq < (uint32_t)m) return false;  // uniform across the row
+    const bool ties = c_gt < (uint32_t)m;
+
+    // ------------------------------------------------ write candidates (+ tie bitmap)
+    {
+        uint2* gc = p.ws_cand + (int64_t)b * CAP + s.ctl[kCtlBase];
+        auto write_pass = [&](auto pos_tag, auto eq_tag) {
+            constexpr bool POS = decltype(pos_tag)::value;
+            constexpr bool EQ = decltype(eq_tag)::value;
+            uint32_t nib = 0;
+            visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int c, int v, bool ok, int t4) {
+                if (ap.gt<POS>(x) && ok) {
+                    gc[o] = make_uint2(x, (uint32_t)(j0 + t4 + (v * NT * 4 + c)));
+                    ++o;
+                }
+                if (EQ) {
+                    nib |= (ap.eq<POS>(x) && ok ? 1u : 0u) << c;
+                    if (c == 3) {
+                        if (nib) {
+                            const int p0 = t4 + v * NT * 4;
+                            __hip_atomic_fetch_or(&s.bitmap[p0 >> 5], nib << (p0 & 31), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+                        }
+                        nib = 0;
+                    }
+                }
+            });
+        };
+        if (P >= 0x80000000u) {
+            if (ties) write_pass(std::true_type{}, std::true_type{});
+            else write_pass(std::true_type{}, std::false_type{});
+        } else {
+            if (ties) write_pass(std::false_type{}, std::true_type{});
+            else write_pass(std::false_type{}, std::false_type{});
+        }
+    }
+
+    // ------------------------------------------------ ties at P: this tile's share
+    if (ties) {
+        if (tid == 0) {
+            uint32_t off = 0;
+            for (int t = 0; t < tile; ++t)
+                off += __hip_atomic_load(&p.ws_ecnt[(int64_t)b * p.tiles_per_row + t], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            s.ctl[kCtlTieOff] = off;
+        }
+        __syncthreads();
+        const uint32_t need = (uint32_t)m - c_gt;
+        const uint32_t tie_off = s.ctl[kCtlTieOff];
+        if (tie_off < need) {
+            constexpr int WPT = (BW + NT - 1) / NT;
+            uint32_t tc = 0;
+#pragma unroll
+            for (int q = 0; q < WPT; ++q) {
+                const int w = tid * WPT + q;
+                if (w < BW) tc += (uint32_t)__popc(s.bitmap[w]);
+            }
+            uint32_t tot;
+            uint32_t rr = tie_off + block_excl_scan<NT>(tc, s.wsum, &tot);
+            const uint32_t vP = bits_of(P);
+#pragma unroll
+            for (int q = 0; q < WPT; ++q) {
+                const int w = tid * WPT + q;
+                if (w < BW) {
+                    uint32_t word = s.bitmap[w];
+                    while (word && rr < need) {
+                        const int bit = __ffs(word) - 1;
+                        word &= word - 1;
+                        r.oidx[c_gt + rr] = j0 + w * 32 + bit;
+                        if (r.oval) r.oval[c_gt + rr] = vP;
+                        ++rr;
+                    }
+                    rr += (uint32_t)__popc(word);
+                }
+            }
+        }
+    }
+
+    // ------------------------------------------------ arrive; the last tile orders the row
+    wait_global_writes();
+    __syncthreads();
+    if (tid == 0) {  // release this tile's candidates; the last arriver acquires all of them
+        const uint32_t old = __hip_atomic_fetch_add(&rw[kRowFastArrive], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s.ctl[kCtlLast] = old == (uint32_t)ntiles - 1u ? 1u : 0u;
+    }
+    for (int i = tid; i < kBuckets / 2; i += NT) s.bucket[i] = 0;
+    if (tid >= kCtlBt && tid <= kCtlMaxBucket) s.ctl[tid] = 0;
+    __syncthreads();
+    if (s.ctl[kCtlLast] == 0) return true;
+    uint32_t L, U;
+    bucket_range(P, ~__hip_atomic_load(&rw[kRowNotLo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                 __hip_atomic_load(&rw[kRowUAll], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                 __hip_atomic_load(&rw[kRowUFin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), &L, &U);
+    const uint2* gc = p.ws_cand + (int64_t)b * CAP;
+    bucket_rank<NT, MS::SCAP, false>(
+        s.bucket, s.S, s.wsum, s.ctl, [&](uint32_t j) { return gc[j]; }, c_gt, (uint32_t)m, ties, L, U,
+        [&](uint32_t slot, uint32_t pos, uint32_t bits) {
+            r.oidx[slot] = (int32_t)pos;
+            if (r.oval) r.oval[slot] = bits;
+        });
+    write_padding<NT>(r.oidx, r.oval, m, r.k);
+    return true;
+}
+
 // ----------------------------------------------------------------------------- exact path
 
 template <int NT, int EPT, int KMAX, bool MULTI, typename ES>
-__device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES& s, const uint32_t (&key)[EPT]) {
+__device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES& s, const uint32_t (&key)[EPT],
+                                           uint32_t bar_target) {
     constexpr int G4 = EPT / 4;
     constexpr int BW = ES::BWORDS;
     constexpr int NW = ES::NW;
@@ -745,7 +1087,6 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
 
     uint32_t* rw = multi ? p.ws_zero + 1 + (int64_t)b * kRowZeroWords : nullptr;  // row words
     uint32_t* err = p.ws_zero;
-    uint32_t bar_target = 0;
     const PairList A{s.akey, s.apos};
 
     // Visit every valid register element: f(key, local index).
@@ -791,13 +1132,13 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
             for (int w = 0; w < NW; ++w) h += s.whist[w][tid];
             s.lhist[tid] = h;
             s.hist[tid] = h;
-            if (multi && h) atomicAdd(&rw[pass * kRadix + tid], h);
+            if (multi && h) atomicAdd(&rw[kRowHist + pass * kRadix + tid], h);
         }
         if (multi) {
             bar_target += (uint32_t)ntiles;
-            row_barrier(&rw[4 * kRadix], bar_target, err);
+            row_barrier(&rw[kRowBar], bar_target, err);
             if (tid < kRadix)
-                s.hist[tid] = __hip_atomic_load(&rw[pass * kRadix + tid], __ATOMIC_RELAXED,
+                s.hist[tid] = __hip_atomic_load(&rw[kRowHist + pass * kRadix + tid], __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
@@ -924,7 +1265,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     if (multi) {
         if (tid == 0) p.ws_ecnt[(int64_t)b * p.tiles_per_row + tile] = s.ctr[2];
         bar_target += (uint32_t)ntiles;
-        row_barrier(&rw[4 * kRadix], bar_target, err);
+        row_barrier(&rw[kRowBar], bar_target, err);
         if (tid == 0) {
             uint32_t o = 0;
             for (int t = 0; t < tile; ++t)
@@ -964,7 +1305,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     }
 
     // multi: publish this tile's G composites, last tile to arrive sorts the row.
-    if (tid == 0) s.ctr[2] = nA ? atomicAdd(&rw[4 * kRadix + 2], nA) : 0u;
+    if (tid == 0) s.ctr[2] = nA ? atomicAdd(&rw[kRowStage], nA) : 0u;
     __syncthreads();
     {
         uint64_t* st = p.ws_stage + (int64_t)b * k;
@@ -975,7 +1316,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     wait_global_writes();
     __syncthreads();
     if (tid == 0) {  // release this tile's stage writes; the last arriver acquires all of them
-        const uint32_t old = __hip_atomic_fetch_add(&rw[4 * kRadix + 1], 1u, __ATOMIC_ACQ_REL,
+        const uint32_t old = __hip_atomic_fetch_add(&rw[kRowArrive], 1u, __ATOMIC_ACQ_REL,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         s.ctr[3] = (old == (uint32_t)ntiles - 1u) ? 1u : 0u;
     }
@@ -1026,13 +1367,21 @@ __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, K
     uint32_t u[EPT];
     load_tile<NT, EPT>(u, p.scores + r.base + r.j0, r.nt);
 
-    if (!r.multi && p.fast) {
-        if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
-        __syncthreads();  // fall back to the exact path on the same registers
+    uint32_t bar_target = 0;  // row barriers passed so far x tiles (several workgroups per row)
+    if (p.fast) {
+        if (!r.multi) {
+            if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
+            __syncthreads();  // fall back to the exact path on the same registers
+        } else {
+            if constexpr (MULTI) {
+                if (multi_fast_tile<NT, EPT, KMAX>(p, r, s.mfast, u, bar_target)) return;
+                __syncthreads();
+            }
+        }
     }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
-    exact_tile<NT, EPT, KMAX, MULTI>(p, r, s.exact, u);
+    exact_tile<NT, EPT, KMAX, MULTI>(p, r, s.exact, u, bar_target);
 }
 
 // MINW: waves per SIMD the register allocation must allow (the LDS footprint fixes

@@ -104,7 +104,8 @@ def _small(name):
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 @pytest.mark.parametrize("shape", ["auto", "single", "single_exact", "single_pivot_miss", "multi4096", "multi8192",
-                                   "single_rescan", "multi_rescan", "multi_tinystage"])
+                                   "multi_exact", "multi_pivot_miss", "single_rescan", "multi_rescan",
+                                   "multi_tinystage"])
 def test_small_workloads(dev, name, shape):
     wl = _small(name)
     if shape.startswith("single") and wl.max_len > 32768:
@@ -116,9 +117,11 @@ def test_small_workloads(dev, name, shape):
         "single_pivot_miss": {"path": 1, "fast": 2},
         "multi4096": {"path": 2, "multi_tile": 4096},
         "multi8192": {"path": 2, "multi_tile": 8192},
+        "multi_exact": {"path": 2, "multi_tile": 4096, "fast": 0},
+        "multi_pivot_miss": {"path": 2, "multi_tile": 4096, "fast": 2},
         "single_rescan": {"path": 1, "stage_cap": 0, "fast": 0},
-        "multi_rescan": {"path": 2, "multi_tile": 4096, "stage_cap": 0},
-        "multi_tinystage": {"path": 2, "multi_tile": 4096, "stage_cap": 3},
+        "multi_rescan": {"path": 2, "multi_tile": 4096, "stage_cap": 0, "fast": 0},
+        "multi_tinystage": {"path": 2, "multi_tile": 4096, "stage_cap": 3, "fast": 0},
     }[shape]
     log("small workload %s shape %s B=%d max_len=%d k=%d" % (name, shape, wl.B, wl.max_len, wl.k))
     with debug_overrides(**cfg):
@@ -139,8 +142,8 @@ def test_full_workload_exact(dev, name):
 @pytest.mark.parametrize("name", ["decode_ragged_64", "long_context_8x262144"])
 def test_full_workload_forced_rescan(dev, name):
     wl = W.full(name)
-    log("full workload %s, staging disabled (every refinement pass rescans)" % name)
-    with debug_overrides(stage_cap=0):
+    log("full workload %s, exact path with staging disabled (every refinement pass rescans)" % name)
+    with debug_overrides(stage_cap=0, fast=0):
         gi, gv = run_gpu(wl, dev)
     oi, ov = run_oracle(wl)
     assert_same(gi, gv, oi, ov, name + "/rescan")
