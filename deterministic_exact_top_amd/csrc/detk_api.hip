@@ -25,15 +25,18 @@ using detk::SmemAll;
 constexpr int kSingleMaxLen = 32768;
 
 template <int TILE> struct Shape;
-template <> struct Shape<4096> { static constexpr int NT = 256, EPT = 16, MINW = 2; };
-template <> struct Shape<8192> { static constexpr int NT = 512, EPT = 16, MINW = 4; };
-template <> struct Shape<16384> { static constexpr int NT = 512, EPT = 32, MINW = 4; };
-template <> struct Shape<32768> { static constexpr int NT = 1024, EPT = 32, MINW = 4; };
+template <> struct Shape<4096> { static constexpr int NT = 256, EPT = 16, MINW = 2, MINW_MULTI = 2; };
+template <> struct Shape<8192> { static constexpr int NT = 512, EPT = 16, MINW = 4, MINW_MULTI = 4; };
+template <> struct Shape<16384> { static constexpr int NT = 512, EPT = 32, MINW = 6, MINW_MULTI = 4; };
+template <> struct Shape<32768> { static constexpr int NT = 1024, EPT = 32, MINW = 4, MINW_MULTI = 4; };
+
+template <int TILE, bool MULTI>
+constexpr int min_waves() { return MULTI ? Shape<TILE>::MINW_MULTI : Shape<TILE>::MINW; }
 
 template <int TILE, int KMAX, bool MULTI>
 const void* kernel_ptr() {
     using S = Shape<TILE>;
-    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>);
+    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, MULTI>()>);
 }
 
 template <int TILE, int KMAX, bool MULTI>
@@ -199,7 +202,7 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
 template <int TILE, int KMAX, bool MULTI>
 hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
     using S = Shape<TILE>;
-    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>), dim3(grid), dim3(S::NT), lds,
+    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, MULTI>()>), dim3(grid), dim3(S::NT), lds,
                        stream, p);
     return hipGetLastError();
 }

@@ -45,9 +45,9 @@ constexpr int kRadix = 256;
 constexpr int kStageCap = 4096;                 // exact path: LDS threshold-bin staging (entries)
 constexpr int kBuckets = 4096;                  // fast path: buckets over the candidate key range
 constexpr int kBucketBits = 12;
-constexpr int kBucketLimit = 256;               // fast path: largest bucket ranked by comparisons
+constexpr int kBucketLimit = 128;               // fast path: largest bucket ranked by comparisons
 static_assert(kBuckets / 2 >= 256, "the packed bucket array doubles as the sample histogram");
-constexpr int kSamplesPerLane = 2;           // fast path: pivot samples per lane
+constexpr int kSamplesPerLane = 4;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 // Per-row workspace words of the multi-workgroup path, zeroed before each launch.
 constexpr int kRowHist = 0;                     // exact path: 4 pass histograms
@@ -253,7 +253,11 @@ struct ExactSmem {
     uint32_t apos[KMAX];          //   and positions
 };
 
-// Candidate capacity of the pivot paths: keys above the pivot, at most twice KMAX.
+// Candidate capacity (keys above the pivot) of the pivot path: 1.5 KMAX in LDS when one
+// workgroup holds the row (so three 16K-element rows fit a CU's LDS); 2 KMAX in the
+// workspace when several share it.
+template <int KMAX>
+constexpr int cand_cap_single() { return 3 * KMAX / 2; }
 template <int KMAX>
 constexpr int cand_cap() { return 2 * KMAX; }
 
@@ -262,7 +266,7 @@ struct FastSmem {
     static constexpr int NW = NT / 64;
     static constexpr int TILE = NT * EPT;
     static constexpr int BWORDS = TILE / 32;
-    static constexpr int CCAP = cand_cap<KMAX>();
+    static constexpr int CCAP = cand_cap_single<KMAX>();
     static constexpr int SCAP = KMAX + kBucketLimit;
     uint32_t ctl[16];             // control words, kCtl* below
     uint32_t wsum[32];
@@ -273,7 +277,7 @@ struct FastSmem {
     union {
         uint2 cand[CCAP];         // candidates: (raw bits, position)
         struct {
-            uint32_t idx[KMAX];
+            uint32_t idx[KMAX];   // output staging (after the candidates are scattered)
             uint32_t val[KMAX];
         } out;
     } u;
@@ -560,7 +564,8 @@ struct AboveP {
 
 // Order the candidates: the m largest of the c_gt candidates (all of them when
 // c_gt <= m) go to slots [0, min(m, c_gt)) in canonical order through
-// emit(slot, position, bits).  cand(j) gives candidate j as (raw bits, position).
+// emit(slot, position, bits).  Thread t owns candidates j = t + i * NT, i < CPT;
+// src(i, j) gives candidate j as (raw bits, position) (CPT * NT >= c_gt).
 // Buckets are linear in the key over [L, U] (keys below L share bucket 0, keys above U
 // the top bucket), counted with 16-bit LDS counters, two per word.  The bucket holding
 // the m-th largest is the threshold; kept candidates (buckets at or above it) go to S
@@ -570,8 +575,8 @@ struct AboveP {
 // LIMITED: returns false, having emitted nothing, when more than SCAP candidates are kept
 // or a kept bucket holds more than kBucketLimit; otherwise c_gt <= SCAP is the caller's.
 // On entry the bucket array and ctl[kCtlBt..kCtlMaxBucket] are zero, a barrier behind.
-template <int NT, int SCAP, bool LIMITED, class Cand, class Emit>
-__device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Cand&& cand,
+template <int NT, int SCAP, int CPT, bool LIMITED, class Src, class Emit>
+__device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             uint32_t c_gt, uint32_t m, bool ties, uint32_t L, uint32_t U, Emit&& emit) {
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
@@ -584,9 +589,13 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     const uint32_t mlim = min(m, c_gt);  // slots the candidates fill
 
     // ---- counts
-    for (uint32_t j = tid; j < c_gt; j += NT) {
-        const uint32_t bk = bucket_of(key_of(cand(j).x));
-        lds_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4));
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const uint32_t j = (uint32_t)(tid + i * NT);
+        if (j < c_gt) {
+            const uint32_t bk = bucket_of(key_of(src(i, j).x));
+            lds_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4));
+        }
     }
     __syncthreads();
 
@@ -630,29 +639,33 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
     if (LIMITED && (kept > (uint32_t)SCAP || ctl[kCtlMaxBucket] > (uint32_t)kBucketLimit)) return false;  // uniform
 
-    // ---- scatter kept candidates by bucket
+    // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write)
     constexpr int SUNR = 2;
-    for (uint32_t j0 = 0; j0 < c_gt; j0 += SUNR * NT) {
-        uint2 cv[SUNR];
 #pragma unroll
-        for (int i = 0; i < SUNR; ++i) {
-            const uint32_t j = j0 + i * NT + tid;
-            cv[i] = j < c_gt ? cand(j) : make_uint2(0u, 0u);
+    for (int i0 = 0; i0 < CPT; i0 += SUNR) {
+        if ((uint32_t)(i0 * NT) >= c_gt) continue;  // uniform
+        uint32_t pos[SUNR];
+        uint64_t comp[SUNR];
+#pragma unroll
+        for (int d = 0; d < SUNR; ++d) {
+            const int i = i0 + d;
+            const uint32_t j = (uint32_t)(tid + i * NT);
+            pos[d] = 0xFFFFFFFFu;
+            comp[d] = 0;
+            if (i < CPT && j < c_gt) {
+                const uint2 cv = src(i, j);
+                const uint32_t kk = key_of(cv.x);
+                const uint32_t bk = bucket_of(kk);
+                comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv.y;
+                if (bk >= bt)
+                    pos[d] = half_of(__hip_atomic_fetch_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4), __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_WORKGROUP),
+                                     bk);
+            }
         }
-        uint32_t pos[SUNR], kk[SUNR];
 #pragma unroll
-        for (int i = 0; i < SUNR; ++i) {
-            kk[i] = key_of(cv[i].x);
-            const uint32_t bk = bucket_of(kk[i]);
-            pos[i] = 0xFFFFFFFFu;
-            if (j0 + i * NT + tid < c_gt && bk >= bt)
-                pos[i] = half_of(__hip_atomic_fetch_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4), __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_WORKGROUP),
-                                 bk);
-        }
-#pragma unroll
-        for (int i = 0; i < SUNR; ++i)
-            if (pos[i] < (uint32_t)SCAP) S[pos[i]] = ((uint64_t)kk[i] << 32) | (uint32_t)~cv[i].y;
+        for (int d = 0; d < SUNR; ++d)
+            if (pos[d] < (uint32_t)SCAP) S[pos[d]] = comp[d];
     }
     __syncthreads();
 
@@ -810,8 +823,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     if (ties && c_gt + s.ctl[kCtlEq] < (uint32_t)m) return false;  // uniform: pivot missed
 
     // ------------------------------------------------ order the candidates
-    if (!bucket_rank<NT, FS::SCAP, true>(
-            s.bucket, s.S, s.wsum, s.ctl, [&](uint32_t j) { return s.u.cand[j]; }, c_gt, (uint32_t)m, ties, L, U,
+    if (!bucket_rank<NT, FS::SCAP, (FS::CCAP + NT - 1) / NT, true>(
+            s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return s.u.cand[j]; }, c_gt, (uint32_t)m, ties, L, U,
             [&](uint32_t slot, uint32_t pos, uint32_t bits) {
                 s.u.out.idx[slot] = pos;
                 s.u.out.val[slot] = bits;
@@ -1058,8 +1071,8 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
                  __hip_atomic_load(&rw[kRowUAll], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                  __hip_atomic_load(&rw[kRowUFin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), &L, &U);
     const uint2* gc = p.ws_cand + (int64_t)b * CAP;
-    bucket_rank<NT, MS::SCAP, false>(
-        s.bucket, s.S, s.wsum, s.ctl, [&](uint32_t j) { return gc[j]; }, c_gt, (uint32_t)m, ties, L, U,
+    bucket_rank<NT, MS::SCAP, (MS::SCAP + NT - 1) / NT, false>(
+        s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return gc[j]; }, c_gt, (uint32_t)m, ties, L, U,
         [&](uint32_t slot, uint32_t pos, uint32_t bits) {
             r.oidx[slot] = (int32_t)pos;
             if (r.oval) r.oval[slot] = bits;
