@@ -366,6 +366,35 @@ __device__ __forceinline__ void select_digit(const uint32_t* hist, uint32_t k_re
     __syncthreads();
 }
 
+// The same selection done by one wave alone, with no barrier, on a complete 256-bin
+// histogram (every wave that calls it gets the same, wave-uniform answer).  Lane l owns
+// bins 255 - 4l .. 252 - 4l.  Returns the digit; *above = count in higher bins, *count =
+// the digit's count (all zero should the counts ever be inconsistent).
+__device__ __forceinline__ uint32_t wave_select_digit(const uint32_t* hist, uint32_t r, uint32_t* above,
+                                                      uint32_t* count) {
+    const int lane = (int)(threadIdx.x & 63);
+    const uint4 q = *reinterpret_cast<const uint4*>(hist + 252 - 4 * lane);
+    const uint32_t c0 = q.w, c1 = q.z, c2 = q.y, c3 = q.x;  // bins 255 - 4l, 254 - 4l, 253 - 4l, 252 - 4l
+    const uint32_t t3 = c0 + c1 + c2 + c3;
+    const uint32_t incl = wave_incl_scan(t3);
+    const uint32_t e0 = incl - t3;       // keys in bins above this lane's
+    const uint32_t e1 = e0 + c0, e2 = e1 + c1, e3 = e2 + c2;
+    const uint64_t hit = __ballot(e0 < r && incl >= r);
+    const uint32_t i = e1 >= r ? 0u : e2 >= r ? 1u : e3 >= r ? 2u : 3u;
+    const uint32_t d = 255u - 4u * (uint32_t)lane - i;
+    const uint32_t ab = i == 0 ? e0 : i == 1 ? e1 : i == 2 ? e2 : e3;
+    const uint32_t ct = i == 0 ? c0 : i == 1 ? c1 : i == 2 ? c2 : c3;
+    if (hit == 0) {
+        *above = 0;
+        *count = 0;
+        return 0;
+    }
+    const int src = __ffsll((unsigned long long)hit) - 1;
+    *above = __builtin_amdgcn_readlane(ab, src);
+    *count = __builtin_amdgcn_readlane(ct, src);
+    return __builtin_amdgcn_readlane(d, src);
+}
+
 // Descending bitonic sort of the composites of A[0..count) (count <= KMAX, a power of
 // two).  Padding entries get composite 0, which no real element has (~pos != 0).
 template <int NT>
@@ -502,29 +531,30 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 
 // P = the key prefix of the rr-th largest sample, MSB first, one 8-bit digit per pass;
 // a pass runs past the second only while the selected bin still holds more than
-// kRefineAbove samples, so after four passes P is that sample's key itself.  `hist` is
-// 256 LDS words; merge(pass, hist) turns this workgroup's histogram into the one the
-// select reads (nothing to do for a single workgroup, a device-wide sum over the row's
-// tiles otherwise).  Every workgroup of a row takes the same decisions.
+// kRefineAbove samples, so after four passes P is that sample's key itself.  Pass p
+// counts into hist4 + 256 p (zeroed beforehand, a barrier behind), so no pass waits for
+// the previous one to be cleared; every wave then selects the digit on its own.
+// merge(pass, hist) turns this workgroup's histogram into the one the select reads
+// (nothing to do for a single workgroup, a device-wide sum over the row's tiles
+// otherwise).  Every wave, and every workgroup of a row, takes the same decisions.
 template <int NT, class Merge>
-__device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist,
-                                                 uint32_t* wsum, uint32_t* sel, Merge&& merge) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, r_rem = rr, P = 0;
+__device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist4,
+                                                 Merge&& merge) {
+    uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        if (pass >= 2 && sel[2] <= kRefineAbove) break;  // uniform: bin resolved
-        if (tid < kRadix) hist[tid] = 0;
-        __syncthreads();
+        if (pass >= 2 && cnt <= kRefineAbove) break;  // uniform: bin resolved
+        uint32_t* hist = hist4 + pass * kRadix;
 #pragma unroll
         for (int i = 0; i < kSamplesPerLane; ++i)
             if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(hist, (sk[i] >> shift) & 0xFFu);
         __syncthreads();
         merge(pass, hist);
-        select_digit<NT>(hist, r_rem, wsum, sel);
-        prefix = (prefix << 8) | sel[0];
-        r_rem -= sel[1];
+        uint32_t above;
+        const uint32_t d = wave_select_digit(hist, r_rem, &above, &cnt);
+        prefix = (prefix << 8) | d;
+        r_rem -= above;
         P = prefix << shift;
     }
     return P;
@@ -674,6 +704,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     // comparison loop runs the wave's longest bucket, uniformly.
     constexpr int RUNR = 2;
     for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
+        if (q0 + (uint32_t)(tid & ~63) >= kept) break;  // wave-uniform: nothing left for this wave
         uint64_t cc[RUNR];
         uint32_t st[RUNR], len[RUNR], rank[RUNR];
         uint32_t lmax = 0;
@@ -730,6 +761,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
 
     // ------------------------------------------------ clear LDS state
     for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
+    for (int i = tid; i < 4 * kRadix; i += NT) s.bucket[i] = 0;  // the sample-digit histograms
     if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot
@@ -755,8 +787,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     {
         // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
         const uint32_t rr = fast_mode == 2 ? 1u : pivot_rank(nsamp, m, nt);
-        if (m < nt && rr < (uint32_t)nsamp)
-            P = pivot_passes<NT>(sk, rr, s.bucket, s.wsum, s.ctl + kCtlSel, [](int, uint32_t*) {});
+        if (m < nt && rr < (uint32_t)nsamp) P = pivot_passes<NT>(sk, rr, s.bucket, [](int, uint32_t*) {});
     }
     {
         uint32_t lo = 0xFFFFFFFFu;
@@ -765,10 +796,6 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         lo = wave_min(lo);
         if (lane == 0) __hip_atomic_fetch_min(&s.ctl[kCtlLo], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    __syncthreads();  // sample extremes published; sample histogram no longer read
-    uint32_t L, U;
-    bucket_range(P, s.ctl[kCtlLo], s.ctl[kCtlSmaxAll], s.ctl[kCtlSmaxFin], &L, &U);
-    for (int i = tid; i < kBuckets / 2; i += NT) s.bucket[i] = 0;
     const AboveP ap(P);
 
     // ------------------------------------------------ count pass: keys > P per lane
@@ -779,8 +806,13 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) { cnt += (ap.gt<false>(x) && ok) ? 1u : 0u; });
     uint32_t c_gt;
     uint32_t o = block_excl_scan<NT>(cnt, s.wsum, &c_gt);
+    // (past this barrier every wave is done with the sample histograms and has published
+    // its sample extremes)
     if (c_gt > (uint32_t)FS::CCAP) return false;  // uniform
     const bool ties = c_gt < (uint32_t)m;          // uniform: keys == P fill the tail
+    uint32_t L, U;
+    bucket_range(P, s.ctl[kCtlLo], s.ctl[kCtlSmaxAll], s.ctl[kCtlSmaxFin], &L, &U);
+    for (int i = tid; i < kBuckets / 2; i += NT) s.bucket[i] = 0;
 
     // ------------------------------------------------ write pass: (bits, position) of the
     // candidates to LDS; keys == P into the position bitmap when the tail needs them.
@@ -901,6 +933,7 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
 
     // ------------------------------------------------ clear LDS state
     for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
+    for (int i = tid; i < 4 * kRadix; i += NT) s.bucket[i] = 0;  // the sample-digit histograms
     if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot (row-wide)
@@ -927,7 +960,7 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
         if (rr < (uint32_t)nsamp) {
             uint32_t* gsamp = rw + kRowSampHist;
-            P = pivot_passes<NT>(sk, rr, s.bucket, s.wsum, s.ctl + kCtlSel, [&](int pass, uint32_t* h) {
+            P = pivot_passes<NT>(sk, rr, s.bucket, [&](int pass, uint32_t* h) {
                 if (tid < kRadix) {
                     const uint32_t c = h[tid];
                     if (c) atomicAdd(&gsamp[pass * kRadix + tid], c);
