@@ -49,7 +49,7 @@ struct DeviceInfo {
     bool gfx950 = false;
     int cus = 0;
     size_t max_lds = 0;
-    int multi_occ[3][2] = {};  // [tile index][kmax index] co-resident workgroups per CU
+    int multi_occ[3][2] = {};   // [tile index][kmax index] co-resident workgroups per CU
 };
 
 std::mutex g_mu;
@@ -65,15 +65,17 @@ hipError_t prepare_kernel() {
                                (int)smem_bytes<TILE, KMAX, MULTI>());
 }
 
-template <int TILE, int KMAX>
-int multi_occupancy() {
-    if (prepare_kernel<TILE, KMAX, true>() != hipSuccess) return 0;
+template <int TILE, int KMAX, bool MULTI>
+int occupancy() {
+    if (prepare_kernel<TILE, KMAX, MULTI>() != hipSuccess) return 0;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel_ptr<TILE, KMAX, true>(), Shape<TILE>::NT,
-                                                     smem_bytes<TILE, KMAX, true>()) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel_ptr<TILE, KMAX, MULTI>(), Shape<TILE>::NT,
+                                                     smem_bytes<TILE, KMAX, MULTI>()) != hipSuccess)
         return 0;
     return blocks;
 }
+template <int TILE, int KMAX>
+int multi_occupancy() { return occupancy<TILE, KMAX, true>(); }
 
 template <int TILE>
 void prepare_both(hipError_t* e) {
@@ -164,7 +166,7 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
     if (!multi) {
         pl->tile = max_len <= 4096 ? 4096 : max_len <= 8192 ? 8192 : max_len <= 16384 ? 16384 : 32768;
         pl->tiles_per_row = 1;
-        pl->grid = B;
+        pl->grid = B;  // one workgroup per row: the dispatcher balances rows of unequal length
         pl->ws_bytes = 0;
     } else {
         pl->tile = g_multi_tile ? g_multi_tile : 8192;

@@ -130,6 +130,10 @@ __device__ __forceinline__ int opaque_tid() {
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
+// base + the number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below_plus(uint64_t m, uint32_t base) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, base));
+}
 
 // DPP lane moves (gfx9 encodings): row_shr:n shifts within 16-lane rows, row_bcast:15 /
 // row_bcast:31 carry the last lane of a row / of the lower half into the next rows.
@@ -199,36 +203,47 @@ __device__ __forceinline__ uint32_t claim_slot(bool pred, uint32_t* counter) {
 // ----------------------------------------------------------------------------- loads
 
 // Load one tile's raw bits: slot (v, c) of lane t holds window position
-// (v * NT + t) * 4 + c.  All loads are issued before any use.  The buffer resource
-// covers exactly the tile's valid bytes, so slots past the window read 0 (callers mask
-// them by position).  A 16-byte aligned tile uses 16-byte loads (a partially valid one
-// never leaves the 16-byte chunk holding valid data); otherwise 4-byte loads.
+// (v * NT + t) * 4 + c.  The buffer resource covers exactly the tile's valid bytes, so
+// slots past the window read 0 (callers mask them by position).  A 16-byte aligned tile
+// uses 16-byte loads (a partially valid one never leaves the 16-byte chunk holding valid
+// data); otherwise 4-byte loads.  PART 0 loads the groups holding the pivot samples,
+// PART 1 the others, PART 2 all of them (sample groups issued first).
 template <int NT, int EPT>
-__device__ __forceinline__ void load_tile(uint32_t (&u)[EPT], const uint32_t* src, int nt) {
+constexpr bool sample_group(int v) {
+    return v % (EPT / 4 >= kSamplesPerLane ? EPT / 4 / kSamplesPerLane : 1) == 0;
+}
+
+template <int NT, int EPT, int PART>
+__device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const uint32_t* src, int nt) {
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src), (short)0, nt * 4, kBufferWord3);
     const int tid = opaque_tid();
     constexpr int G4 = EPT / 4;
-    constexpr int SG = G4 >= kSamplesPerLane ? G4 / kSamplesPerLane : 1;  // pivot-sample groups first
-    if ((((uintptr_t)src) & 15u) == 0) {
+    const bool aligned = (((uintptr_t)src) & 15u) == 0;
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass)
+    for (int pass = 0; pass < 2; ++pass) {
+        if ((PART == 0 && pass == 1) || (PART == 1 && pass == 0)) continue;
 #pragma unroll
-            for (int v = 0; v < G4; ++v) {
-                if ((v % SG == 0) != (pass == 0)) continue;
+        for (int v = 0; v < G4; ++v) {
+            if (sample_group<NT, EPT>(v) != (pass == 0)) continue;
+            if (aligned) {
                 const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (v * NT + tid) * 16, 0, 0);
                 u[4 * v + 0] = q[0];
                 u[4 * v + 1] = q[1];
                 u[4 * v + 2] = q[2];
                 u[4 * v + 3] = q[3];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, ((v * NT + tid) * 4 + c) * 4, 0, 0);
             }
-    } else {
-#pragma unroll
-        for (int v = 0; v < EPT / 4; ++v)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, ((v * NT + tid) * 4 + c) * 4, 0, 0);
+        }
     }
+}
+
+template <int NT, int EPT>
+__device__ __forceinline__ void load_tile(uint32_t (&u)[EPT], const uint32_t* src, int nt) {
+    load_tile_part<NT, EPT, 2>(u, src, nt);
 }
 
 // ----------------------------------------------------------------------------- shared memory
@@ -275,7 +290,10 @@ struct FastSmem {
                                     // while choosing P, a 256-bin 32-bit sample histogram
     uint64_t S[SCAP];             // kept candidates as composites, grouped by bucket
     union {
-        uint2 cand[CCAP];         // candidates: (raw bits, position)
+        struct {
+            uint32_t bits[CCAP];  // candidates: raw bits
+            uint32_t pos[CCAP];   //   and positions
+        } cand;
         struct {
             uint32_t idx[KMAX];   // output staging (after the candidates are scattered)
             uint32_t val[KMAX];
@@ -602,9 +620,11 @@ struct AboveP {
 // grouped by bucket as composites (key << 32 | ~position), which are unique and whose
 // descending order is the canonical order; a kept candidate's slot is its bucket's start
 // plus the number of larger composites in its bucket.
-// LIMITED: returns false, having emitted nothing, when more than SCAP candidates are kept
-// or a kept bucket holds more than kBucketLimit; otherwise c_gt <= SCAP is the caller's.
-// On entry the bucket array and ctl[kCtlBt..kCtlMaxBucket] are zero, a barrier behind.
+// LIMITED: returns false, having emitted nothing, when more than SCAP candidates are
+// kept, and sets ctl[kCtlMaxBucket] (some slots then stay unwritten: the caller must check
+// it after a barrier) when a kept bucket holds more than kBucketLimit; otherwise
+// c_gt <= SCAP is the caller's.  On entry the bucket array and ctl[kCtlBt..kCtlMaxBucket]
+// are zero, a barrier behind.
 template <int NT, int SCAP, int CPT, bool LIMITED, class Src, class Emit>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             uint32_t c_gt, uint32_t m, bool ties, uint32_t L, uint32_t U, Emit&& emit) {
@@ -630,44 +650,48 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     __syncthreads();
 
     // ---- suffix scan: bucket starts.  Thread t owns buckets [kBuckets - (t + 1) * BPT,
-    // kBuckets - t * BPT), scanned from the top, so slot offsets grow with t.
-    uint32_t cnts[BPT];
-    uint32_t tsum = 0;
-    const int btop = kBuckets - tid * BPT - 1;  // odd: the high half of word btop / 2
+    // kBuckets - t * BPT), i.e. counter words W - (t + 1) * WPT .. W - t * WPT - 1, scanned
+    // from the top (high half first), so slot offsets grow with t.
+    constexpr int WPT = BPT / 2;  // counter words per thread
+    const int w0 = kBuckets / 2 - (tid + 1) * WPT;
+    uint32_t cw[WPT];
+    uint32_t packed = 0;  // both halves summed at once: no carry, counts stay below 2^16
 #pragma unroll
-    for (int i = 0; i < BPT; i += 2) {
-        const uint32_t w = bucket[(btop - i) >> 1];
-        cnts[i] = w >> 16;          // bucket btop - i
-        cnts[i + 1] = w & 0xFFFFu;  // bucket btop - i - 1
-        tsum += cnts[i] + cnts[i + 1];
+    for (int i = 0; i < WPT; ++i) {
+        cw[i] = bucket[w0 + i];
+        packed += cw[i];
     }
+    const uint32_t tsum = (packed >> 16) + (packed & 0xFFFFu);
     uint32_t total;
-    uint32_t run = block_excl_scan<NT>(tsum, wsum + 16, &total);
-    uint32_t mx = 0;
-    uint32_t hi_start = 0;
+    const uint32_t run0 = block_excl_scan<NT>(tsum, wsum + 16, &total);
+    {
+        uint32_t run = run0;
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-        const uint32_t st = run;
-        if ((i & 1) == 0) {
-            hi_start = st;
-        } else {
-            bucket[(btop - i) >> 1] = (hi_start << 16) | st;  // cursors start at first slots
+        for (int i = WPT - 1; i >= 0; --i) {  // word w0 + i holds buckets 2 (w0 + i) + 1 (high), 2 (w0 + i)
+            const uint32_t hi = cw[i] >> 16, lo = cw[i] & 0xFFFFu;
+            bucket[w0 + i] = (run << 16) | (run + hi);  // cursors start at first slots
+            run += hi + lo;
         }
-        if (ties || st < m) mx = max(mx, cnts[i]);
-        if (!ties && st < m && st + cnts[i] >= m) {
-            ctl[kCtlBt] = (uint32_t)(btop - i);  // threshold bucket
-            ctl[kCtlKept] = st + cnts[i];        // kept candidates (slots of buckets >= b_t)
-        }
-        run += cnts[i];
     }
-    if (LIMITED) {
-        mx = wave_max(mx);
-        if (lane == 0) __hip_atomic_fetch_max(&ctl[kCtlMaxBucket], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (!ties && run0 < m && run0 + tsum >= m) {  // this thread owns the threshold bucket
+        uint32_t run = run0;
+#pragma unroll
+        for (int i = WPT - 1; i >= 0; --i) {
+#pragma unroll
+            for (int h = 1; h >= 0; --h) {
+                const uint32_t c = h ? cw[i] >> 16 : cw[i] & 0xFFFFu;
+                if (run < m && run + c >= m) {
+                    ctl[kCtlBt] = (uint32_t)(2 * (w0 + i) + h);  // threshold bucket
+                    ctl[kCtlKept] = run + c;                     // kept: slots of buckets >= b_t
+                }
+                run += c;
+            }
+        }
     }
     __syncthreads();
     const uint32_t bt = ties ? 0u : ctl[kCtlBt];
     const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
-    if (LIMITED && (kept > (uint32_t)SCAP || ctl[kCtlMaxBucket] > (uint32_t)kBucketLimit)) return false;  // uniform
+    if (LIMITED && kept > (uint32_t)SCAP) return false;  // uniform
 
     // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write)
     constexpr int SUNR = 2;
@@ -721,6 +745,10 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
             rank[i] = 0;
         }
         lmax = wave_max(lmax);
+        if (LIMITED && lmax > (uint32_t)kBucketLimit) {  // too long to rank by comparisons
+            if (lane == 0) ctl[kCtlMaxBucket] = 1u;
+            lmax = 0;
+        }
         for (uint32_t f = 0; f < lmax; ++f) {
 #pragma unroll
             for (int i = 0; i < RUNR; ++i) {
@@ -798,16 +826,30 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     }
     const AboveP ap(P);
 
-    // ------------------------------------------------ count pass: keys > P per lane
-    uint32_t cnt = 0;
+    // ------------------------------------------------ count pass: keys > P per wave
+    // (ballot popcounts: the counting is scalar work)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t wcnt = 0;
     if (P >= 0x80000000u)
-        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) { cnt += (ap.gt<true>(x) && ok) ? 1u : 0u; });
+        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
+            wcnt += (uint32_t)__popcll(__ballot(ap.gt<true>(x)) & __ballot(ok));
+        });
     else
-        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) { cnt += (ap.gt<false>(x) && ok) ? 1u : 0u; });
-    uint32_t c_gt;
-    uint32_t o = block_excl_scan<NT>(cnt, s.wsum, &c_gt);
+        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
+            wcnt += (uint32_t)__popcll(__ballot(ap.gt<false>(x)) & __ballot(ok));
+        });
+    if (lane == 0) s.wsum[wave] = wcnt;
+    __syncthreads();
     // (past this barrier every wave is done with the sample histograms and has published
     // its sample extremes)
+    uint32_t o = 0, c_gt = 0;  // this wave's first candidate slot; all candidates
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t c = s.wsum[w];
+        o += w < wave ? c : 0u;
+        c_gt += c;
+    }
+    o = __builtin_amdgcn_readfirstlane(o);  // wave-uniform: keep the running slot scalar
     if (c_gt > (uint32_t)FS::CCAP) return false;  // uniform
     const bool ties = c_gt < (uint32_t)m;          // uniform: keys == P fill the tail
     uint32_t L, U;
@@ -822,10 +864,14 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         constexpr bool EQ = decltype(eq_tag)::value;
         uint32_t nib = 0;
         visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int c, int v, bool ok, int t4) {
-            if (ap.gt<POS>(x) && ok) {
-                s.u.cand[o] = make_uint2(x, (uint32_t)(t4 + (v * NT * 4 + c)));
-                ++o;
+            const bool gx = ap.gt<POS>(x);
+            const uint64_t mk = __ballot(gx) & __ballot(ok);
+            if (gx && ok) {
+                const uint32_t q = lanes_below_plus(mk, o);
+                s.u.cand.bits[q] = x;
+                s.u.cand.pos[q] = (uint32_t)(t4 + (v * NT * 4 + c));
             }
+            o += (uint32_t)__popcll(mk);
             if (EQ) {
                 nib |= (ap.eq<POS>(x) && ok ? 1u : 0u) << c;
                 if (c == 3) {
@@ -856,7 +902,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
 
     // ------------------------------------------------ order the candidates
     if (!bucket_rank<NT, FS::SCAP, (FS::CCAP + NT - 1) / NT, true>(
-            s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return s.u.cand[j]; }, c_gt, (uint32_t)m, ties, L, U,
+            s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return make_uint2(s.u.cand.bits[j], s.u.cand.pos[j]); },
+            c_gt, (uint32_t)m, ties, L, U,
             [&](uint32_t slot, uint32_t pos, uint32_t bits) {
                 s.u.out.idx[slot] = pos;
                 s.u.out.val[slot] = bits;
@@ -893,6 +940,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         }
     }
     __syncthreads();
+    if (s.ctl[kCtlMaxBucket]) return false;  // uniform: a bucket too long to rank
 
     // ------------------------------------------------ store the row
     for (int q = tid; q < m; q += NT) {
@@ -1382,11 +1430,12 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     write_padding<NT>(oidx, oval, m, k);
 }
 
-// ----------------------------------------------------------------------------- one item
+// ----------------------------------------------------------------------------- rows
 
-template <int NT, int EPT, int KMAX, bool MULTI>
-__device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, int b, int tile) {
-    constexpr int TILE = NT * EPT;
+// Row setup: window (clamped length, start), output rows, and the tile of it this
+// workgroup item covers (nt <= 0 when the row has no such tile).
+template <int TILE, bool MULTI>
+__device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     RowCtx r;
     const int32_t len = p.lengths ? p.lengths[b] : p.max_len;
     r.b = b;
@@ -1396,12 +1445,19 @@ __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, K
     r.k = p.k;
     r.m = min(r.k, r.n);
     r.ntiles = MULTI ? max(1, (r.n + TILE - 1) / TILE) : 1;
-    if (tile >= r.ntiles) return;
     r.multi = MULTI && r.ntiles > 1;
     r.oidx = p.out_idx + (int64_t)b * r.k;
     r.oval = p.out_val ? p.out_val + (int64_t)b * r.k : nullptr;
     r.j0 = tile * TILE;
     r.nt = min(TILE, r.n - r.j0);
+    return r;
+}
+
+// One (row, tile) item: a whole row in the one-workgroup-per-row kernel (MULTI false).
+template <int NT, int EPT, int KMAX, bool MULTI>
+__device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, int b, int tile) {
+    const RowCtx r = row_setup<NT * EPT, MULTI>(p, b, tile);
+    if (tile >= r.ntiles) return;
 
     __syncthreads();  // previous item of a persistent workgroup is done with LDS
 
@@ -1417,13 +1473,12 @@ __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, K
     if (p.fast) {
         if (!r.multi) {
             if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
-            __syncthreads();  // fall back to the exact path on the same registers
         } else {
             if constexpr (MULTI) {
                 if (multi_fast_tile<NT, EPT, KMAX>(p, r, s.mfast, u, bar_target)) return;
-                __syncthreads();
             }
         }
+        __syncthreads();  // fall back to the exact path on the same registers
     }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
