@@ -321,12 +321,15 @@ struct NoSmem {};
 // Exact-path staging: smaller in one-workgroup-per-row kernels so that the LDS footprint
 // lets three rows share a CU.
 template <bool MULTI>
-constexpr int stage_entries() { return MULTI ? kStageCap : 2560; }
+constexpr int stage_entries() { return MULTI ? 3072 : 2560; }
 
+// LDS of one workgroup: the exact path's, or the pivot path's of the kernel's kind (the
+// several-workgroups-per-row kernel takes its one-tile rows through the workspace
+// candidate list too, so its LDS never holds a whole candidate list).
 template <int NT, int EPT, int KMAX, bool MULTI>
 union SmemAll {
     ExactSmem<NT, EPT, KMAX, stage_entries<MULTI>()> exact;
-    FastSmem<NT, EPT, KMAX> fast;
+    typename std::conditional<MULTI, NoSmem, FastSmem<NT, EPT, KMAX>>::type fast;
     typename std::conditional<MULTI, MultiFastSmem<NT, EPT, KMAX>, NoSmem>::type mfast;
 };
 
@@ -432,6 +435,31 @@ __device__ __forceinline__ void bitonic_desc(const PairList& A, int count) {
                 if ((a < b) == desc) {
                     A.set_composite(lo, b);
                     A.set_composite(hi, a);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// The same on a plain array of composites.
+template <int NT>
+__device__ __forceinline__ void bitonic_desc_u64(uint64_t* A, int count) {
+    const int tid = threadIdx.x;
+    int P = 1;
+    while (P < count) P <<= 1;
+    for (int i = count + tid; i < P; i += NT) A[i] = 0;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < (P >> 1); i += NT) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const uint64_t a = A[lo], b = A[hi];
+                const bool desc = (lo & size) == 0;
+                if ((a < b) == desc) {
+                    A[lo] = b;
+                    A[hi] = a;
                 }
             }
             __syncthreads();
@@ -622,9 +650,11 @@ struct AboveP {
 // plus the number of larger composites in its bucket.
 // LIMITED: returns false, having emitted nothing, when more than SCAP candidates are
 // kept, and sets ctl[kCtlMaxBucket] (some slots then stay unwritten: the caller must check
-// it after a barrier) when a kept bucket holds more than kBucketLimit; otherwise
-// c_gt <= SCAP is the caller's.  On entry the bucket array and ctl[kCtlBt..kCtlMaxBucket]
-// are zero, a barrier behind.
+// it after a barrier) when a kept bucket holds more than kBucketLimit.  Otherwise
+// c_gt <= SCAP (a power of two) is the caller's, and when some bucket holds more than
+// kBucketLimit the kept composites are ordered by a bitonic sort of S instead (the
+// comparison count of ranking grows with the square of a bucket's length).  On entry the
+// bucket array and ctl[kCtlBt..kCtlMaxBucket] are zero, a barrier behind.
 template <int NT, int SCAP, int CPT, bool LIMITED, class Src, class Emit>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             uint32_t c_gt, uint32_t m, bool ties, uint32_t L, uint32_t U, Emit&& emit) {
@@ -662,6 +692,13 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         packed += cw[i];
     }
     const uint32_t tsum = (packed >> 16) + (packed & 0xFFFFu);
+    if (!LIMITED) {  // longest bucket (kept or not: a safe overestimate)
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) mx = max(mx, max(cw[i] >> 16, cw[i] & 0xFFFFu));
+        mx = wave_max(mx);
+        if (lane == 0) __hip_atomic_fetch_max(&ctl[kCtlMaxBucket], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     uint32_t total;
     const uint32_t run0 = block_excl_scan<NT>(tsum, wsum + 16, &total);
     {
@@ -722,6 +759,13 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
             if (pos[d] < (uint32_t)SCAP) S[pos[d]] = comp[d];
     }
     __syncthreads();
+
+    if (!LIMITED && ctl[kCtlMaxBucket] > (uint32_t)kBucketLimit) {  // uniform
+        static_assert(LIMITED || (SCAP & (SCAP - 1)) == 0, "the sort pads S to a power of two");
+        bitonic_desc_u64<NT>(S, (int)kept);
+        for (uint32_t q = tid; q < mlim; q += NT) emit(q, ~(uint32_t)S[q], bits_of((uint32_t)(S[q] >> 32)));
+        return true;
+    }
 
     // ---- rank inside buckets -> final slot.  Bucket b's counter now holds its end; its
     // start is the end of bucket b + 1.  Each lane ranks RUNR elements at once; the
@@ -1471,12 +1515,10 @@ __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, K
 
     uint32_t bar_target = 0;  // row barriers passed so far x tiles (several workgroups per row)
     if (p.fast) {
-        if (!r.multi) {
-            if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
+        if constexpr (MULTI) {
+            if (multi_fast_tile<NT, EPT, KMAX>(p, r, s.mfast, u, bar_target)) return;
         } else {
-            if constexpr (MULTI) {
-                if (multi_fast_tile<NT, EPT, KMAX>(p, r, s.mfast, u, bar_target)) return;
-            }
+            if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
         }
         __syncthreads();  // fall back to the exact path on the same registers
     }

@@ -81,6 +81,22 @@ def _negative(B=8, L=9000, k=1500, name="gpu_negative"):
     return W.Workload(name, buf, (np.arange(B) * L).astype(np.int32), np.full(B, L, np.int32), L, k)
 
 
+def _tie_block(B=6, L=20000, k=2048, name="gpu_tie_block"):
+    """Rows whose top k hold a block of 1500 bitwise-equal scores above the rest: the
+    candidates above the pivot fall into one long bucket (exercises the long-bucket
+    fallbacks: the exact path for one-workgroup rows, a full sort of the kept candidates
+    for rows split over workgroups)."""
+    buf = np.empty(B * L, np.float32)
+    for b in range(B):
+        rng = W.row_rng(W.seed_of(name), b)
+        row = W.relu_sum_mixture(rng, L, 0.3)
+        row = np.minimum(row, np.float32(4.0))
+        pos = rng.choice(L, size=1500, replace=False)
+        row[pos] = np.float32(5.0) if b % 2 == 0 else np.float32(-0.0)
+        buf[b * L:(b + 1) * L] = row
+    return W.Workload(name, buf, (np.arange(B) * L).astype(np.int32), np.full(B, L, np.int32), L, k)
+
+
 SMALL = {
     "quantized": _quantized,
     "outliers": _outliers,
@@ -92,6 +108,7 @@ SMALL = {
     "long_context": lambda: W.long_context(B=5, L=40000, k=2048, short_n=1500, name="gpu_long"),
     "small_k": lambda: W.decode_ragged(B=16, n_lo=1, n_hi=6000, k=7, name="gpu_smallk"),
     "k_not_pow2": lambda: W.decode_ragged(B=16, n_lo=1, n_hi=12000, k=3000, name="gpu_k3000"),
+    "tie_block": _tie_block,
 }
 _SMALL_CACHE = {}
 
