@@ -21,7 +21,8 @@ using detk::SmemAll;
 // VGPRs; MINW is the waves per SIMD their register allocation must allow.
 //   one workgroup per row: 4096 = 256 x 16, 8192 = 512 x 16, 16384 = 512 x 32,
 //                          32768 = 1024 x 32
-//   several per row:       4096 = 256 x 16, 8192 = 512 x 16, 16384 = 512 x 32
+//   several per row:       4096 = 256 x 16, 8192 = 512 x 16, 16384 = 512 x 32,
+//                          32768 = 1024 x 32
 constexpr int kSingleMaxLen = 32768;
 
 template <int TILE> struct Shape;
@@ -49,7 +50,7 @@ struct DeviceInfo {
     bool gfx950 = false;
     int cus = 0;
     size_t max_lds = 0;
-    int multi_occ[3][2] = {};   // [tile index][kmax index] co-resident workgroups per CU
+    int multi_occ[4][2] = {};   // [tile index][kmax index] co-resident workgroups per CU
 };
 
 std::mutex g_mu;
@@ -104,6 +105,8 @@ int device_info(int device, DeviceInfo* out) {
             d.multi_occ[1][1] = multi_occupancy<8192, 4096>();
             d.multi_occ[2][0] = multi_occupancy<16384, 2048>();
             d.multi_occ[2][1] = multi_occupancy<16384, 4096>();
+            d.multi_occ[3][0] = multi_occupancy<32768, 2048>();
+            d.multi_occ[3][1] = multi_occupancy<32768, 4096>();
             prepare_both<4096>(&e);
             prepare_both<8192>(&e);
             prepare_both<16384>(&e);
@@ -141,7 +144,7 @@ size_t lds_bytes_t(int tile, int kmax) {
 }
 size_t lds_bytes(int tile, int kmax, bool multi) { return multi ? lds_bytes_t<true>(tile, kmax) : lds_bytes_t<false>(tile, kmax); }
 
-int tile_index(int tile) { return tile == 4096 ? 0 : tile == 8192 ? 1 : 2; }
+int tile_index(int tile) { return tile == 4096 ? 0 : tile == 8192 ? 1 : tile == 16384 ? 2 : 3; }
 
 // Decide the launch shape from host-known sizes only.
 int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
@@ -158,9 +161,9 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
     } else if (g_force_path == 2) {
         multi = true;
     } else {
-        // One workgroup per row when the row fits a tile and the batch alone fills the
-        // chip; long rows, or few rows of moderate length, split over workgroups.
-        multi = max_len > kSingleMaxLen || (max_len > 8192 && (int64_t)B * 2 < dev.cus);
+        // One workgroup per row whenever the row fits one tile (splitting a row costs row
+        // barriers, which outweigh the extra parallelism even for small batches).
+        multi = max_len > kSingleMaxLen;
     }
     pl->multi = multi;
     if (!multi) {
@@ -169,7 +172,7 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         pl->grid = B;  // one workgroup per row: the dispatcher balances rows of unequal length
         pl->ws_bytes = 0;
     } else {
-        pl->tile = g_multi_tile ? g_multi_tile : 8192;
+        pl->tile = g_multi_tile ? g_multi_tile : 32768;  // fewest tiles per row: fewest barrier arrivals
         const int64_t tpr = max_len == 0 ? 1 : ((int64_t)max_len + pl->tile - 1) / pl->tile;
         const int occ = dev.multi_occ[tile_index(pl->tile)][ki];
         const int64_t capacity = (int64_t)occ * dev.cus;
@@ -228,8 +231,10 @@ hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
                          : launch<4096, 4096, true>(p, pl.grid, pl.lds, stream);
     case 8192: return k2 ? launch<8192, 2048, true>(p, pl.grid, pl.lds, stream)
                          : launch<8192, 4096, true>(p, pl.grid, pl.lds, stream);
-    default: return k2 ? launch<16384, 2048, true>(p, pl.grid, pl.lds, stream)
-                       : launch<16384, 4096, true>(p, pl.grid, pl.lds, stream);
+    case 16384: return k2 ? launch<16384, 2048, true>(p, pl.grid, pl.lds, stream)
+                          : launch<16384, 4096, true>(p, pl.grid, pl.lds, stream);
+    default: return k2 ? launch<32768, 2048, true>(p, pl.grid, pl.lds, stream)
+                       : launch<32768, 4096, true>(p, pl.grid, pl.lds, stream);
     }
 }
 
@@ -336,7 +341,8 @@ int detk_debug_set(int what, int value) {
         g_stage_cap = value;
         return DETK_OK;
     case DETK_DEBUG_MULTI_TILE:
-        if (value != 0 && value != 4096 && value != 8192 && value != 16384) return DETK_ERR_INVALID_ARG;
+        if (value != 0 && value != 4096 && value != 8192 && value != 16384 && value != 32768)
+            return DETK_ERR_INVALID_ARG;
         g_multi_tile = value;
         return DETK_OK;
     case DETK_DEBUG_FAST:

@@ -112,11 +112,11 @@ int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* st
  *                                  candidate count staged in LDS (0 forces every
  *                                  refinement pass to rescan the register-resident row).
  *   what = DETK_DEBUG_MULTI_TILE:  0 default; else elements per workgroup tile of the
- *                                  multi-workgroup path (4096, 8192 or 16384).
- *   what = DETK_DEBUG_FAST:        1 default (sampled-pivot path on rows that fit one
- *                                  workgroup, exact radix path when it misses); 0 exact
- *                                  radix path only; 2 pivot forced to miss, so every such
- *                                  row starts on the pivot path and falls back.
+ *                                  multi-workgroup path (4096, 8192, 16384 or 32768).
+ *   what = DETK_DEBUG_FAST:        1 default (sampled-pivot path, exact radix path when
+ *                                  it misses); 0 exact radix path only; 2 pivot forced
+ *                                  to miss, so every row starts on the pivot path and
+ *                                  falls back.
  * Returns DETK_OK or DETK_ERR_INVALID_ARG.
  */
 #define DETK_DEBUG_PATH 1

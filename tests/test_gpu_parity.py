@@ -121,8 +121,8 @@ def _small(name):
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 @pytest.mark.parametrize("shape", ["auto", "single", "single_exact", "single_pivot_miss", "multi4096", "multi8192",
-                                   "multi_exact", "multi_pivot_miss", "single_rescan", "multi_rescan",
-                                   "multi_tinystage"])
+                                   "multi16384", "multi32768", "multi_exact", "multi_pivot_miss", "single_rescan",
+                                   "multi_rescan", "multi_tinystage"])
 def test_small_workloads(dev, name, shape):
     wl = _small(name)
     if shape.startswith("single") and wl.max_len > 32768:
@@ -134,6 +134,8 @@ def test_small_workloads(dev, name, shape):
         "single_pivot_miss": {"path": 1, "fast": 2},
         "multi4096": {"path": 2, "multi_tile": 4096},
         "multi8192": {"path": 2, "multi_tile": 8192},
+        "multi16384": {"path": 2, "multi_tile": 16384},
+        "multi32768": {"path": 2, "multi_tile": 32768},
         "multi_exact": {"path": 2, "multi_tile": 4096, "fast": 0},
         "multi_pivot_miss": {"path": 2, "multi_tile": 4096, "fast": 2},
         "single_rescan": {"path": 1, "stage_cap": 0, "fast": 0},
