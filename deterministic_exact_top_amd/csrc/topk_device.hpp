@@ -46,7 +46,8 @@ constexpr int kStageCap = 4096;                 // exact path: LDS threshold-bin
 constexpr int kBuckets = 4096;                  // fast path: buckets over the candidate key range
 constexpr int kBucketBits = 12;
 constexpr int kBucketLimit = 128;               // fast path: largest bucket ranked by comparisons
-static_assert(kBuckets / 2 >= 256, "the packed bucket array doubles as the sample histogram");
+constexpr int kKeptSlack = 96;                  // fast path: kept candidates past KMAX that fit S
+static_assert(kBuckets / 2 >= 4 * 256, "the packed bucket array doubles as the sample histograms");
 constexpr int kSamplesPerLane = 4;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 // Per-row workspace words of the multi-workgroup path, zeroed before each launch.
@@ -282,23 +283,18 @@ struct FastSmem {
     static constexpr int TILE = NT * EPT;
     static constexpr int BWORDS = TILE / 32;
     static constexpr int CCAP = cand_cap_single<KMAX>();
-    static constexpr int SCAP = KMAX + kBucketLimit;
+    static constexpr int SCAP = KMAX + kKeptSlack;
     uint32_t ctl[16];             // control words, kCtl* below
     uint32_t wsum[32];
     uint32_t bitmap[BWORDS];      // positions with key == P
-    uint32_t bucket[kBuckets / 2];  // 16-bit bucket counters, cursors and ends, two per word;
-                                    // while choosing P, a 256-bin 32-bit sample histogram
-    uint64_t S[SCAP];             // kept candidates as composites, grouped by bucket
-    union {
-        struct {
-            uint32_t bits[CCAP];  // candidates: raw bits
-            uint32_t pos[CCAP];   //   and positions
-        } cand;
-        struct {
-            uint32_t idx[KMAX];   // output staging (after the candidates are scattered)
-            uint32_t val[KMAX];
-        } out;
-    } u;
+    uint32_t bucket[kBuckets / 2];  // 16-bit bucket counters, cursors and ends, two per word
+    uint64_t S[SCAP];             // kept candidates as composites, grouped by bucket; while
+                                  // choosing P, its first 2 KiB hold two sample-digit histograms
+    struct {
+        uint32_t bits[CCAP];      // candidates: raw bits
+        uint32_t pos[CCAP];       //   and positions
+    } cand;
+    static_assert(sizeof(uint64_t) * SCAP >= sizeof(uint32_t) * 2 * kRadix, "S holds the sample histograms");
 };
 
 // Pivot path of a row split over several workgroups: candidates live in the workspace,
@@ -578,27 +574,36 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 // P = the key prefix of the rr-th largest sample, MSB first, one 8-bit digit per pass;
 // a pass runs past the second only while the selected bin still holds more than
 // kRefineAbove samples, so after four passes P is that sample's key itself.  Pass p
-// counts into hist4 + 256 p (zeroed beforehand, a barrier behind), so no pass waits for
-// the previous one to be cleared; every wave then selects the digit on its own.
-// merge(pass, hist) turns this workgroup's histogram into the one the select reads
-// (nothing to do for a single workgroup, a device-wide sum over the row's tiles
-// otherwise).  Every wave, and every workgroup of a row, takes the same decisions.
-template <int NT, class Merge>
-__device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist4,
+// counts into hist + 256 (p % NH), NH regions zeroed beforehand with a barrier behind
+// (with NH < 4 a region is zeroed again, behind one more barrier, before its reuse); no
+// pass waits for the previous one's histogram to be cleared, and every wave then
+// selects the digit on its own.  merge(pass, h) turns this workgroup's histogram into
+// the one the select reads (nothing to do for a single workgroup, a device-wide sum
+// over the row's tiles otherwise).  Every wave, and every workgroup of a row, takes the
+// same decisions.
+template <int NT, int NH, class Merge>
+__device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist,
                                                  Merge&& merge) {
+    const int tid = threadIdx.x;
     uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         if (pass >= 2 && cnt <= kRefineAbove) break;  // uniform: bin resolved
-        uint32_t* hist = hist4 + pass * kRadix;
+        uint32_t* h = hist + (pass % NH) * kRadix;
+        if (pass >= NH) {  // every wave has selected from this region's previous pass
+            if (tid < kRadix) h[tid] = 0;
+            __syncthreads();
+        }
+        // (lanes sharing a bin merge into one atomic: scores concentrate on few digits,
+        // and same-address LDS atomics serialise)
 #pragma unroll
         for (int i = 0; i < kSamplesPerLane; ++i)
-            if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(hist, (sk[i] >> shift) & 0xFFu);
+            if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(h, (sk[i] >> shift) & 0xFFu);
         __syncthreads();
-        merge(pass, hist);
+        merge(pass, h);
         uint32_t above;
-        const uint32_t d = wave_select_digit(hist, r_rem, &above, &cnt);
+        const uint32_t d = wave_select_digit(h, r_rem, &above, &cnt);
         prefix = (prefix << 8) | d;
         r_rem -= above;
         P = prefix << shift;
@@ -638,46 +643,59 @@ struct AboveP {
     __device__ __forceinline__ bool eq(uint32_t x) const { return POS ? x == (uint32_t)pr : key_of(x) == P; }
 };
 
+// Bucket of a key: linear in the key over [L, U] (keys below L share bucket 0, keys
+// above U the top bucket); monotone, so bucket order never contradicts key order.
+struct BucketMap {
+    uint32_t L;
+    int sh;
+    __device__ BucketMap(uint32_t lo, uint32_t hi) : L(lo), sh(max(0, (32 - __clz(hi - lo)) - kBucketBits)) {}
+    __device__ __forceinline__ uint32_t operator()(uint32_t kx) const {
+        return min((max(kx, L) - L) >> sh, (uint32_t)(kBuckets - 1));
+    }
+};
+// Count one key into the 16-bit bucket counters (bucket b lives in word b / 2, bits
+// 16 * (b % 2) and up).
+__device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
+    lds_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4));
+}
+
 // Order the candidates: the m largest of the c_gt candidates (all of them when
 // c_gt <= m) go to slots [0, min(m, c_gt)) in canonical order through
 // emit(slot, position, bits).  Thread t owns candidates j = t + i * NT, i < CPT;
 // src(i, j) gives candidate j as (raw bits, position) (CPT * NT >= c_gt).
-// Buckets are linear in the key over [L, U] (keys below L share bucket 0, keys above U
-// the top bucket), counted with 16-bit LDS counters, two per word.  The bucket holding
-// the m-th largest is the threshold; kept candidates (buckets at or above it) go to S
-// grouped by bucket as composites (key << 32 | ~position), which are unique and whose
-// descending order is the canonical order; a kept candidate's slot is its bucket's start
-// plus the number of larger composites in its bucket.
+// The bucket (BucketMap) holding the m-th largest is the threshold; kept candidates
+// (buckets at or above it) go to S grouped by bucket as composites
+// (key << 32 | ~position), which are unique and whose descending order is the canonical
+// order; a kept candidate's slot is its bucket's start plus the number of larger
+// composites in its bucket.
+// COUNTED: the caller has already counted every candidate into the bucket array (a
+// barrier behind); otherwise the bucket array is zero (a barrier behind) and counted here.
+// ctl[kCtlBt..kCtlMaxBucket] are zero on entry.
 // LIMITED: returns false, having emitted nothing, when more than SCAP candidates are
-// kept, and sets ctl[kCtlMaxBucket] (some slots then stay unwritten: the caller must check
-// it after a barrier) when a kept bucket holds more than kBucketLimit.  Otherwise
-// c_gt <= SCAP (a power of two) is the caller's, and when some bucket holds more than
-// kBucketLimit the kept composites are ordered by a bitonic sort of S instead (the
-// comparison count of ranking grows with the square of a bucket's length).  On entry the
-// bucket array and ctl[kCtlBt..kCtlMaxBucket] are zero, a barrier behind.
-template <int NT, int SCAP, int CPT, bool LIMITED, class Src, class Emit>
+// kept or a bucket holds more than kBucketLimit.  Otherwise c_gt <= SCAP (a power of
+// two) is the caller's, and when a bucket holds more than kBucketLimit the kept
+// composites are ordered by a bitonic sort of S instead (ranking compares each element
+// with its whole bucket).
+template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Emit>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
-                                            uint32_t c_gt, uint32_t m, bool ties, uint32_t L, uint32_t U, Emit&& emit) {
+                                            uint32_t c_gt, uint32_t m, bool ties, const BucketMap& bucket_of,
+                                            Emit&& emit) {
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     const int tid = opaque_tid();
     const int lane = tid & 63;
-    const int sh = max(0, (32 - __clz(U - L)) - kBucketBits);
-    auto bucket_of = [&](uint32_t kx) -> uint32_t { return min((max(kx, L) - L) >> sh, (uint32_t)(kBuckets - 1)); };
-    // bucket b lives in word b / 2, bits 16 * (b % 2) and up
     auto half_of = [](uint32_t word, uint32_t b) -> uint32_t { return (word >> ((b & 1u) << 4)) & 0xFFFFu; };
     const uint32_t mlim = min(m, c_gt);  // slots the candidates fill
 
     // ---- counts
+    if (!COUNTED) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const uint32_t j = (uint32_t)(tid + i * NT);
-        if (j < c_gt) {
-            const uint32_t bk = bucket_of(key_of(src(i, j).x));
-            lds_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4));
+        for (int i = 0; i < CPT; ++i) {
+            const uint32_t j = (uint32_t)(tid + i * NT);
+            if (j < c_gt) bucket_count(bucket, bucket_of(key_of(src(i, j).x)));
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- suffix scan: bucket starts.  Thread t owns buckets [kBuckets - (t + 1) * BPT,
     // kBuckets - t * BPT), i.e. counter words W - (t + 1) * WPT .. W - t * WPT - 1, scanned
@@ -692,7 +710,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         packed += cw[i];
     }
     const uint32_t tsum = (packed >> 16) + (packed & 0xFFFFu);
-    if (!LIMITED) {  // longest bucket (kept or not: a safe overestimate)
+    {  // longest bucket (kept or not: a safe overestimate)
         uint32_t mx = 0;
 #pragma unroll
         for (int i = 0; i < WPT; ++i) mx = max(mx, max(cw[i] >> 16, cw[i] & 0xFFFFu));
@@ -728,7 +746,8 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     __syncthreads();
     const uint32_t bt = ties ? 0u : ctl[kCtlBt];
     const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
-    if (LIMITED && kept > (uint32_t)SCAP) return false;  // uniform
+    const bool too_long = ctl[kCtlMaxBucket] > (uint32_t)kBucketLimit;
+    if (LIMITED && (kept > (uint32_t)SCAP || too_long)) return false;  // uniform
 
     // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write)
     constexpr int SUNR = 2;
@@ -760,7 +779,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     }
     __syncthreads();
 
-    if (!LIMITED && ctl[kCtlMaxBucket] > (uint32_t)kBucketLimit) {  // uniform
+    if (!LIMITED && too_long) {  // uniform
         static_assert(LIMITED || (SCAP & (SCAP - 1)) == 0, "the sort pads S to a power of two");
         bitonic_desc_u64<NT>(S, (int)kept);
         for (uint32_t q = tid; q < mlim; q += NT) emit(q, ~(uint32_t)S[q], bits_of((uint32_t)(S[q] >> 32)));
@@ -789,10 +808,6 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
             rank[i] = 0;
         }
         lmax = wave_max(lmax);
-        if (LIMITED && lmax > (uint32_t)kBucketLimit) {  // too long to rank by comparisons
-            if (lane == 0) ctl[kCtlMaxBucket] = 1u;
-            lmax = 0;
-        }
         for (uint32_t f = 0; f < lmax; ++f) {
 #pragma unroll
             for (int i = 0; i < RUNR; ++i) {
@@ -833,7 +848,9 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
 
     // ------------------------------------------------ clear LDS state
     for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
-    for (int i = tid; i < 4 * kRadix; i += NT) s.bucket[i] = 0;  // the sample-digit histograms
+    uint32_t* const shist = reinterpret_cast<uint32_t*>(s.S);  // sample histograms (S is free until the scatter)
+    for (int i = tid; i < 2 * kRadix; i += NT) shist[i] = 0;
+    for (int i = tid; i < kBuckets / 8; i += NT) reinterpret_cast<uint4*>(s.bucket)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot
@@ -859,7 +876,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     {
         // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
         const uint32_t rr = fast_mode == 2 ? 1u : pivot_rank(nsamp, m, nt);
-        if (m < nt && rr < (uint32_t)nsamp) P = pivot_passes<NT>(sk, rr, s.bucket, [](int, uint32_t*) {});
+        if (m < nt && rr < (uint32_t)nsamp) P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {});
     }
     {
         uint32_t lo = 0xFFFFFFFFu;
@@ -898,10 +915,11 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     const bool ties = c_gt < (uint32_t)m;          // uniform: keys == P fill the tail
     uint32_t L, U;
     bucket_range(P, s.ctl[kCtlLo], s.ctl[kCtlSmaxAll], s.ctl[kCtlSmaxFin], &L, &U);
-    for (int i = tid; i < kBuckets / 2; i += NT) s.bucket[i] = 0;
+    const BucketMap bucket_of(L, U);
 
     // ------------------------------------------------ write pass: (bits, position) of the
     // candidates to LDS; keys == P into the position bitmap when the tail needs them.
+    const uint32_t o_first = o;  // this wave's candidates: [o_first, o) after the pass
     uint32_t neq = 0;
     auto write_pass = [&](auto pos_tag, auto eq_tag) {
         constexpr bool POS = decltype(pos_tag)::value;
@@ -912,8 +930,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
             const uint64_t mk = __ballot(gx) & __ballot(ok);
             if (gx && ok) {
                 const uint32_t q = lanes_below_plus(mk, o);
-                s.u.cand.bits[q] = x;
-                s.u.cand.pos[q] = (uint32_t)(t4 + (v * NT * 4 + c));
+                s.cand.bits[q] = x;
+                s.cand.pos[q] = (uint32_t)(t4 + (v * NT * 4 + c));
             }
             o += (uint32_t)__popcll(mk);
             if (EQ) {
@@ -941,16 +959,21 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         neq = wave_incl_scan(neq);
         if (lane == 63) lds_add(&s.ctl[kCtlEq], neq);
     }
+    // Each wave counts its own candidates into the buckets (its writes are complete once
+    // its LDS counter drains), so the count needs no barrier of its own.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (uint32_t j = o_first + (uint32_t)lane; j < o; j += 64) bucket_count(s.bucket, bucket_of(key_of(s.cand.bits[j])));
     __syncthreads();
     if (ties && c_gt + s.ctl[kCtlEq] < (uint32_t)m) return false;  // uniform: pivot missed
 
-    // ------------------------------------------------ order the candidates
-    if (!bucket_rank<NT, FS::SCAP, (FS::CCAP + NT - 1) / NT, true>(
-            s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return make_uint2(s.u.cand.bits[j], s.u.cand.pos[j]); },
-            c_gt, (uint32_t)m, ties, L, U,
+    // ------------------------------------------------ order the candidates, straight to
+    // the output row (S is in bucket order, so a wave's slots are nearly contiguous)
+    if (!bucket_rank<NT, FS::SCAP, (FS::CCAP + NT - 1) / NT, true, true>(
+            s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return make_uint2(s.cand.bits[j], s.cand.pos[j]); },
+            c_gt, (uint32_t)m, ties, bucket_of,
             [&](uint32_t slot, uint32_t pos, uint32_t bits) {
-                s.u.out.idx[slot] = pos;
-                s.u.out.val[slot] = bits;
+                r.oidx[slot] = (int32_t)pos;
+                if (r.oval) r.oval[slot] = bits;
             }))
         return false;
 
@@ -975,21 +998,13 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
                 while (word && rr < need) {
                     const int bit = __ffs(word) - 1;
                     word &= word - 1;
-                    s.u.out.idx[c_gt + rr] = (uint32_t)(w * 32 + bit);
-                    s.u.out.val[c_gt + rr] = vP;
+                    r.oidx[c_gt + rr] = w * 32 + bit;
+                    if (r.oval) r.oval[c_gt + rr] = vP;
                     ++rr;
                 }
                 rr += (uint32_t)__popc(word);
             }
         }
-    }
-    __syncthreads();
-    if (s.ctl[kCtlMaxBucket]) return false;  // uniform: a bucket too long to rank
-
-    // ------------------------------------------------ store the row
-    for (int q = tid; q < m; q += NT) {
-        r.oidx[q] = (int32_t)s.u.out.idx[q];
-        if (r.oval) r.oval[q] = s.u.out.val[q];
     }
     write_padding<NT>(r.oidx, r.oval, m, r.k);
     return true;
@@ -1052,7 +1067,7 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
         if (rr < (uint32_t)nsamp) {
             uint32_t* gsamp = rw + kRowSampHist;
-            P = pivot_passes<NT>(sk, rr, s.bucket, [&](int pass, uint32_t* h) {
+            P = pivot_passes<NT, 4>(sk, rr, s.bucket, [&](int pass, uint32_t* h) {
                 if (tid < kRadix) {
                     const uint32_t c = h[tid];
                     if (c) atomicAdd(&gsamp[pass * kRadix + tid], c);
@@ -1196,8 +1211,9 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
                  __hip_atomic_load(&rw[kRowUAll], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                  __hip_atomic_load(&rw[kRowUFin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), &L, &U);
     const uint2* gc = p.ws_cand + (int64_t)b * CAP;
-    bucket_rank<NT, MS::SCAP, (MS::SCAP + NT - 1) / NT, false>(
-        s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return gc[j]; }, c_gt, (uint32_t)m, ties, L, U,
+    bucket_rank<NT, MS::SCAP, (MS::SCAP + NT - 1) / NT, false, false>(
+        s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return gc[j]; }, c_gt, (uint32_t)m, ties,
+        BucketMap(L, U),
         [&](uint32_t slot, uint32_t pos, uint32_t bits) {
             r.oidx[slot] = (int32_t)pos;
             if (r.oval) r.oval[slot] = bits;
