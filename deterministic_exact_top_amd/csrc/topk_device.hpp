@@ -46,6 +46,7 @@ constexpr int kStageCap = 4096;                 // exact path: LDS threshold-bin
 constexpr int kBuckets = 4096;                  // fast path: buckets over the candidate key range
 constexpr int kBucketBits = 12;
 constexpr int kBucketLimit = 128;               // fast path: largest bucket ranked by comparisons
+constexpr int kBucketLimitRow = 512;            // the same, ordering a split row's candidates
 constexpr int kKeptSlack = 96;                  // fast path: kept candidates past KMAX that fit S
 static_assert(kBuckets / 2 >= 4 * 256, "the packed bucket array doubles as the sample histograms");
 constexpr int kSamplesPerLane = 4;           // fast path: pivot samples per lane
@@ -228,7 +229,8 @@ __device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const uint32_
         for (int v = 0; v < G4; ++v) {
             if (sample_group<NT, EPT>(v) != (pass == 0)) continue;
             if (aligned) {
-                const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (v * NT + tid) * 16, 0, 0);
+                // (the per-group offset rides in the scalar offset: one address VGPR for all)
+                const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, tid * 16, v * NT * 16, 0);
                 u[4 * v + 0] = q[0];
                 u[4 * v + 1] = q[1];
                 u[4 * v + 2] = q[2];
@@ -236,7 +238,7 @@ __device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const uint32_
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, ((v * NT + tid) * 4 + c) * 4, 0, 0);
+                    u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 16 + c * 4, v * NT * 16, 0);
             }
         }
     }
@@ -330,6 +332,26 @@ union SmemAll {
 };
 
 // ----------------------------------------------------------------------------- block helpers
+
+// Zero N words of LDS with the whole workgroup (trip count fixed at compile time).
+template <int NT, int N>
+__device__ __forceinline__ void block_zero(uint32_t* p) {
+    const int tid = (int)threadIdx.x;
+    if constexpr (N % 4 == 0 && N / 4 >= NT) {
+#pragma unroll
+        for (int i = 0; i < (N / 4 + NT - 1) / NT; ++i) {
+            const int q = tid + i * NT;
+            if ((N / 4) % NT == 0 || q < N / 4) reinterpret_cast<uint4*>(p)[q] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < (N + NT - 1) / NT; ++i) {
+            const int q = tid + i * NT;
+            if (N % NT == 0 || q < N) p[q] = 0u;
+        }
+    }
+}
+
 
 // Exclusive prefix sum over the workgroup in thread order; *total gets the sum.  One
 // barrier: `wsum` must not be written again before the caller's next barrier.
@@ -583,11 +605,12 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 // same decisions.
 template <int NT, int NH, class Merge>
 __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist,
-                                                 Merge&& merge) {
+                                                 Merge&& merge, int* passes = nullptr) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
+    int pass = 0;
 #pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
+    for (; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         if (pass >= 2 && cnt <= kRefineAbove) break;  // uniform: bin resolved
         uint32_t* h = hist + (pass % NH) * kRadix;
@@ -608,6 +631,7 @@ __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPe
         r_rem -= above;
         P = prefix << shift;
     }
+    if (passes) *passes = pass;
     return P;
 }
 
@@ -673,7 +697,7 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // ctl[kCtlBt..kCtlMaxBucket] are zero on entry.
 // LIMITED: returns false, having emitted nothing, when more than SCAP candidates are
 // kept or a bucket holds more than kBucketLimit.  Otherwise c_gt <= SCAP (a power of
-// two) is the caller's, and when a bucket holds more than kBucketLimit the kept
+// two) is the caller's, and when a bucket holds more than kBucketLimitRow the kept
 // composites are ordered by a bitonic sort of S instead (ranking compares each element
 // with its whole bucket).
 template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Emit>
@@ -746,7 +770,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     __syncthreads();
     const uint32_t bt = ties ? 0u : ctl[kCtlBt];
     const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
-    const bool too_long = ctl[kCtlMaxBucket] > (uint32_t)kBucketLimit;
+    const bool too_long = ctl[kCtlMaxBucket] > (uint32_t)(LIMITED ? kBucketLimit : kBucketLimitRow);
     if (LIMITED && (kept > (uint32_t)SCAP || too_long)) return false;  // uniform
 
     // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write)
@@ -847,10 +871,10 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     const int32_t m = r.m;
 
     // ------------------------------------------------ clear LDS state
-    for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
+    block_zero<NT, BW>(s.bitmap);
     uint32_t* const shist = reinterpret_cast<uint32_t*>(s.S);  // sample histograms (S is free until the scatter)
-    for (int i = tid; i < 2 * kRadix; i += NT) shist[i] = 0;
-    for (int i = tid; i < kBuckets / 8; i += NT) reinterpret_cast<uint4*>(s.bucket)[i] = make_uint4(0u, 0u, 0u, 0u);
+    block_zero<NT, 2 * kRadix>(shist);
+    block_zero<NT, kBuckets / 2>(s.bucket);
     if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot
@@ -858,27 +882,25 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     take_samples<NT, EPT>(u, nt, sk);
     const int nsamp = tile_samples<NT, EPT>(nt);
     {
-        uint32_t sa = 0, sf = 0;
+        uint32_t sf = 0;  // largest sample below key(+inf)
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) {
-            sa = max(sa, sk[i]);
-            sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
-        }
-        sa = wave_max(sa);
+        for (int i = 0; i < kSamplesPerLane; ++i) sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
         sf = wave_max(sf);
         __syncthreads();
-        if (lane == 0) {
-            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxAll], sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
+        if (lane == 0) __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     uint32_t P = 0;
+    int passes = 0;
     {
         // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
         const uint32_t rr = fast_mode == 2 ? 1u : pivot_rank(nsamp, m, nt);
-        if (m < nt && rr < (uint32_t)nsamp) P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {});
+        if (m < nt && rr < (uint32_t)nsamp) P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {}, &passes);
     }
-    {
+    // The least sample above P starts the bucket range when P may sit far below the kept
+    // keys: P = 0 (no pivot) or P exactly a sample's key (a plateau of equal scores, four
+    // passes); otherwise P, the low end of a bin holding samples, is as good.
+    const bool need_lo = P == 0 || passes == 4;  // uniform
+    if (need_lo) {
         uint32_t lo = 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < kSamplesPerLane; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
@@ -913,8 +935,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     o = __builtin_amdgcn_readfirstlane(o);  // wave-uniform: keep the running slot scalar
     if (c_gt > (uint32_t)FS::CCAP) return false;  // uniform
     const bool ties = c_gt < (uint32_t)m;          // uniform: keys == P fill the tail
-    uint32_t L, U;
-    bucket_range(P, s.ctl[kCtlLo], s.ctl[kCtlSmaxAll], s.ctl[kCtlSmaxFin], &L, &U);
+    const uint32_t U = max(P, s.ctl[kCtlSmaxFin]);
+    const uint32_t L = need_lo ? min(s.ctl[kCtlLo], U) : P;
     const BucketMap bucket_of(L, U);
 
     // ------------------------------------------------ write pass: (bits, position) of the
@@ -1039,8 +1061,8 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
     uint32_t* err = p.ws_zero;
 
     // ------------------------------------------------ clear LDS state
-    for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
-    for (int i = tid; i < 4 * kRadix; i += NT) s.bucket[i] = 0;  // the sample-digit histograms
+    block_zero<NT, BW>(s.bitmap);
+    block_zero<NT, 4 * kRadix>(s.bucket);  // the sample-digit histograms
     if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot (row-wide)
@@ -1202,7 +1224,7 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
         const uint32_t old = __hip_atomic_fetch_add(&rw[kRowFastArrive], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         s.ctl[kCtlLast] = old == (uint32_t)ntiles - 1u ? 1u : 0u;
     }
-    for (int i = tid; i < kBuckets / 2; i += NT) s.bucket[i] = 0;
+    block_zero<NT, kBuckets / 2>(s.bucket);
     if (tid >= kCtlBt && tid <= kCtlMaxBucket) s.ctl[tid] = 0;
     __syncthreads();
     if (s.ctl[kCtlLast] == 0) return true;
