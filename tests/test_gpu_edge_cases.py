@@ -1,0 +1,165 @@
+"""GPU parity on edge cases and a seeded randomized sweep.
+
+Every case is checked bit for bit against the CPU oracle (indices and value bits) and
+against the invariants of the canonical order.  Cases: extreme k (1, 4096), rows made
+entirely of one value (finite, +/-0.0, +inf, NaN payloads), overlapping windows, rows
+whose length is a whole number of tiles on the split-row path, a tie block straddling
+tile boundaries, empty and one-row batches, and ~40 random (shape, k, value family)
+draws from a fixed seed.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_same, debug_overrides, log, run_gpu, run_oracle
+from topk_checks import check_batch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    import deterministic_exact_top_amd as detk
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    detk.load_library()
+    return torch.device("cuda:0")
+
+
+def _dense(rows, k, name, L=None):
+    rows = [np.asarray(r, dtype=np.float32) for r in rows]
+    L = L or max(1, max(r.size for r in rows))
+    buf = np.full(len(rows) * L, W.QNAN, np.uint32).view(np.float32)
+    for b, r in enumerate(rows):
+        buf[b * L:b * L + r.size] = r
+    starts = (np.arange(len(rows)) * L).astype(np.int32)
+    lens = np.array([r.size for r in rows], np.int32)
+    return W.Workload(name, buf, starts, lens, L, k)
+
+
+def _check(dev, wl, what, **over):
+    log("edge case %s: B=%d max_len=%d k=%d %s" % (what, wl.B, wl.max_len, wl.k, over))
+    with debug_overrides(**over):
+        gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, what)
+    check_batch(wl.scores.view(np.uint32), wl.row_starts, wl.lengths, wl.max_len, wl.k, gi, gv)
+
+
+SHAPES = {"auto": {}, "single": {"path": 1}, "multi": {"path": 2, "multi_tile": 4096}}
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+@pytest.mark.parametrize("k", [1, 4096])
+def test_extreme_k(dev, shape, k):
+    rng = np.random.default_rng(11 + k)
+    rows = [W.relu_sum_mixture(rng, n, 0.5) for n in (1, 5000, 9000, 16000)]
+    _check(dev, _dense(rows, k, "extreme_k"), "k=%d/%s" % (k, shape), **SHAPES[shape])
+
+
+CONSTANT = {
+    "finite": np.float32(1.5),
+    "pos_zero": np.float32(0.0),
+    "neg_zero": np.float32(-0.0),
+    "pos_inf": np.float32(np.inf),
+    "neg_inf": np.float32(-np.inf),
+    "qnan": np.uint32(0x7FC00000).view(np.float32),
+    "neg_nan_payload": np.uint32(0xFFC00123).view(np.float32),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+@pytest.mark.parametrize("value", sorted(CONSTANT))
+def test_constant_rows(dev, shape, value):
+    v = CONSTANT[value]
+    rows = [np.full(n, v, np.float32) for n in (3000, 12000, 20000)]
+    _check(dev, _dense(rows, 2048, "constant"), "constant %s/%s" % (value, shape), **SHAPES[shape])
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+def test_two_values_half_and_half(dev, shape):
+    rng = np.random.default_rng(5)
+    rows = []
+    for n in (4097, 10000, 18000):
+        r = np.where(rng.random(n) < 0.5, np.float32(2.0), np.float32(1.0)).astype(np.float32)
+        rows.append(r)
+    _check(dev, _dense(rows, 2048, "two_values"), "two values/%s" % shape, **SHAPES[shape])
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+def test_overlapping_windows(dev, shape):
+    rng = np.random.default_rng(9)
+    buf = W.relu_sum_mixture(rng, 40000, 0.6)
+    starts = np.array([0, 100, 5000, 5000, 20000, 39990], np.int32)
+    lens = np.array([30000, 10000, 2000, 30000, 20000, 10], np.int32)
+    wl = W.Workload("overlap", buf, starts, lens, 30000, 1000)
+    _check(dev, wl, "overlapping windows/%s" % shape, **SHAPES[shape])
+
+
+@pytest.mark.parametrize("n", [32768, 65536, 98304])
+def test_split_rows_whole_tiles(dev, n):
+    rng = np.random.default_rng(n)
+    rows = [W.relu_sum_mixture(rng, n, 0.7), -np.abs(rng.standard_normal(n)).astype(np.float32)]
+    _check(dev, _dense(rows, 2048, "whole_tiles"), "whole tiles n=%d" % n)
+
+
+@pytest.mark.parametrize("tile", [4096, 32768])
+def test_tie_block_across_tiles(dev, tile):
+    """The boundary tie set (equal keys at the k-th place) spread over several tiles:
+    the smallest indices must come first, tile order being index order."""
+    rng = np.random.default_rng(3)
+    n = 100000
+    u = rng.random(n)
+    r = np.full(n, np.float32(7.0), np.float32)            # the tie value: ~60% of the row
+    hi = u < 0.01                                           # ~1000 keys above it (< k)
+    r[hi] = np.abs(rng.standard_normal(int(hi.sum()))).astype(np.float32) + np.float32(10.0)
+    r[u > 0.6] = np.float32(3.0)                            # keys below it
+    rows = [r, r[::-1].copy()]
+    _check(dev, _dense(rows, 4096, "tie_block"), "tie block across tiles %d" % tile, path=2, multi_tile=tile)
+
+
+def test_one_row_and_tiny_rows(dev):
+    rng = np.random.default_rng(4)
+    _check(dev, _dense([W.relu_sum_mixture(rng, 7000, 0.3)], 300, "one_row"), "one row")
+    _check(dev, _dense([rng.standard_normal(n).astype(np.float32) for n in (1, 2, 3)], 2, "tiny"), "tiny rows")
+
+
+def test_empty_batch(dev):
+    import torch
+    import deterministic_exact_top_amd as detk
+    s = torch.zeros(0, 100, device=dev)
+    idx, val = detk.topk_ragged(s, None, None, 10)
+    assert idx.shape == (0, 10) and val.shape == (0, 10)
+
+
+FAMILIES = ["mixture", "normal", "quantized", "narrow", "mixed_signs"]
+
+
+def _family(rng, fam, n):
+    if fam == "mixture":
+        return W.relu_sum_mixture(rng, n, float(rng.uniform(0.0, 0.95)))
+    if fam == "normal":
+        return rng.standard_normal(n).astype(np.float32)
+    if fam == "quantized":
+        return (rng.integers(0, 16, n) / 4.0).astype(np.float32)
+    if fam == "narrow":
+        return W.narrow_bits(rng, n)
+    r = rng.standard_normal(n).astype(np.float32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf], np.float32)
+    pos = rng.random(n) < 0.05
+    r[pos] = special[rng.integers(0, 4, int(pos.sum()))]
+    return r
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_sweep(dev, case):
+    rng = np.random.default_rng(1000 + case)
+    B = int(rng.integers(1, 24))
+    max_len = int(rng.choice([100, 3000, 9000, 20000, 40000, 90000]))
+    k = int(rng.choice([1, 7, 64, 500, 2048, 3000, 4096]))
+    fam = FAMILIES[case % len(FAMILIES)]
+    rows = [_family(rng, fam, int(rng.integers(0, max_len + 1))) for _ in range(B)]
+    wl = _dense(rows, k, "sweep%d" % case, L=max_len)
+    _check(dev, wl, "sweep %d (%s)" % (case, fam))
