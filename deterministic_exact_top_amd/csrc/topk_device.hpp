@@ -48,6 +48,11 @@ constexpr int kBucketBits = 12;
 constexpr int kBucketLimit = 128;               // fast path: largest bucket ranked by comparisons
 constexpr int kBucketLimitRow = 512;            // the same, ordering a split row's candidates
 constexpr int kKeptSlack = 96;                  // fast path: kept candidates past KMAX that fit S
+constexpr int kRankUnroll = 4;                  // composites compared per turn of the ranking loop
+// Zero composites past the kept ones: a ranking loop running past a bucket's end reads
+// lower buckets' composites or these, all smaller than its own, so it needs no bound.
+template <bool LIMITED>
+constexpr int rank_pad() { return (LIMITED ? kBucketLimit : kBucketLimitRow) + kRankUnroll; }
 static_assert(kBuckets / 2 >= 4 * 256, "the packed bucket array doubles as the sample histograms");
 constexpr int kSamplesPerLane = 4;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
@@ -221,21 +226,30 @@ __device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const uint32_
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src), (short)0, nt * 4, kBufferWord3);
     const int tid = opaque_tid();
     constexpr int G4 = EPT / 4;
-    const bool aligned = (((uintptr_t)src) & 15u) == 0;
+    // (one branch around all the loads: with a branch per load the compiler's wait counts
+    // turn conservative, and the samples would wait for the whole tile)
+    if ((((uintptr_t)src) & 15u) == 0) {
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        if ((PART == 0 && pass == 1) || (PART == 1 && pass == 0)) continue;
+        for (int pass = 0; pass < 2; ++pass) {
+            if ((PART == 0 && pass == 1) || (PART == 1 && pass == 0)) continue;
 #pragma unroll
-        for (int v = 0; v < G4; ++v) {
-            if (sample_group<NT, EPT>(v) != (pass == 0)) continue;
-            if (aligned) {
+            for (int v = 0; v < G4; ++v) {
+                if (sample_group<NT, EPT>(v) != (pass == 0)) continue;
                 // (the per-group offset rides in the scalar offset: one address VGPR for all)
                 const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, tid * 16, v * NT * 16, 0);
                 u[4 * v + 0] = q[0];
                 u[4 * v + 1] = q[1];
                 u[4 * v + 2] = q[2];
                 u[4 * v + 3] = q[3];
-            } else {
+            }
+        }
+    } else {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            if ((PART == 0 && pass == 1) || (PART == 1 && pass == 0)) continue;
+#pragma unroll
+            for (int v = 0; v < G4; ++v) {
+                if (sample_group<NT, EPT>(v) != (pass == 0)) continue;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 16 + c * 4, v * NT * 16, 0);
@@ -286,16 +300,21 @@ struct FastSmem {
     static constexpr int BWORDS = TILE / 32;
     static constexpr int CCAP = cand_cap_single<KMAX>();
     static constexpr int SCAP = KMAX + kKeptSlack;
-    uint32_t ctl[16];             // control words, kCtl* below
-    uint32_t wsum[32];
-    uint32_t bitmap[BWORDS];      // positions with key == P
-    uint32_t bucket[kBuckets / 2];  // 16-bit bucket counters, cursors and ends, two per word
-    uint64_t S[SCAP];             // kept candidates as composites, grouped by bucket; while
-                                  // choosing P, its first 2 KiB hold two sample-digit histograms
+    // (first, at LDS offset 0: the two arrays sit at multiples of 256 bytes, so one
+    // two-address LDS store writes a candidate with no offset arithmetic)
     struct {
         uint32_t bits[CCAP];      // candidates: raw bits
         uint32_t pos[CCAP];       //   and positions
     } cand;
+    uint64_t S[SCAP + rank_pad<true>()];  // kept candidates as composites, grouped by bucket,
+                                          // then zeros; while choosing P, its first 2 KiB
+                                          // hold two sample-digit histograms
+    uint32_t ctl[16];             // control words, kCtl* below
+    uint32_t wsum[32];
+    uint32_t bitmap[BWORDS];      // positions with key == P
+    uint32_t bucket[kBuckets / 2 + 2];  // 16-bit bucket counters, cursors and ends, two per
+                                        // word; then a zero (the end above the top bucket)
+    static_assert((CCAP * 4) % 256 == 0, "candidate arrays on 256-byte boundaries");
     static_assert(sizeof(uint64_t) * SCAP >= sizeof(uint32_t) * 2 * kRadix, "S holds the sample histograms");
 };
 
@@ -310,8 +329,8 @@ struct MultiFastSmem {
     uint32_t ctl[16];
     uint32_t wsum[32];
     uint32_t bitmap[BWORDS];
-    uint32_t bucket[kBuckets / 2];
-    uint64_t S[SCAP];
+    uint32_t bucket[kBuckets / 2 + 2];
+    uint64_t S[SCAP + rank_pad<false>()];
 };
 
 struct NoSmem {};
@@ -338,10 +357,14 @@ template <int NT, int N>
 __device__ __forceinline__ void block_zero(uint32_t* p) {
     const int tid = (int)threadIdx.x;
     if constexpr (N % 4 == 0 && N / 4 >= NT) {
+        // (a zero made here: a zero vector hoisted out of the row loop gets spilled, and its
+        // reload from scratch would wait for every outstanding tile load)
+        uint32_t z = 0;
+        asm volatile("" : "+v"(z));
 #pragma unroll
         for (int i = 0; i < (N / 4 + NT - 1) / NT; ++i) {
             const int q = tid + i * NT;
-            if ((N / 4) % NT == 0 || q < N / 4) reinterpret_cast<uint4*>(p)[q] = make_uint4(0u, 0u, 0u, 0u);
+            if ((N / 4) % NT == 0 || q < N / 4) reinterpret_cast<uint4*>(p)[q] = make_uint4(z, z, z, z);
         }
     } else {
 #pragma unroll
@@ -700,6 +723,8 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // two) is the caller's, and when a bucket holds more than kBucketLimitRow the kept
 // composites are ordered by a bitonic sort of S instead (ranking compares each element
 // with its whole bucket).
+// bucket has kBuckets / 2 + 1 words (the last one is cleared here) and S has
+// SCAP + rank_pad<LIMITED>() entries (those past the kept ones are cleared here).
 template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Emit>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             uint32_t c_gt, uint32_t m, bool ties, const BucketMap& bucket_of,
@@ -710,6 +735,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     const int lane = tid & 63;
     auto half_of = [](uint32_t word, uint32_t b) -> uint32_t { return (word >> ((b & 1u) << 4)) & 0xFFFFu; };
     const uint32_t mlim = min(m, c_gt);  // slots the candidates fill
+    if (tid == 0) bucket[kBuckets / 2] = 0;  // the end above the top bucket (read past a barrier)
 
     // ---- counts
     if (!COUNTED) {
@@ -780,27 +806,35 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         if ((uint32_t)(i0 * NT) >= c_gt) continue;  // uniform
         uint32_t pos[SUNR];
         uint64_t comp[SUNR];
+        uint32_t old[SUNR], bks[SUNR];
+        bool kp[SUNR];
 #pragma unroll
         for (int d = 0; d < SUNR; ++d) {
             const int i = i0 + d;
             const uint32_t j = (uint32_t)(tid + i * NT);
-            pos[d] = 0xFFFFFFFFu;
             comp[d] = 0;
+            bks[d] = 0;
+            kp[d] = false;
             if (i < CPT && j < c_gt) {
                 const uint2 cv = src(i, j);
                 const uint32_t kk = key_of(cv.x);
-                const uint32_t bk = bucket_of(kk);
+                bks[d] = bucket_of(kk);
                 comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv.y;
-                if (bk >= bt)
-                    pos[d] = half_of(__hip_atomic_fetch_add(&bucket[bk >> 1], 1u << ((bk & 1u) << 4), __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_WORKGROUP),
-                                     bk);
+                kp[d] = bks[d] >= bt;
             }
+            old[d] = 0;
+            if (kp[d])
+                old[d] = __hip_atomic_fetch_add(&bucket[bks[d] >> 1], 1u << ((bks[d] & 1u) << 4), __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        // (the claimed slots are read only once every claim of this turn is issued)
+#pragma unroll
+        for (int d = 0; d < SUNR; ++d) pos[d] = kp[d] ? half_of(old[d], bks[d]) : 0xFFFFFFFFu;
 #pragma unroll
         for (int d = 0; d < SUNR; ++d)
             if (pos[d] < (uint32_t)SCAP) S[pos[d]] = comp[d];
     }
+    for (int i = tid; i < rank_pad<LIMITED>(); i += NT) S[kept + i] = 0;  // kept <= SCAP here
     __syncthreads();
 
     if (!LIMITED && too_long) {  // uniform
@@ -810,14 +844,17 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         return true;
     }
 
-    // ---- rank inside buckets -> final slot.  Bucket b's counter now holds its end; its
-    // start is the end of bucket b + 1.  Each lane ranks RUNR elements at once; the
-    // comparison loop runs the wave's longest bucket, uniformly.
+    // ---- rank inside buckets -> final slot.  Bucket b's 16-bit counter now holds its end;
+    // its start is the end of bucket b + 1 (zero above the top bucket).  Each lane ranks
+    // RUNR elements at once: it counts the larger composites among the lmax entries from
+    // its bucket's start, lmax being the wave's longest bucket; entries past its bucket's
+    // end belong to lower buckets or the zero padding, so every lane compares them all.
+    const uint16_t* const b16 = reinterpret_cast<const uint16_t*>(bucket);
     constexpr int RUNR = 2;
     for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
         if (q0 + (uint32_t)(tid & ~63) >= kept) break;  // wave-uniform: nothing left for this wave
         uint64_t cc[RUNR];
-        uint32_t st[RUNR], len[RUNR], rank[RUNR];
+        uint32_t st[RUNR], rank[RUNR];
         uint32_t lmax = 0;
 #pragma unroll
         for (int i = 0; i < RUNR; ++i) {
@@ -825,18 +862,18 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
             const bool in = q < kept;
             cc[i] = in ? S[q] : 0ull;
             const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
-            const uint32_t en = in ? min(half_of(bucket[bk >> 1], bk), kept) : 0u;
-            st[i] = bk == (uint32_t)(kBuckets - 1) ? 0u : half_of(bucket[(bk + 1) >> 1], bk + 1);
-            len[i] = en > st[i] ? en - st[i] : 0u;
-            lmax = max(lmax, len[i]);
+            const uint32_t en = min((uint32_t)b16[bk], kept);
+            st[i] = in ? (uint32_t)b16[bk + 1] : 0u;
+            lmax = max(lmax, in && en > st[i] ? en - st[i] : 0u);
             rank[i] = 0;
         }
         lmax = wave_max(lmax);
-        for (uint32_t f = 0; f < lmax; ++f) {
+        for (uint32_t f = 0; f < lmax; f += kRankUnroll) {
 #pragma unroll
             for (int i = 0; i < RUNR; ++i) {
-                const uint64_t other = S[f < len[i] ? st[i] + f : 0u];
-                rank[i] += (f < len[i] && other > cc[i]) ? 1u : 0u;
+                const uint64_t* const o = S + st[i] + f;
+#pragma unroll
+                for (int u = 0; u < kRankUnroll; ++u) rank[i] += o[u] > cc[i] ? 1u : 0u;
             }
         }
 #pragma unroll
@@ -984,7 +1021,13 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     // Each wave counts its own candidates into the buckets (its writes are complete once
     // its LDS counter drains), so the count needs no barrier of its own.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (uint32_t j = o_first + (uint32_t)lane; j < o; j += 64) bucket_count(s.bucket, bucket_of(key_of(s.cand.bits[j])));
+    for (uint32_t j = o_first + (uint32_t)lane; j < o; j += 128) {  // two reads in flight
+        const uint32_t x0 = s.cand.bits[j];
+        const bool two = j + 64 < o;
+        const uint32_t x1 = two ? s.cand.bits[j + 64] : 0u;
+        bucket_count(s.bucket, bucket_of(key_of(x0)));
+        if (two) bucket_count(s.bucket, bucket_of(key_of(x1)));
+    }
     __syncthreads();
     if (ties && c_gt + s.ctl[kCtlEq] < (uint32_t)m) return false;  // uniform: pivot missed
 
