@@ -28,7 +28,7 @@ constexpr int kSingleMaxLen = 32768;
 template <int TILE> struct Shape;
 template <> struct Shape<4096> { static constexpr int NT = 256, EPT = 16, MINW = 2, MINW_MULTI = 2; };
 template <> struct Shape<8192> { static constexpr int NT = 512, EPT = 16, MINW = 4, MINW_MULTI = 4; };
-template <> struct Shape<16384> { static constexpr int NT = 512, EPT = 32, MINW = 6, MINW_MULTI = 4; };
+template <> struct Shape<16384> { static constexpr int NT = 512, EPT = 32, MINW = 8, MINW_MULTI = 4; };
 template <> struct Shape<32768> { static constexpr int NT = 1024, EPT = 32, MINW = 4, MINW_MULTI = 4; };
 
 template <int TILE, bool MULTI>

@@ -300,15 +300,19 @@ struct FastSmem {
     static constexpr int BWORDS = TILE / 32;
     static constexpr int CCAP = cand_cap_single<KMAX>();
     static constexpr int SCAP = KMAX + kKeptSlack;
-    // (first, at LDS offset 0: the two arrays sit at multiples of 256 bytes, so one
-    // two-address LDS store writes a candidate with no offset arithmetic)
-    struct {
-        uint32_t bits[CCAP];      // candidates: raw bits
-        uint32_t pos[CCAP];       //   and positions
-    } cand;
-    uint64_t S[SCAP + rank_pad<true>()];  // kept candidates as composites, grouped by bucket,
-                                          // then zeros; while choosing P, its first 2 KiB
-                                          // hold two sample-digit histograms
+    // (first, at LDS offset 0: the two candidate arrays sit at multiples of 256 bytes, so
+    // one two-address LDS store writes a candidate with no offset arithmetic)
+    union {
+        struct {
+            uint32_t bits[CCAP];  // candidates: raw bits
+            uint32_t pos[CCAP];   //   and positions
+        } cand;
+        uint64_t S[SCAP + rank_pad<true>()];  // kept candidates as composites, grouped by
+                                              // bucket, then zeros (written once every
+                                              // candidate has been read into registers);
+                                              // while choosing P, its first 2 KiB hold two
+                                              // sample-digit histograms
+    };
     uint32_t ctl[16];             // control words, kCtl* below
     uint32_t wsum[32];
     uint32_t bitmap[BWORDS];      // positions with key == P
@@ -337,15 +341,15 @@ struct NoSmem {};
 
 // Exact-path staging: smaller in one-workgroup-per-row kernels so that the LDS footprint
 // lets three rows share a CU.
-template <bool MULTI>
-constexpr int stage_entries() { return MULTI ? 3072 : 2560; }
+template <int NT, int EPT, bool MULTI>
+constexpr int stage_entries() { return MULTI ? 3072 : (NT == 512 && EPT == 32) ? 1248 : 2560; }
 
 // LDS of one workgroup: the exact path's, or the pivot path's of the kernel's kind (the
 // several-workgroups-per-row kernel takes its one-tile rows through the workspace
 // candidate list too, so its LDS never holds a whole candidate list).
 template <int NT, int EPT, int KMAX, bool MULTI>
 union SmemAll {
-    ExactSmem<NT, EPT, KMAX, stage_entries<MULTI>()> exact;
+    ExactSmem<NT, EPT, KMAX, stage_entries<NT, EPT, MULTI>()> exact;
     typename std::conditional<MULTI, NoSmem, FastSmem<NT, EPT, KMAX>>::type fast;
     typename std::conditional<MULTI, MultiFastSmem<NT, EPT, KMAX>, NoSmem>::type mfast;
 };
@@ -717,6 +721,8 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // composites in its bucket.
 // COUNTED: the caller has already counted every candidate into the bucket array (a
 // barrier behind); otherwise the bucket array is zero (a barrier behind) and counted here.
+// Every candidate is read into registers before the first barrier in here, so S may
+// overlay the memory src reads.
 // ctl[kCtlBt..kCtlMaxBucket] are zero on entry.
 // LIMITED: returns false, having emitted nothing, when more than SCAP candidates are
 // kept or a bucket holds more than kBucketLimit.  Otherwise c_gt <= SCAP (a power of
@@ -737,12 +743,20 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     const uint32_t mlim = min(m, c_gt);  // slots the candidates fill
     if (tid == 0) bucket[kBuckets / 2] = 0;  // the end above the top bucket (read past a barrier)
 
+    // ---- this thread's candidates, into registers
+    uint2 cv[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const uint32_t j = (uint32_t)(tid + i * NT);
+        cv[i] = j < c_gt ? src(i, j) : make_uint2(0u, 0u);
+    }
+
     // ---- counts
     if (!COUNTED) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const uint32_t j = (uint32_t)(tid + i * NT);
-            if (j < c_gt) bucket_count(bucket, bucket_of(key_of(src(i, j).x)));
+            if (j < c_gt) bucket_count(bucket, bucket_of(key_of(cv[i].x)));
         }
         __syncthreads();
     }
@@ -816,10 +830,9 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
             bks[d] = 0;
             kp[d] = false;
             if (i < CPT && j < c_gt) {
-                const uint2 cv = src(i, j);
-                const uint32_t kk = key_of(cv.x);
+                const uint32_t kk = key_of(cv[i].x);
                 bks[d] = bucket_of(kk);
-                comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv.y;
+                comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv[i].y;
                 kp[d] = bks[d] >= bt;
             }
             old[d] = 0;
@@ -1601,7 +1614,10 @@ __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, K
         } else {
             if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
         }
-        __syncthreads();  // fall back to the exact path on the same registers
+        __syncthreads();  // fall back to the exact path
+        // (a single-workgroup row reloads its tile, so the pivot path's later phases get
+        // the tile's registers; a split row's tiles keep theirs)
+        if constexpr (!MULTI) load_tile<NT, EPT>(u, p.scores + r.base + r.j0, r.nt);
     }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
@@ -1614,6 +1630,12 @@ template <int NT, int EPT, int KMAX, bool MULTI, int MINW>
 __global__ __launch_bounds__(NT, MINW) void topk_ragged_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto& s = *reinterpret_cast<SmemAll<NT, EPT, KMAX, MULTI>*>(smem_raw);
+    if constexpr (!MULTI) {
+        // One workgroup per row (grid = B): no item loop, so nothing row-invariant is
+        // hoisted into registers that would stay live across the row.
+        process_tile<NT, EPT, KMAX, MULTI>(p, s, (int)blockIdx.x, 0);
+        return;
+    }
     const int64_t items = MULTI ? (int64_t)p.B * p.tiles_per_row : (int64_t)p.B;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int b = MULTI ? (int)(it / p.tiles_per_row) : (int)it;
