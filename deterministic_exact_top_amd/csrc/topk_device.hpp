@@ -200,7 +200,7 @@ __device__ __forceinline__ uint32_t claim_slot(bool pred, uint32_t* counter) {
     if (m == 0) return 0;
     const int leader = __ffsll((unsigned long long)m) - 1;
     uint32_t base = 0;
-    if ((int)(threadIdx.x & 63) == leader)
+    if ((opaque_tid() & 63) == leader)
         base = __hip_atomic_fetch_add(counter, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_WORKGROUP);
     base = __builtin_amdgcn_readlane(base, leader);
@@ -359,7 +359,7 @@ union SmemAll {
 // Zero N words of LDS with the whole workgroup (trip count fixed at compile time).
 template <int NT, int N>
 __device__ __forceinline__ void block_zero(uint32_t* p) {
-    const int tid = (int)threadIdx.x;
+    const int tid = opaque_tid();
     if constexpr (N % 4 == 0 && N / 4 >= NT) {
         // (a zero made here: a zero vector hoisted out of the row loop gets spilled, and its
         // reload from scratch would wait for every outstanding tile load)
@@ -384,7 +384,7 @@ __device__ __forceinline__ void block_zero(uint32_t* p) {
 // barrier: `wsum` must not be written again before the caller's next barrier.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     const uint32_t incl = wave_incl_scan(x);
     if ((tid & 63) == 63) wsum[tid >> 6] = incl;
     __syncthreads();
@@ -404,7 +404,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wsum, 
 template <int NT>
 __device__ __forceinline__ void select_digit(const uint32_t* hist, uint32_t k_rem, uint32_t* wsum,
                                              uint32_t* sel) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     if (tid == 0) {  // safe result should the counts ever be inconsistent
         sel[0] = 0;
         sel[1] = 0;
@@ -438,7 +438,7 @@ __device__ __forceinline__ void select_digit(const uint32_t* hist, uint32_t k_re
 // the digit's count (all zero should the counts ever be inconsistent).
 __device__ __forceinline__ uint32_t wave_select_digit(const uint32_t* hist, uint32_t r, uint32_t* above,
                                                       uint32_t* count) {
-    const int lane = (int)(threadIdx.x & 63);
+    const int lane = (opaque_tid() & 63);
     const uint4 q = *reinterpret_cast<const uint4*>(hist + 252 - 4 * lane);
     const uint32_t c0 = q.w, c1 = q.z, c2 = q.y, c3 = q.x;  // bins 255 - 4l, 254 - 4l, 253 - 4l, 252 - 4l
     const uint32_t t3 = c0 + c1 + c2 + c3;
@@ -465,7 +465,7 @@ __device__ __forceinline__ uint32_t wave_select_digit(const uint32_t* hist, uint
 // two).  Padding entries get composite 0, which no real element has (~pos != 0).
 template <int NT>
 __device__ __forceinline__ void bitonic_desc(const PairList& A, int count) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     int P = 1;
     while (P < count) P <<= 1;
     for (int i = count + tid; i < P; i += NT) A.set_composite(i, 0);
@@ -490,7 +490,7 @@ __device__ __forceinline__ void bitonic_desc(const PairList& A, int count) {
 // The same on a plain array of composites.
 template <int NT>
 __device__ __forceinline__ void bitonic_desc_u64(uint64_t* A, int count) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     int P = 1;
     while (P < count) P <<= 1;
     for (int i = count + tid; i < P; i += NT) A[i] = 0;
@@ -515,7 +515,7 @@ __device__ __forceinline__ void bitonic_desc_u64(uint64_t* A, int count) {
 // Write the padding slots [m, k) of one output row.
 template <int NT>
 __device__ __forceinline__ void write_padding(int32_t* oidx, uint32_t* oval, int m, int k) {
-    for (int q = m + (int)threadIdx.x; q < k; q += NT) {
+    for (int q = m + opaque_tid(); q < k; q += NT) {
         oidx[q] = -1;
         if (oval) oval[q] = kNegInfBits;
     }
@@ -576,7 +576,7 @@ enum : int {
     kCtlLo = 2,         // least sample key above P (all ones when there is none)
     kCtlBt = 3,         // threshold bucket
     kCtlKept = 4,       // kept candidates
-    kCtlMaxBucket = 5,  // longest kept bucket
+    kCtlMaxBucket = 5,  // set when some bucket is longer than the ranking limit
     kCtlSel = 6,        // [6..8] sample digit select: digit, count above, bin count
     kCtlEq = 9,         // keys equal to P
     kCtlSmaxFin = 10,   // largest sample key below key(+inf)
@@ -629,11 +629,12 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 // selects the digit on its own.  merge(pass, h) turns this workgroup's histogram into
 // the one the select reads (nothing to do for a single workgroup, a device-wide sum
 // over the row's tiles otherwise).  Every wave, and every workgroup of a row, takes the
-// same decisions.
+// same decisions.  With sel (three LDS words), wave 0 alone selects each digit and
+// publishes it behind one more barrier, instead of every wave repeating the selection.
 template <int NT, int NH, class Merge>
 __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist,
-                                                 Merge&& merge, int* passes = nullptr) {
-    const int tid = threadIdx.x;
+                                                 Merge&& merge, int* passes = nullptr, uint32_t* sel = nullptr) {
+    const int tid = opaque_tid();
     uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
     int pass = 0;
 #pragma unroll 1
@@ -652,8 +653,23 @@ __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPe
             if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(h, (sk[i] >> shift) & 0xFFu);
         __syncthreads();
         merge(pass, h);
-        uint32_t above;
-        const uint32_t d = wave_select_digit(h, r_rem, &above, &cnt);
+        uint32_t above, d;
+        if (sel) {
+            if (tid < 64) {
+                d = wave_select_digit(h, r_rem, &above, &cnt);
+                if (tid == 0) {
+                    sel[0] = d;
+                    sel[1] = above;
+                    sel[2] = cnt;
+                }
+            }
+            __syncthreads();
+            d = __builtin_amdgcn_readfirstlane(sel[0]);  // (uniform: kept scalar)
+            above = __builtin_amdgcn_readfirstlane(sel[1]);
+            cnt = __builtin_amdgcn_readfirstlane(sel[2]);
+        } else {
+            d = wave_select_digit(h, r_rem, &above, &cnt);
+        }
         prefix = (prefix << 8) | d;
         r_rem -= above;
         P = prefix << shift;
@@ -723,7 +739,10 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // barrier behind); otherwise the bucket array is zero (a barrier behind) and counted here.
 // Every candidate is read into registers before the first barrier in here, so S may
 // overlay the memory src reads.
-// ctl[kCtlBt..kCtlMaxBucket] are zero on entry.
+// ctl[kCtlBt..kCtlMaxBucket] are zero on entry (kCtlMaxBucket becomes a flag: some bucket
+// is longer than the limit).
+// scattered() runs once the kept composites are in S, past the last point of returning
+// false.
 // LIMITED: returns false, having emitted nothing, when more than SCAP candidates are
 // kept or a bucket holds more than kBucketLimit.  Otherwise c_gt <= SCAP (a power of
 // two) is the caller's, and when a bucket holds more than kBucketLimitRow the kept
@@ -731,10 +750,10 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // with its whole bucket).
 // bucket has kBuckets / 2 + 1 words (the last one is cleared here) and S has
 // SCAP + rank_pad<LIMITED>() entries (those past the kept ones are cleared here).
-template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Emit>
+template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Emit, class Scattered>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             uint32_t c_gt, uint32_t m, bool ties, const BucketMap& bucket_of,
-                                            Emit&& emit) {
+                                            Emit&& emit, Scattered&& scattered) {
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     const int tid = opaque_tid();
@@ -774,12 +793,16 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         packed += cw[i];
     }
     const uint32_t tsum = (packed >> 16) + (packed & 0xFFFFu);
-    {  // longest bucket (kept or not: a safe overestimate)
-        uint32_t mx = 0;
+    {  // does any bucket (kept or not) hold more than the limit?  Adding 0x7FFF - limit to
+       // each 16-bit count sets its bit 15 exactly when it exceeds the limit; counts stay
+       // below 2^15, so neither half carries into the other.
+        constexpr uint32_t LIM = LIMITED ? kBucketLimit : kBucketLimitRow;
+        constexpr uint32_t BIAS = (0x7FFFu - LIM) * 0x10001u;
+        static_assert(CPT * NT + (0x7FFF - LIM) < 0x10000, "bucket counts (at most c_gt) stay below 2^15");
+        uint32_t ov = 0;
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) mx = max(mx, max(cw[i] >> 16, cw[i] & 0xFFFFu));
-        mx = wave_max(mx);
-        if (lane == 0) __hip_atomic_fetch_max(&ctl[kCtlMaxBucket], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int i = 0; i < WPT; ++i) ov |= cw[i] + BIAS;
+        if (ov & 0x80008000u) ctl[kCtlMaxBucket] = 1u;  // (any lane; all store the same)
     }
     uint32_t total;
     const uint32_t run0 = block_excl_scan<NT>(tsum, wsum + 16, &total);
@@ -810,7 +833,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     __syncthreads();
     const uint32_t bt = ties ? 0u : ctl[kCtlBt];
     const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
-    const bool too_long = ctl[kCtlMaxBucket] > (uint32_t)(LIMITED ? kBucketLimit : kBucketLimitRow);
+    const bool too_long = ctl[kCtlMaxBucket] != 0u;
     if (LIMITED && (kept > (uint32_t)SCAP || too_long)) return false;  // uniform
 
     // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write)
@@ -849,6 +872,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     }
     for (int i = tid; i < rank_pad<LIMITED>(); i += NT) S[kept + i] = 0;  // kept <= SCAP here
     __syncthreads();
+    scattered();  // past the point of falling back: the caller may reuse its registers
 
     if (!LIMITED && too_long) {  // uniform
         static_assert(LIMITED || (SCAP & (SCAP - 1)) == 0, "the sort pads S to a power of two");
@@ -864,8 +888,9 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     // end belong to lower buckets or the zero padding, so every lane compares them all.
     const uint16_t* const b16 = reinterpret_cast<const uint16_t*>(bucket);
     constexpr int RUNR = 2;
+    const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(tid & ~63));  // (scalar: a uniform loop exit)
     for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
-        if (q0 + (uint32_t)(tid & ~63) >= kept) break;  // wave-uniform: nothing left for this wave
+        if (q0 + wbase >= kept) break;  // nothing left for this wave
         uint64_t cc[RUNR];
         uint32_t st[RUNR], rank[RUNR];
         uint32_t lmax = 0;
@@ -873,11 +898,12 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         for (int i = 0; i < RUNR; ++i) {
             const uint32_t q = q0 + i * NT + tid;
             const bool in = q < kept;
-            cc[i] = in ? S[q] : 0ull;
+            cc[i] = S[min(q, kept)];  // S[kept] is zero: no branch around the read
             const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
             const uint32_t en = min((uint32_t)b16[bk], kept);
-            st[i] = in ? (uint32_t)b16[bk + 1] : 0u;
-            lmax = max(lmax, in && en > st[i] ? en - st[i] : 0u);
+            const uint32_t s0 = b16[bk + 1];
+            st[i] = in ? s0 : 0u;
+            lmax = max(lmax, in && en > s0 ? en - s0 : 0u);
             rank[i] = 0;
         }
         lmax = wave_max(lmax);
@@ -908,11 +934,12 @@ __device__ __forceinline__ void bucket_range(uint32_t P, uint32_t lo, uint32_t s
     *L = min(lo, *U);
 }
 
-// Pivot path of a row that fits one workgroup (raw bits in u[]).  Returns false, with LDS
-// left dirty but registers untouched, when the row needs the exact path.
-template <int NT, int EPT, int KMAX>
+// Pivot path of a row that fits one workgroup (raw bits in u[], dead after the write pass).
+// Returns false, with LDS left dirty, when the row needs the exact path.  scattered() runs
+// once the row can no longer fall back.
+template <int NT, int EPT, int KMAX, class Scattered>
 __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMAX>& s, const uint32_t (&u)[EPT],
-                                          int fast_mode) {
+                                          int fast_mode, Scattered&& scattered) {
     using FS = FastSmem<NT, EPT, KMAX>;
     constexpr int BW = FS::BWORDS;
     const int tid = opaque_tid();
@@ -944,7 +971,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     {
         // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
         const uint32_t rr = fast_mode == 2 ? 1u : pivot_rank(nsamp, m, nt);
-        if (m < nt && rr < (uint32_t)nsamp) P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {}, &passes);
+        if (m < nt && rr < (uint32_t)nsamp)
+            P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {}, &passes, s.ctl + kCtlSel);
     }
     // The least sample above P starts the bucket range when P may sit far below the kept
     // keys: P = 0 (no pivot) or P exactly a sample's key (a plateau of equal scores, four
@@ -1052,7 +1080,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
             [&](uint32_t slot, uint32_t pos, uint32_t bits) {
                 r.oidx[slot] = (int32_t)pos;
                 if (r.oval) r.oval[slot] = bits;
-            }))
+            },
+            scattered))
         return false;
 
     // ------------------------------------------------ ties at P: smallest positions
@@ -1295,7 +1324,8 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
         [&](uint32_t slot, uint32_t pos, uint32_t bits) {
             r.oidx[slot] = (int32_t)pos;
             if (r.oval) r.oval[slot] = bits;
-        });
+        },
+        [] {});
     write_padding<NT>(r.oidx, r.oval, m, r.k);
     return true;
 }
@@ -1591,7 +1621,7 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     return r;
 }
 
-// One (row, tile) item: a whole row in the one-workgroup-per-row kernel (MULTI false).
+// One (row, tile) item of the several-workgroups-per-row kernel.
 template <int NT, int EPT, int KMAX, bool MULTI>
 __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, int b, int tile) {
     const RowCtx r = row_setup<NT * EPT, MULTI>(p, b, tile);
@@ -1609,19 +1639,36 @@ __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, K
 
     uint32_t bar_target = 0;  // row barriers passed so far x tiles (several workgroups per row)
     if (p.fast) {
-        if constexpr (MULTI) {
-            if (multi_fast_tile<NT, EPT, KMAX>(p, r, s.mfast, u, bar_target)) return;
-        } else {
-            if (fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast)) return;
-        }
-        __syncthreads();  // fall back to the exact path
-        // (a single-workgroup row reloads its tile, so the pivot path's later phases get
-        // the tile's registers; a split row's tiles keep theirs)
-        if constexpr (!MULTI) load_tile<NT, EPT>(u, p.scores + r.base + r.j0, r.nt);
+        if (multi_fast_tile<NT, EPT, KMAX>(p, r, s.mfast, u, bar_target)) return;
+        __syncthreads();  // fall back to the exact path on the same registers
     }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
     exact_tile<NT, EPT, KMAX, MULTI>(p, r, s.exact, u, bar_target);
+}
+
+// One row of the one-workgroup-per-row kernel (grid = B: no row loop, so nothing
+// row-invariant is hoisted into registers that would stay live across the row).
+template <int NT, int EPT, int KMAX>
+__device__ __forceinline__ void single_row(const Params& p, SmemAll<NT, EPT, KMAX, false>& s, int b) {
+    const RowCtx r = row_setup<NT * EPT, false>(p, b, 0);
+    if (r.m == 0) {  // empty window: every slot is padding
+        write_padding<NT>(r.oidx, r.oval, 0, r.k);
+        return;
+    }
+    uint32_t u[EPT];
+    load_tile<NT, EPT>(u, p.scores + r.base, r.nt);
+    if (p.fast && fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast, [] {})) return;
+    if (p.fast) {
+        __syncthreads();  // fall back to the exact path
+        // (reloaded: kept in registers through the pivot path, the tile would crowd out its
+        // later phases)
+        load_tile<NT, EPT>(u, p.scores + r.base, r.nt);
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
+    uint32_t bar_target = 0;
+    exact_tile<NT, EPT, KMAX, false>(p, r, s.exact, u, bar_target);
 }
 
 // MINW: waves per SIMD the register allocation must allow (the LDS footprint fixes
@@ -1631,16 +1678,11 @@ __global__ __launch_bounds__(NT, MINW) void topk_ragged_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto& s = *reinterpret_cast<SmemAll<NT, EPT, KMAX, MULTI>*>(smem_raw);
     if constexpr (!MULTI) {
-        // One workgroup per row (grid = B): no item loop, so nothing row-invariant is
-        // hoisted into registers that would stay live across the row.
-        process_tile<NT, EPT, KMAX, MULTI>(p, s, (int)blockIdx.x, 0);
-        return;
-    }
-    const int64_t items = MULTI ? (int64_t)p.B * p.tiles_per_row : (int64_t)p.B;
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int b = MULTI ? (int)(it / p.tiles_per_row) : (int)it;
-        const int tile = MULTI ? (int)(it % p.tiles_per_row) : 0;
-        process_tile<NT, EPT, KMAX, MULTI>(p, s, b, tile);
+        single_row<NT, EPT, KMAX>(p, s, (int)blockIdx.x);
+    } else {
+        const int64_t items = (int64_t)p.B * p.tiles_per_row;
+        for (int64_t it = blockIdx.x; it < items; it += gridDim.x)
+            process_tile<NT, EPT, KMAX, MULTI>(p, s, (int)(it / p.tiles_per_row), (int)(it % p.tiles_per_row));
     }
 }
 
