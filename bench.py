@@ -88,6 +88,17 @@ def time_gpu(wl, steps, warmup, rotate):
     return wall, launch_ms, need
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s: float = 15.0):
     """The oracle as it stands, on the host cores, over rows of the same workload."""
     import oracle
@@ -103,6 +114,11 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     t0 = time.perf_counter()
     oracle.topk_ragged(wl.scores, rs, ln, wl.k, wl.max_len, threads=threads)
     dt = time.perf_counter() - t0
+    extra = {}
+    if wl.B <= 64 and threads > 1:  # small batches: the single-thread figure as well
+        t0 = time.perf_counter()
+        oracle.topk_ragged(wl.scores, rs, ln, wl.k, wl.max_len, threads=1)
+        extra["value_1thread"] = rows / (time.perf_counter() - t0)
     return {
         "value": rows / dt,
         "unit": "rows/s",
@@ -111,6 +127,8 @@ def cpu_baseline(wl, budget_s: float = 15.0):
         "sample": "%d of %d rows (%s), qsort by (total-order key desc, index asc) + truncate, %d threads"
                   % (rows, wl.B, "all" if rows == wl.B else "evenly spaced", threads),
         "seconds": dt,
+        "cpu_model": cpu_model(),
+        **extra,
     }
 
 
@@ -123,6 +141,89 @@ def traffic_for(workload, algo_bytes):
     if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def event_us(fn, reps: int, stream) -> list:
+    """Per-call µs of fn() over `reps` back-to-back calls, 5 rounds (events on `stream`)."""
+    import torch
+    out = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return out
+
+
+def attainable_bandwidth() -> dict:
+    """What plain streaming kernels reach on this GPU, median of 5 rounds: the library's
+    read probe (16-byte loads, every byte once) over 1 GiB, and a 512 MiB device copy."""
+    import torch
+    import deterministic_exact_top_amd as detk
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    x = torch.rand(1 << 28, device=dev)  # 1 GiB
+    word = torch.zeros(1, dtype=torch.int32, device=dev)
+    rd = event_us(lambda: detk.read_probe(x, word, stream), 10, stream)
+    src = torch.rand(1 << 27, device=dev)  # 512 MiB
+    dst = torch.empty_like(src)
+    cp = event_us(lambda: dst.copy_(src), 10, stream)
+    return {
+        "stream_read_gbps": x.nbytes / (float(np.median(rd)) * 1e-6) / 1e9,
+        "copy_gbps": 2 * src.nbytes / (float(np.median(cp)) * 1e-6) / 1e9,
+        "kernels": "detk_read_probe over 1 GiB (read only); 512 MiB device copy (read + write)",
+    }
+
+
+def graph_timing(wl, calls: int = 20) -> dict:
+    """Per-call time with `calls` calls (over rotated input copies) captured in one HIP graph
+    and replayed: no host work between the kernels."""
+    import torch
+    import deterministic_exact_top_amd as detk
+    dev = torch.device("cuda:0")
+    rotate = max(1, min(calls, -(-2 * MALL_BYTES // max(wl.scores.nbytes, 1))))
+    copies = [torch.from_numpy(wl.scores).to(dev) for _ in range(rotate)]
+    rs = torch.from_numpy(wl.row_starts).to(dev)
+    ln = torch.from_numpy(wl.lengths).to(dev)
+    out_i = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
+    out_v = torch.empty((wl.B, wl.k), dtype=torch.float32, device=dev)
+    need = detk.workspace_size(wl.B, wl.k, wl.max_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    kw = dict(max_len=wl.max_len, out_idx=out_i, out_val=out_v, workspace=ws)
+    detk.topk_ragged(copies[0], rs, ln, wl.k, **kw)  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            detk.topk_ragged(copies[i % rotate], rs, ln, wl.k, **kw)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    per = [u / calls for u in event_us(g.replay, 1, torch.cuda.current_stream(dev))]
+    return {"graph_us_per_call": float(np.median(per)), "calls_per_graph": calls, "input_copies": rotate}
+
+
+def dispatch_floor(wl) -> dict:
+    """Per-call time of the same call with every row empty (all padding): the host-side
+    argument handling plus the launch, back to back."""
+    import torch
+    import deterministic_exact_top_amd as detk
+    dev = torch.device("cuda:0")
+    s = torch.zeros(16, device=dev)
+    rs = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+    ln = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+    out_i = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
+    out_v = torch.empty((wl.B, wl.k), dtype=torch.float32, device=dev)
+    need = detk.workspace_size(wl.B, wl.k, wl.max_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    call = lambda: detk.topk_ragged(s, rs, ln, wl.k, max_len=wl.max_len, out_idx=out_i, out_val=out_v, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    per = event_us(call, 200, torch.cuda.current_stream(dev))
+    return {"empty_call_us": float(np.median(per)), "note": "same B, k and max_len, every length 0"}
 
 
 def copy_probe(nbytes: int, reps: int) -> None:
@@ -147,6 +248,10 @@ def main():
                     help="input copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
+    ap.add_argument("--attainable", action="store_true",
+                    help="add the bandwidth a plain streaming read and a plain copy reach on this GPU")
+    ap.add_argument("--graph", action="store_true", help="add the per-call time with the calls replayed from a HIP graph")
+    ap.add_argument("--floor", action="store_true", help="add the per-call time of the same call with every row empty")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -201,6 +306,15 @@ def main():
             "kernel": "topk_ragged_kernel",
         },
     }
+    if args.graph:
+        log("timing graph replay")
+        result["graph"] = graph_timing(wl)
+    if args.floor:
+        log("timing empty calls")
+        result["floor"] = dispatch_floor(wl)
+    if args.attainable:
+        log("timing plain streaming kernels")
+        result["attainable"] = attainable_bandwidth()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -61,6 +61,8 @@ def load_library():
     lib.detk_workspace_error.argtypes = [vp, sz, vp]
     lib.detk_workspace_error.restype = ctypes.c_int
     lib.detk_debug_set.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.detk_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.detk_read_probe.restype = ctypes.c_int
     lib.detk_debug_set.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -87,6 +89,21 @@ def debug_set(what: int, value: int) -> None:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def read_probe(data, out, stream=None) -> None:
+    """Measurement only: one plain streaming read of `data` (a contiguous CUDA tensor,
+    16-byte aligned, size a multiple of 16 bytes), XOR-reduced into `out` (an int32 CUDA
+    tensor of one element the caller zeroed).  Asynchronous on `stream`."""
+    import torch
+    lib = load_library()
+    if not data.is_cuda or not data.is_contiguous() or out.dtype != torch.int32 or not out.is_cuda:
+        raise ValueError("read_probe needs a contiguous CUDA tensor and an int32 CUDA word")
+    s = stream if stream is not None else torch.cuda.current_stream(data.device)
+    st = lib.detk_read_probe(_ptr(data), int(data.numel() * data.element_size()), _ptr(out),
+                             ctypes.c_void_p(s.cuda_stream))
+    if st != DETK_OK:
+        raise DetkError(st, "detk_read_probe")
 
 
 def workspace_error(workspace, stream=None) -> int:

@@ -240,6 +240,28 @@ hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
 
 }  // namespace
 
+// A plain streaming read (measurement only): every 16-byte chunk once, eight loads in
+// flight per thread, XOR-reduced so the loads cannot be dropped.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* out) {
+    constexpr int U = 8;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        uint4 v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) v[j] = p[i + j * stride];
+#pragma unroll
+        for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    for (int off = 32; off > 0; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, 64);
+    if ((threadIdx.x & 63) == 0) atomicXor(out, acc);
+}
+
 extern "C" {
 
 int detk_can_implement(int device, int k, int32_t max_len) {
@@ -328,6 +350,24 @@ int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* st
     uint32_t word = 0;
     if (hipMemcpy(&word, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
     return (int)word;
+}
+
+int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream_ptr) {
+    if (bytes == 0) return DETK_OK;
+    if (!data || !out || (bytes & 15u) != 0 || (reinterpret_cast<uintptr_t>(data) & 15u) != 0)
+        return DETK_ERR_INVALID_ARG;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return DETK_ERR_HIP;
+    DeviceInfo dev;
+    const int st = device_info(device, &dev);
+    if (st != DETK_OK) return st;
+    const size_t n16 = bytes / 16;
+    const int64_t want = (int64_t)dev.cus * 8;  // 8 workgroups of 4 waves per CU: 32 waves
+    const int64_t need = (int64_t)((n16 + 255) / 256);
+    const int grid = (int)(need < want ? need : want);
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream_ptr),
+                       reinterpret_cast<const uint4*>(data), n16, out);
+    return hipGetLastError() == hipSuccess ? DETK_OK : DETK_ERR_HIP;
 }
 
 int detk_debug_set(int what, int value) {

@@ -119,6 +119,16 @@ int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* st
  *                                  falls back.
  * Returns DETK_OK or DETK_ERR_INVALID_ARG.
  */
+/*
+ * detk_read_probe -- MEASUREMENT, not part of the top-k path.  Reads the `bytes` bytes at
+ * `data` (device memory) exactly once with 16-byte loads, a grid-stride loop spread over
+ * every CU, and XORs them into *out (one device word the caller zeroed).  Its bandwidth is
+ * what a plain streaming read attains on the GPU: the ceiling for the score scan.
+ * `data` must be 16-byte aligned and `bytes` a multiple of 16 (else DETK_ERR_INVALID_ARG);
+ * bytes == 0 returns DETK_OK with no launch.  Ordered on `stream`; allocates nothing.
+ */
+int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream);
+
 #define DETK_DEBUG_PATH 1
 #define DETK_DEBUG_STAGING_CAP 2
 #define DETK_DEBUG_MULTI_TILE 3

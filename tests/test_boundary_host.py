@@ -30,8 +30,18 @@ def lib():
 def test_header_declares_entry_points():
     names = _declared()
     for n in ("detk_topk_ragged", "detk_workspace_size", "detk_can_implement", "detk_status_string",
-              "detk_workspace_error", "detk_debug_set"):
+              "detk_workspace_error", "detk_debug_set", "detk_read_probe"):
         assert n in names
+
+
+def test_read_probe_argument_errors(lib):
+    # argument errors are found on the host, before any device call
+    vp = ctypes.c_void_p
+    assert lib.detk_read_probe(None, 0, None, None) == detk.DETK_OK          # nothing to read
+    assert lib.detk_read_probe(None, 16, vp(256), None) == detk.DETK_ERR_INVALID_ARG
+    assert lib.detk_read_probe(vp(256), 16, None, None) == detk.DETK_ERR_INVALID_ARG
+    assert lib.detk_read_probe(vp(256), 20, vp(512), None) == detk.DETK_ERR_INVALID_ARG  # not a multiple of 16
+    assert lib.detk_read_probe(vp(260), 16, vp(512), None) == detk.DETK_ERR_INVALID_ARG  # misaligned
 
 
 def test_library_exports_every_declared_symbol(lib):

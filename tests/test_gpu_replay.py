@@ -163,3 +163,16 @@ def test_hip_graph_replay_matches_eager(dev, shape):
         assert np.array_equal(gv, ev.cpu().numpy().view(np.uint32)), "replay %d val" % rep
         oi, ov = run_oracle(w)
         assert_same(gi, gv, oi, ov, "graph replay %d" % rep)
+
+
+def test_read_probe_reads_every_word(dev):
+    """The streaming-read probe's XOR equals the XOR of every input word (so no load is
+    skipped), for a size that leaves a ragged tail past the four-way unrolled loop."""
+    import torch
+    rng = np.random.default_rng(77)
+    words = rng.integers(0, 2**32, size=(1 << 20) + 12, dtype=np.uint32)  # multiple of 4 words
+    x = torch.from_numpy(words.view(np.int32)).to(dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    detk.read_probe(x, out)
+    torch.cuda.synchronize()
+    assert int(out.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(words))
