@@ -340,7 +340,9 @@ struct MultiFastSmem {
 struct NoSmem {};
 
 // Exact-path staging: smaller in one-workgroup-per-row kernels so that the LDS footprint
-// lets three rows share a CU.
+// lets three rows share a CU, and four for the 16K-element tile (1,248 entries keep its
+// exact path at 40,880 bytes, the most that leaves room for four workgroups; more
+// survivors than that only fall back to a rescan).
 template <int NT, int EPT, bool MULTI>
 constexpr int stage_entries() { return MULTI ? 3072 : (NT == 512 && EPT == 32) ? 1248 : 2560; }
 
@@ -1624,6 +1626,7 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
 // One (row, tile) item of the several-workgroups-per-row kernel.
 template <int NT, int EPT, int KMAX, bool MULTI>
 __device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, int b, int tile) {
+    static_assert(MULTI, "one-workgroup-per-row kernels take single_row");
     const RowCtx r = row_setup<NT * EPT, MULTI>(p, b, tile);
     if (tile >= r.ntiles) return;
 
