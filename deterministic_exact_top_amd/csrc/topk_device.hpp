@@ -54,7 +54,7 @@ constexpr int kRankUnroll = 4;                  // composites compared per turn 
 template <bool LIMITED>
 constexpr int rank_pad() { return (LIMITED ? kBucketLimit : kBucketLimitRow) + kRankUnroll; }
 static_assert(kBuckets / 2 >= 4 * 256, "the packed bucket array doubles as the sample histograms");
-constexpr int kSamplesPerLane = 4;           // fast path: pivot samples per lane
+constexpr int kSamplesPerLane = 2;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 // Per-row workspace words of the multi-workgroup path, zeroed before each launch.
 constexpr int kRowHist = 0;                     // exact path: 4 pass histograms
@@ -285,11 +285,12 @@ struct ExactSmem {
     uint32_t apos[KMAX];          //   and positions
 };
 
-// Candidate capacity (keys above the pivot) of the pivot path: 1.5 KMAX in LDS when one
-// workgroup holds the row (so three 16K-element rows fit a CU's LDS); 2 KMAX in the
-// workspace when several share it.
+// Candidate capacity (keys above the pivot) of the pivot path: 1.75 KMAX in LDS when one
+// workgroup holds the row (the list still fits under the exact path's footprint, so four
+// 16K-element rows share a CU; the pivot from two samples per lane overshoots by a few
+// hundred keys); 2 KMAX in the workspace when several workgroups share a row.
 template <int KMAX>
-constexpr int cand_cap_single() { return 3 * KMAX / 2; }
+constexpr int cand_cap_single() { return 7 * KMAX / 4; }
 template <int KMAX>
 constexpr int cand_cap() { return 2 * KMAX; }
 
