@@ -761,7 +761,6 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     const int tid = opaque_tid();
     const int lane = tid & 63;
-    auto half_of = [](uint32_t word, uint32_t b) -> uint32_t { return (word >> ((b & 1u) << 4)) & 0xFFFFu; };
     const uint32_t mlim = min(m, c_gt);  // slots the candidates fill
     if (tid == 0) bucket[kBuckets / 2] = 0;  // the end above the top bucket (read past a barrier)
 
@@ -839,39 +838,35 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     const bool too_long = ctl[kCtlMaxBucket] != 0u;
     if (LIMITED && (kept > (uint32_t)SCAP || too_long)) return false;  // uniform
 
-    // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write)
+    // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write).
+    // A candidate that is not kept claims nothing: its claim word stays all ones, whose
+    // 16-bit half (65535) is past SCAP, so it is not stored.
+    static_assert(SCAP < 0xFFFF, "an unclaimed slot reads as past the end of S");
     constexpr int SUNR = 2;
 #pragma unroll
     for (int i0 = 0; i0 < CPT; i0 += SUNR) {
         if ((uint32_t)(i0 * NT) >= c_gt) continue;  // uniform
-        uint32_t pos[SUNR];
+        uint32_t old[SUNR], sh[SUNR];
         uint64_t comp[SUNR];
-        uint32_t old[SUNR], bks[SUNR];
-        bool kp[SUNR];
 #pragma unroll
         for (int d = 0; d < SUNR; ++d) {
-            const int i = i0 + d;
-            const uint32_t j = (uint32_t)(tid + i * NT);
-            comp[d] = 0;
-            bks[d] = 0;
-            kp[d] = false;
-            if (i < CPT && j < c_gt) {
-                const uint32_t kk = key_of(cv[i].x);
-                bks[d] = bucket_of(kk);
-                comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv[i].y;
-                kp[d] = bks[d] >= bt;
-            }
-            old[d] = 0;
-            if (kp[d])
-                old[d] = __hip_atomic_fetch_add(&bucket[bks[d] >> 1], 1u << ((bks[d] & 1u) << 4), __ATOMIC_RELAXED,
+            const int i = i0 + d < CPT ? i0 + d : CPT - 1;
+            const uint32_t j = (uint32_t)(tid + (i0 + d) * NT);
+            const uint32_t kk = key_of(cv[i].x);
+            const uint32_t bk = bucket_of(kk);
+            comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv[i].y;
+            sh[d] = (bk & 1u) << 4;
+            old[d] = 0xFFFFFFFFu;
+            if (i0 + d < CPT && j < c_gt && bk >= bt)
+                old[d] = __hip_atomic_fetch_add(&bucket[bk >> 1], 1u << sh[d], __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         // (the claimed slots are read only once every claim of this turn is issued)
 #pragma unroll
-        for (int d = 0; d < SUNR; ++d) pos[d] = kp[d] ? half_of(old[d], bks[d]) : 0xFFFFFFFFu;
-#pragma unroll
-        for (int d = 0; d < SUNR; ++d)
-            if (pos[d] < (uint32_t)SCAP) S[pos[d]] = comp[d];
+        for (int d = 0; d < SUNR; ++d) {
+            const uint32_t pos = (old[d] >> sh[d]) & 0xFFFFu;
+            if (pos < (uint32_t)SCAP) S[pos] = comp[d];
+        }
     }
     for (int i = tid; i < rank_pad<LIMITED>(); i += NT) S[kept + i] = 0;  // kept <= SCAP here
     __syncthreads();
