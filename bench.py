@@ -266,7 +266,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the top-k rows are independent, so a multi-GPU "
-              "run would only shard rows; this build measures one GPU's share (--gpus 1).", file=sys.stderr)
+              "run would only shard rows; the benchmark measures one GPU's share (--gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe, 5)
