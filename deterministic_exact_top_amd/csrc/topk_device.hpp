@@ -586,6 +586,7 @@ enum : int {
     kCtlBase = 11,      // several workgroups: this tile's first candidate slot in the row
     kCtlLast = 12,      // several workgroups: this tile arrived last
     kCtlTieOff = 13,    // several workgroups: keys equal to P in earlier tiles
+    kCtlPool = 15,      // one workgroup: slots claimed in the candidate pool
 };
 
 // Real samples among a tile's nt elements (uniform): slot i * EPT / kSamplesPerLane of
@@ -731,8 +732,9 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 
 // Order the candidates: the m largest of the c_gt candidates (all of them when
 // c_gt <= m) go to slots [0, min(m, c_gt)) in canonical order through
-// emit(slot, position, bits).  Thread t owns candidates j = t + i * NT, i < CPT;
-// src(i, j) gives candidate j as (raw bits, position) (CPT * NT >= c_gt).
+// emit(slot, position, bits).  Each thread owns up to CPT candidates: valid(i) says
+// whether its i-th exists, src(i) gives it as (raw bits, position), and live(i)
+// (wave-uniform) whether some lane of the wave has an i-th candidate.
 // The bucket (BucketMap) holding the m-th largest is the threshold; kept candidates
 // (buckets at or above it) go to S grouped by bucket as composites
 // (key << 32 | ~position), which are unique and whose descending order is the canonical
@@ -753,10 +755,11 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // with its whole bucket).
 // bucket has kBuckets / 2 + 1 words (the last one is cleared here) and S has
 // SCAP + rank_pad<LIMITED>() entries (those past the kept ones are cleared here).
-template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Emit, class Scattered>
+template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Valid, class Live, class Emit,
+          class Scattered>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
-                                            uint32_t c_gt, uint32_t m, bool ties, const BucketMap& bucket_of,
-                                            Emit&& emit, Scattered&& scattered) {
+                                            Valid&& valid, Live&& live, uint32_t c_gt, uint32_t m, bool ties,
+                                            const BucketMap& bucket_of, Emit&& emit, Scattered&& scattered) {
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     const int tid = opaque_tid();
@@ -767,18 +770,13 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     // ---- this thread's candidates, into registers
     uint2 cv[CPT];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const uint32_t j = (uint32_t)(tid + i * NT);
-        cv[i] = j < c_gt ? src(i, j) : make_uint2(0u, 0u);
-    }
+    for (int i = 0; i < CPT; ++i) cv[i] = valid(i) ? src(i) : make_uint2(0u, 0u);
 
     // ---- counts
     if (!COUNTED) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const uint32_t j = (uint32_t)(tid + i * NT);
-            if (j < c_gt) bucket_count(bucket, bucket_of(key_of(cv[i].x)));
-        }
+        for (int i = 0; i < CPT; ++i)
+            if (valid(i)) bucket_count(bucket, bucket_of(key_of(cv[i].x)));
         __syncthreads();
     }
 
@@ -845,19 +843,18 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     constexpr int SUNR = 2;
 #pragma unroll
     for (int i0 = 0; i0 < CPT; i0 += SUNR) {
-        if ((uint32_t)(i0 * NT) >= c_gt) continue;  // uniform
+        if (!live(i0) && !(i0 + 1 < CPT && live(i0 + 1))) continue;  // uniform
         uint32_t old[SUNR], sh[SUNR];
         uint64_t comp[SUNR];
 #pragma unroll
         for (int d = 0; d < SUNR; ++d) {
             const int i = i0 + d < CPT ? i0 + d : CPT - 1;
-            const uint32_t j = (uint32_t)(tid + (i0 + d) * NT);
             const uint32_t kk = key_of(cv[i].x);
             const uint32_t bk = bucket_of(kk);
             comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv[i].y;
             sh[d] = (bk & 1u) << 4;
             old[d] = 0xFFFFFFFFu;
-            if (i0 + d < CPT && j < c_gt && bk >= bt)
+            if (i0 + d < CPT && valid(i0 + d) && bk >= bt)
                 old[d] = __hip_atomic_fetch_add(&bucket[bk >> 1], 1u << sh[d], __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         }
@@ -985,53 +982,44 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     }
     const AboveP ap(P);
 
-    // ------------------------------------------------ count pass: keys > P per wave
-    // (ballot popcounts: the counting is scalar work)
+    // ------------------------------------------------ one pass: candidates (bits, position)
+    // into per-wave regions of R slots, keys == P into the position bitmap when P is a
+    // plateau value (then the tail may need them).  The running count is scalar and
+    // checked before each slot's stores: a slot that no longer fits its wave's region
+    // claims slots in the shared pool after the regions instead (one LDS atomic per wave
+    // and slot); only an exhausted pool sends the row to the exact path.  (Past the
+    // pivot's last barrier no wave reads the sample histograms, so the regions may
+    // overwrite them.)
+    constexpr uint32_t NW = NT / 64;
+    constexpr uint32_t R = ((uint32_t)FS::CCAP * 7 / 8 / NW) / 64 * 64;  // region slots per wave
+    constexpr uint32_t POOL = (uint32_t)FS::CCAP - NW * R;                 // shared overflow slots
+    static_assert(R > 0 && POOL > 0, "regions and pool both have room");
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t wcnt = 0;
-    if (P >= 0x80000000u)
-        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
-            wcnt += (uint32_t)__popcll(__ballot(ap.gt<true>(x)) & __ballot(ok));
-        });
-    else
-        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
-            wcnt += (uint32_t)__popcll(__ballot(ap.gt<false>(x)) & __ballot(ok));
-        });
-    if (lane == 0) s.wsum[wave] = wcnt;
-    __syncthreads();
-    // (past this barrier every wave is done with the sample histograms and has published
-    // its sample extremes)
-    uint32_t o = 0, c_gt = 0;  // this wave's first candidate slot; all candidates
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const uint32_t c = s.wsum[w];
-        o += w < wave ? c : 0u;
-        c_gt += c;
-    }
-    o = __builtin_amdgcn_readfirstlane(o);  // wave-uniform: keep the running slot scalar
-    if (c_gt > (uint32_t)FS::CCAP) return false;  // uniform
-    const bool ties = c_gt < (uint32_t)m;          // uniform: keys == P fill the tail
-    const uint32_t U = max(P, s.ctl[kCtlSmaxFin]);
-    const uint32_t L = need_lo ? min(s.ctl[kCtlLo], U) : P;
-    const BucketMap bucket_of(L, U);
-
-    // ------------------------------------------------ write pass: (bits, position) of the
-    // candidates to LDS; keys == P into the position bitmap when the tail needs them.
-    const uint32_t o_first = o;  // this wave's candidates: [o_first, o) after the pass
-    uint32_t neq = 0;
-    auto write_pass = [&](auto pos_tag, auto eq_tag) {
+    const uint32_t base = (uint32_t)wave * R, limit = base + R;
+    const bool mark_eq = passes == 4;  // uniform: P is a sample's key exactly
+    uint32_t o = base, neq = 0;
+    auto one_pass = [&](auto pos_tag, auto eq_tag) {
         constexpr bool POS = decltype(pos_tag)::value;
         constexpr bool EQ = decltype(eq_tag)::value;
         uint32_t nib = 0;
         visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int c, int v, bool ok, int t4) {
             const bool gx = ap.gt<POS>(x);
             const uint64_t mk = __ballot(gx) & __ballot(ok);
-            if (gx && ok) {
-                const uint32_t q = lanes_below_plus(mk, o);
-                s.cand.bits[q] = x;
-                s.cand.pos[q] = (uint32_t)(t4 + (v * NT * 4 + c));
+            const uint32_t cnt = (uint32_t)__popcll(mk);
+            if (o + cnt <= limit) {  // uniform
+                if (gx && ok) {
+                    const uint32_t q = lanes_below_plus(mk, o);
+                    s.cand.bits[q] = x;
+                    s.cand.pos[q] = (uint32_t)(t4 + (v * NT * 4 + c));
+                }
+                o += cnt;
+            } else {  // the pool (rare)
+                const uint32_t q = claim_slot(gx && ok, &s.ctl[kCtlPool]);
+                if (gx && ok && q < POOL) {
+                    s.cand.bits[NW * R + q] = x;
+                    s.cand.pos[NW * R + q] = (uint32_t)(t4 + (v * NT * 4 + c));
+                }
             }
-            o += (uint32_t)__popcll(mk);
             if (EQ) {
                 nib |= (ap.eq<POS>(x) && ok ? 1u : 0u) << c;
                 if (c == 3) {
@@ -1047,33 +1035,48 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         });
     };
     if (P >= 0x80000000u) {
-        if (ties) write_pass(std::true_type{}, std::true_type{});
-        else write_pass(std::true_type{}, std::false_type{});
+        if (mark_eq) one_pass(std::true_type{}, std::true_type{});
+        else one_pass(std::true_type{}, std::false_type{});
     } else {
-        if (ties) write_pass(std::false_type{}, std::true_type{});
-        else write_pass(std::false_type{}, std::false_type{});
+        if (mark_eq) one_pass(std::false_type{}, std::true_type{});
+        else one_pass(std::false_type{}, std::false_type{});
     }
-    if (ties) {
+    if (mark_eq) {
         neq = wave_incl_scan(neq);
         if (lane == 63) lds_add(&s.ctl[kCtlEq], neq);
     }
-    // Each wave counts its own candidates into the buckets (its writes are complete once
-    // its LDS counter drains), so the count needs no barrier of its own.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (uint32_t j = o_first + (uint32_t)lane; j < o; j += 128) {  // two reads in flight
-        const uint32_t x0 = s.cand.bits[j];
-        const bool two = j + 64 < o;
-        const uint32_t x1 = two ? s.cand.bits[j + 64] : 0u;
-        bucket_count(s.bucket, bucket_of(key_of(x0)));
-        if (two) bucket_count(s.bucket, bucket_of(key_of(x1)));
-    }
+    if (lane == 0) s.wsum[wave] = o - base;
     __syncthreads();
-    if (ties && c_gt + s.ctl[kCtlEq] < (uint32_t)m) return false;  // uniform: pivot missed
+    // (past this barrier every wave has published its count, its sample extremes and its
+    // keys equal to P)
+    const uint32_t pooled = __builtin_amdgcn_readfirstlane(s.ctl[kCtlPool]);
+    if (pooled > POOL) return false;  // uniform: the pool overflowed
+    uint32_t c_gt = pooled;
+#pragma unroll
+    for (int w = 0; w < (int)NW; ++w) c_gt += s.wsum[w];
+    c_gt = __builtin_amdgcn_readfirstlane(c_gt);
+    const bool ties = c_gt < (uint32_t)m;  // uniform: keys == P fill the tail
+    if (ties && (!mark_eq || c_gt + s.ctl[kCtlEq] < (uint32_t)m)) return false;  // uniform: pivot missed
+    const uint32_t U = max(P, s.ctl[kCtlSmaxFin]);
+    const uint32_t L = need_lo ? min(s.ctl[kCtlLo], U) : P;
+    const BucketMap bucket_of(L, U);
 
     // ------------------------------------------------ order the candidates, straight to
     // the output row (S is in bucket order, so a wave's slots are nearly contiguous)
-    if (!bucket_rank<NT, FS::SCAP, (FS::CCAP + NT - 1) / NT, true, true>(
-            s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return make_uint2(s.cand.bits[j], s.cand.pos[j]); },
+    // (a thread owns RC entries of its wave's region, lane + 64 i, then PC pool entries,
+    // tid + NT i)
+    constexpr int RC = (int)(R / 64), PC = (int)((POOL + NT - 1) / NT);
+    const uint32_t c_w = o - base;  // this wave's region entries (scalar)
+    if (!bucket_rank<NT, FS::SCAP, RC + PC, true, false>(
+            s.bucket, s.S, s.wsum, s.ctl,
+            [&](int i) {
+                const uint32_t q = i < RC ? base + (uint32_t)(lane + 64 * i) : NW * R + (uint32_t)(tid + (i - RC) * NT);
+                return make_uint2(s.cand.bits[q], s.cand.pos[q]);
+            },
+            [&](int i) {
+                return i < RC ? (uint32_t)(lane + 64 * i) < c_w : (uint32_t)(tid + (i - RC) * NT) < pooled;
+            },
+            [&](int i) { return i < RC ? (uint32_t)(64 * i) < c_w : (uint32_t)((i - RC) * NT) < pooled; },
             c_gt, (uint32_t)m, ties, bucket_of,
             [&](uint32_t slot, uint32_t pos, uint32_t bits) {
                 r.oidx[slot] = (int32_t)pos;
@@ -1317,8 +1320,9 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
                  __hip_atomic_load(&rw[kRowUFin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), &L, &U);
     const uint2* gc = p.ws_cand + (int64_t)b * CAP;
     bucket_rank<NT, MS::SCAP, (MS::SCAP + NT - 1) / NT, false, false>(
-        s.bucket, s.S, s.wsum, s.ctl, [&](int, uint32_t j) { return gc[j]; }, c_gt, (uint32_t)m, ties,
-        BucketMap(L, U),
+        s.bucket, s.S, s.wsum, s.ctl, [&](int i) { return gc[tid + i * NT]; },
+        [&](int i) { return (uint32_t)(tid + i * NT) < c_gt; }, [&](int i) { return (uint32_t)(i * NT) < c_gt; },
+        c_gt, (uint32_t)m, ties, BucketMap(L, U),
         [&](uint32_t slot, uint32_t pos, uint32_t bits) {
             r.oidx[slot] = (int32_t)pos;
             if (r.oval) r.oval[slot] = bits;
