@@ -163,3 +163,40 @@ def test_random_sweep(dev, case):
     rows = [_family(rng, fam, int(rng.integers(0, max_len + 1))) for _ in range(B)]
     wl = _dense(rows, k, "sweep%d" % case, L=max_len)
     _check(dev, wl, "sweep %d (%s)" % (case, fam))
+
+
+def _wave_positions(n, nt_threads=512, wave=0):
+    """Window positions a 16K-element tile gives to one wave (slot (v, c) of lane t holds
+    position (v * NT + t) * 4 + c)."""
+    pos = []
+    for v in range(n // (nt_threads * 4)):
+        start = v * nt_threads * 4 + wave * 256
+        pos.extend(range(start, start + 256))
+    return np.array(pos, dtype=np.int64)
+
+
+@pytest.mark.parametrize("shift", [0.25, 0.75, 1.5, 4.0])
+def test_candidates_crowd_one_wave(dev, shift):
+    """Keys above the pivot concentrated in one wave's share of the tile: its region fills
+    and the rest go to the shared overflow pool (or, for the largest shifts, the pool runs
+    out and the row takes the exact path).  Results must not depend on which."""
+    rng = np.random.default_rng(int(shift * 100))
+    n = 16384
+    rows = []
+    for wave in (0, 3, 7):
+        r = np.abs(rng.standard_normal(n)).astype(np.float32)
+        pw = _wave_positions(n, wave=wave)
+        r[pw] += np.float32(shift)
+        rows.append(r)
+    _check(dev, _dense(rows, 2048, "crowd"), "candidates crowd one wave (shift %.2f)" % shift, path=1)
+
+
+def test_only_one_wave_has_candidates(dev):
+    """Every non-zero score sits in wave 0's share: the pivot lands on the 0.0 plateau, all
+    2048 positives are candidates of one wave, and the pool cannot hold them."""
+    rng = np.random.default_rng(21)
+    n = 16384
+    r = np.zeros(n, np.float32)
+    pw = _wave_positions(n, wave=0)
+    r[pw] = (np.abs(rng.standard_normal(pw.size)) + 0.01).astype(np.float32)
+    _check(dev, _dense([r, r.copy()], 2048, "one_wave"), "only one wave has candidates", path=1)
