@@ -305,8 +305,8 @@ struct FastSmem {
     // one two-address LDS store writes a candidate with no offset arithmetic)
     union {
         struct {
-            uint32_t bits[CCAP];  // candidates: raw bits
-            uint32_t pos[CCAP];   //   and positions
+            uint32_t bits[CCAP];  // candidates: raw bits (per-wave regions, then the shared
+            uint32_t pos[CCAP];   //   overflow pool) and positions
         } cand;
         uint64_t S[SCAP + rank_pad<true>()];  // kept candidates as composites, grouped by
                                               // bucket, then zeros (written once every
@@ -944,7 +944,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
 
     // ------------------------------------------------ clear LDS state
     block_zero<NT, BW>(s.bitmap);
-    uint32_t* const shist = reinterpret_cast<uint32_t*>(s.S);  // sample histograms (S is free until the scatter)
+    uint32_t* const shist = reinterpret_cast<uint32_t*>(s.S);  // sample histograms (the list's LDS is free until the write pass)
     block_zero<NT, 2 * kRadix>(shist);
     block_zero<NT, kBuckets / 2>(s.bucket);
     if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
