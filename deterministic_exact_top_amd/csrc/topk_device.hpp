@@ -1001,38 +1001,71 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     auto one_pass = [&](auto pos_tag, auto eq_tag) {
         constexpr bool POS = decltype(pos_tag)::value;
         constexpr bool EQ = decltype(eq_tag)::value;
-        uint32_t nib = 0;
-        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int c, int v, bool ok, int t4) {
-            const bool gx = ap.gt<POS>(x);
-            const uint64_t mk = __ballot(gx) & __ballot(ok);
-            const uint32_t cnt = (uint32_t)__popcll(mk);
-            if (o + cnt <= limit) {  // uniform
-                if (gx && ok) {
-                    const uint32_t q = lanes_below_plus(mk, o);
-                    s.cand.bits[q] = x;
-                    s.cand.pos[q] = (uint32_t)(t4 + (v * NT * 4 + c));
+        const int t4 = tid * 4;
+        // One group of four slots (v): the four masks and counts first, so a group that
+        // fits the region takes one check; a group that does not goes slot by slot,
+        // region first, then the pool.  FULL: every lane's four slots are in the tile.
+        auto group = [&](int v, auto full_tag, int llim) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int p0 = t4 + v * NT * 4;
+            bool g[4];
+            uint64_t mk[4];
+            uint32_t tot = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                g[c] = ap.gt<POS>(u[4 * v + c]) && (FULL || c < llim);
+                mk[c] = __ballot(g[c]);
+                tot += (uint32_t)__popcll(mk[c]);
+            }
+            if (o + tot <= limit) {  // uniform
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    uint32_t* const cb = s.cand.bits + o;  // (scalar base: one address op per lane)
+                    if (g[c]) {
+                        const uint32_t q = lanes_below(mk[c]);
+                        cb[q] = u[4 * v + c];
+                        cb[q + (uint32_t)FS::CCAP] = (uint32_t)(p0 + c);
+                    }
+                    o += (uint32_t)__popcll(mk[c]);
                 }
-                o += cnt;
-            } else {  // the pool (rare)
-                const uint32_t q = claim_slot(gx && ok, &s.ctl[kCtlPool]);
-                if (gx && ok && q < POOL) {
-                    s.cand.bits[NW * R + q] = x;
-                    s.cand.pos[NW * R + q] = (uint32_t)(t4 + (v * NT * 4 + c));
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t cnt = (uint32_t)__popcll(mk[c]);
+                    if (o + cnt <= limit) {  // uniform
+                        if (g[c]) {
+                            const uint32_t q = lanes_below_plus(mk[c], o);
+                            s.cand.bits[q] = u[4 * v + c];
+                            s.cand.pos[q] = (uint32_t)(p0 + c);
+                        }
+                        o += cnt;
+                    } else {  // the pool (rare)
+                        const uint32_t q = claim_slot(g[c], &s.ctl[kCtlPool]);
+                        if (g[c] && q < POOL) {
+                            s.cand.bits[NW * R + q] = u[4 * v + c];
+                            s.cand.pos[NW * R + q] = (uint32_t)(p0 + c);
+                        }
+                    }
                 }
             }
             if (EQ) {
-                nib |= (ap.eq<POS>(x) && ok ? 1u : 0u) << c;
-                if (c == 3) {
-                    if (nib) {
-                        const int p0 = t4 + v * NT * 4;
-                        __hip_atomic_fetch_or(&s.bitmap[p0 >> 5], nib << (p0 & 31), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_WORKGROUP);
-                        neq += (uint32_t)__popc(nib);
-                    }
-                    nib = 0;
+                uint32_t nib = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) nib |= (ap.eq<POS>(u[4 * v + c]) && (FULL || c < llim) ? 1u : 0u) << c;
+                if (nib) {
+                    __hip_atomic_fetch_or(&s.bitmap[p0 >> 5], nib << (p0 & 31), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+                    neq += (uint32_t)__popc(nib);
                 }
             }
-        });
+        };
+#pragma unroll
+        for (int v = 0; v < EPT / 4; ++v) {
+            const int lim = nt - v * NT * 4;
+            if (lim <= 0) break;
+            if (lim >= NT * 4) group(v, std::true_type{}, 0);
+            else group(v, std::false_type{}, lim - t4);
+        }
     };
     if (P >= 0x80000000u) {
         if (mark_eq) one_pass(std::true_type{}, std::true_type{});
