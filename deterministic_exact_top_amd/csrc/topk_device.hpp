@@ -515,12 +515,19 @@ __device__ __forceinline__ void bitonic_desc_u64(uint64_t* A, int count) {
     }
 }
 
+// base[i] = v, addressed as a 32-bit byte offset from the (wave-uniform) row base, which
+// the store takes as its scalar base: no 64-bit address arithmetic per element.
+template <class T>
+__device__ __forceinline__ void store_at(T* base, uint32_t i, T v) {
+    *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T)) = v;
+}
+
 // Write the padding slots [m, k) of one output row.
 template <int NT>
 __device__ __forceinline__ void write_padding(int32_t* oidx, uint32_t* oval, int m, int k) {
     for (int q = m + opaque_tid(); q < k; q += NT) {
-        oidx[q] = -1;
-        if (oval) oval[q] = kNegInfBits;
+        store_at(oidx, (uint32_t)q, -1);
+        if (oval) store_at(oval, (uint32_t)q, kNegInfBits);
     }
 }
 
@@ -619,9 +626,12 @@ __device__ __forceinline__ void take_samples(const uint32_t (&u)[EPT], int32_t n
 // Sample rank whose key bounds the m-th largest of n keys from below with high
 // probability: the expected rank of that key among nsamp samples plus 3.5 standard
 // deviations plus 4.
+// (Only the path a row takes depends on it, never the result, so the hardware's
+// reciprocal and square-root approximations serve: a few instructions instead of the
+// correctly rounded sequences.)
 __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) {
-    const float expct = (float)nsamp * (float)m / (float)n;
-    return (uint32_t)ceilf(expct + 3.5f * sqrtf(expct) + 4.0f);
+    const float expct = (float)nsamp * (float)m * __builtin_amdgcn_rcpf((float)n);
+    return (uint32_t)ceilf(expct + 3.5f * __builtin_amdgcn_sqrtf(expct) + 4.0f);
 }
 
 // P = the key prefix of the rr-th largest sample, MSB first, one 8-bit digit per pass;
@@ -767,16 +777,40 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     const uint32_t mlim = min(m, c_gt);  // slots the candidates fill
     if (tid == 0) bucket[kBuckets / 2] = 0;  // the end above the top bucket (read past a barrier)
 
-    // ---- this thread's candidates, into registers
+    // ---- this thread's candidates, into registers as (key, position), with their buckets
+    // (computed once for the count and the scatter; only for entries some lane of the
+    // wave holds)
+    // (keys and buckets stay in registers only for a few candidates per thread; with
+    // more, the count and the scatter each derive them from the raw bits rather than spill)
+    constexpr bool KEEP = CPT <= 8;
     uint2 cv[CPT];
+    uint32_t bk[KEEP ? CPT : 1];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) cv[i] = valid(i) ? src(i) : make_uint2(0u, 0u);
+    if constexpr (KEEP) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            bk[i] = 0;
+            if (live(i)) {  // uniform
+                cv[i].x = key_of(cv[i].x);
+                bk[i] = bucket_of(cv[i].x);
+            }
+        }
+    }
+    auto key_at = [&](int i) -> uint32_t {
+        if constexpr (KEEP) return cv[i].x;
+        else return key_of(cv[i].x);
+    };
+    auto bucket_at = [&](int i) -> uint32_t {
+        if constexpr (KEEP) return bk[i];
+        else return bucket_of(key_of(cv[i].x));
+    };
 
     // ---- counts
     if (!COUNTED) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
-            if (valid(i)) bucket_count(bucket, bucket_of(key_of(cv[i].x)));
+            if (valid(i)) bucket_count(bucket, bucket_at(i));
         __syncthreads();
     }
 
@@ -849,13 +883,12 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
 #pragma unroll
         for (int d = 0; d < SUNR; ++d) {
             const int i = i0 + d < CPT ? i0 + d : CPT - 1;
-            const uint32_t kk = key_of(cv[i].x);
-            const uint32_t bk = bucket_of(kk);
-            comp[d] = ((uint64_t)kk << 32) | (uint32_t)~cv[i].y;
-            sh[d] = (bk & 1u) << 4;
+            const uint32_t b = bucket_at(i);
+            comp[d] = ((uint64_t)key_at(i) << 32) | (uint32_t)~cv[i].y;
+            sh[d] = (b & 1u) << 4;
             old[d] = 0xFFFFFFFFu;
-            if (i0 + d < CPT && valid(i0 + d) && bk >= bt)
-                old[d] = __hip_atomic_fetch_add(&bucket[bk >> 1], 1u << sh[d], __ATOMIC_RELAXED,
+            if (i0 + d < CPT && valid(i0 + d) && b >= bt)
+                old[d] = __hip_atomic_fetch_add(&bucket[b >> 1], 1u << sh[d], __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         // (the claimed slots are read only once every claim of this turn is issued)
@@ -1112,8 +1145,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
             [&](int i) { return i < RC ? (uint32_t)(64 * i) < c_w : (uint32_t)((i - RC) * NT) < pooled; },
             c_gt, (uint32_t)m, ties, bucket_of,
             [&](uint32_t slot, uint32_t pos, uint32_t bits) {
-                r.oidx[slot] = (int32_t)pos;
-                if (r.oval) r.oval[slot] = bits;
+                store_at(r.oidx, slot, (int32_t)pos);
+                if (r.oval) store_at(r.oval, slot, bits);
             },
             scattered))
         return false;
