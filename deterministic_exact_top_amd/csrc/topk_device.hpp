@@ -712,6 +712,19 @@ __device__ __forceinline__ void visit_slots(const uint32_t (&u)[EPT], int32_t nt
     }
 }
 
+// The least key of a tile's nt elements, exact (the same value in every thread).  word:
+// an LDS word that is zero, with a barrier behind, on entry (it collects the maximum of
+// ~key).  Contains a barrier.
+template <int NT, int EPT>
+__device__ __forceinline__ uint32_t tile_min_key(const uint32_t (&u)[EPT], int32_t nt, uint32_t* word) {
+    uint32_t nk = 0;
+    visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) { nk = ok ? max(nk, ~key_of(x)) : nk; });
+    nk = wave_max(nk);
+    if ((opaque_tid() & 63) == 0) __hip_atomic_fetch_max(word, nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+    return ~__builtin_amdgcn_readfirstlane(*word);
+}
+
 // Keys above P, compared on the raw bits when P >= key(+0.0) (then only non-negative
 // patterns qualify and their signed order is the key order).
 struct AboveP {
@@ -999,8 +1012,16 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     {
         // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
         const uint32_t rr = fast_mode == 2 ? 1u : pivot_rank(nsamp, m, nt);
-        if (m < nt && rr < (uint32_t)nsamp)
+        if (m < nt && rr < (uint32_t)nsamp) {
             P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {}, &passes, s.ctl + kCtlSel);
+        } else if (m == nt && fast_mode != 2) {
+            // The whole row is output: pivot on its least key, taken exactly.  No key lies
+            // below it, so the keys equal to it are the tail, in index order from the
+            // bitmap; a plateau at the bottom of a short row then costs a bitmap scan
+            // instead of a sort of one long bucket.  (Least key 0: no pivot.)
+            P = tile_min_key<NT, EPT>(u, nt, s.ctl + kCtlSel);
+            passes = P ? 4 : 0;
+        }
     }
     // The least sample above P starts the bucket range when P may sit far below the kept
     // keys: P = 0 (no pivot) or P exactly a sample's key (a plateau of equal scores, four
@@ -1239,7 +1260,11 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
     uint32_t P = 0;
     {
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
-        if (rr < (uint32_t)nsamp) {
+        if (m == n && ntiles == 1 && p.fast != 2) {
+            // The whole row is output (and fits this tile): pivot on its least key, exact;
+            // the keys equal to it fill the tail in index order (see fast_tile).
+            P = tile_min_key<NT, EPT>(u, nt, s.ctl + kCtlSel);
+        } else if (rr < (uint32_t)nsamp) {
             uint32_t* gsamp = rw + kRowSampHist;
             P = pivot_passes<NT, 4>(sk, rr, s.bucket, [&](int pass, uint32_t* h) {
                 if (tid < kRadix) {

@@ -200,3 +200,48 @@ def test_only_one_wave_has_candidates(dev):
     pw = _wave_positions(n, wave=0)
     r[pw] = (np.abs(rng.standard_normal(pw.size)) + 0.01).astype(np.float32)
     _check(dev, _dense([r, r.copy()], 2048, "one_wave"), "only one wave has candidates", path=1)
+
+
+def _bottom_family(rng, fam, n):
+    """Rows whose least key takes a particular form (every row here is output whole)."""
+    if fam == "zero_plateau":  # +0.0 on 80 % of the row, positive scores above it
+        return W.relu_sum_mixture(rng, n, 0.8)
+    if fam == "neg_inf_plateau":
+        r = rng.standard_normal(n).astype(np.float32)
+        r[rng.random(n) < 0.5] = np.float32(-np.inf)
+        return r
+    if fam == "neg_nan_bottom":  # negative NaNs order below -inf; two payloads
+        r = rng.standard_normal(n).astype(np.float32)
+        u = r.view(np.uint32)
+        pick = rng.random(n)
+        u[pick < 0.3] = np.uint32(0xFFC00123)
+        u[pick > 0.9] = np.uint32(0xFF800001)
+        return r
+    if fam == "unique_min":
+        return rng.standard_normal(n).astype(np.float32)
+    if fam == "constant":
+        return np.full(n, np.float32(-2.5), np.float32)
+    # the least possible key (bits 0xFFFFFFFF) present: no pivot is taken then
+    r = rng.standard_normal(n).astype(np.float32)
+    r.view(np.uint32)[rng.random(n) < 0.2] = np.uint32(0xFFFFFFFF)
+    return r
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+@pytest.mark.parametrize("fam", ["zero_plateau", "neg_inf_plateau", "neg_nan_bottom", "unique_min", "constant",
+                                 "least_key"])
+def test_whole_row_outputs(dev, shape, fam):
+    """Rows no longer than k (every element is output): the pivot is the row's least key,
+    and the keys equal to it fill the tail in index order.  Row lengths from 1 to k, and
+    one row longer than k for contrast."""
+    rng = np.random.default_rng(len(fam) * 31 + len(shape))
+    rows = [_bottom_family(rng, fam, n) for n in (1, 2, 7, 64, 1500, 2047, 2048, 2100)]
+    _check(dev, _dense(rows, 2048, "whole_" + fam), "whole-row outputs %s/%s" % (fam, shape), **SHAPES[shape])
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+def test_whole_row_outputs_k4096(dev, shape):
+    rng = np.random.default_rng(77)
+    rows = [_bottom_family(rng, f, n) for f, n in (("zero_plateau", 4096), ("neg_inf_plateau", 3000),
+                                                    ("neg_nan_bottom", 4095), ("unique_min", 1))]
+    _check(dev, _dense(rows, 4096, "whole_k4096"), "whole-row outputs k=4096/%s" % shape, **SHAPES[shape])
