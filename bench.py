@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -35,10 +36,15 @@ def log(msg):
 
 
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources with comments and whitespace taken out, so that a
+    comment edit does not mark counters taken on the same code as stale."""
     h = hashlib.sha256()
     for name in ("detk_api.hip", "topk_device.hpp"):
-        with open(os.path.join(ROOT, "deterministic_exact_top_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "deterministic_exact_top_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

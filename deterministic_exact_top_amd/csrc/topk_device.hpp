@@ -1039,7 +1039,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     // ------------------------------------------------ one pass: candidates (bits, position)
     // into per-wave regions of R slots, keys == P into the position bitmap when P is a
     // plateau value (then the tail may need them).  The running count is scalar and
-    // checked before each slot's stores: a slot that no longer fits its wave's region
+    // checked once per group of four slots: a slot that no longer fits its wave's region
     // claims slots in the shared pool after the regions instead (one LDS atomic per wave
     // and slot); only an exhausted pool sends the row to the exact path.  (Past the
     // pivot's last barrier no wave reads the sample histograms, so the regions may
