@@ -464,55 +464,68 @@ __device__ __forceinline__ uint32_t wave_select_digit(const uint32_t* hist, uint
     return __builtin_amdgcn_readlane(d, src);
 }
 
-// Descending bitonic sort of the composites of A[0..count) (count <= KMAX, a power of
-// two).  Padding entries get composite 0, which no real element has (~pos != 0).
-template <int NT>
-__device__ __forceinline__ void bitonic_desc(const PairList& A, int count) {
+// Orders one wave's LDS accesses: its earlier LDS writes are seen by its later LDS reads,
+// in any of its lanes.  LDS serves a wave's instructions in issue order, so this only has
+// to keep the compiler from moving accesses across it.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    asm volatile("" ::: "memory");
+}
+
+// A plain LDS array of composites, with PairList's accessors.
+struct U64List {
+    uint64_t* a;
+    __device__ __forceinline__ uint64_t composite(uint32_t i) const { return a[i]; }
+    __device__ __forceinline__ void set_composite(uint32_t i, uint64_t c) const { a[i] = c; }
+};
+
+// Descending bitonic sort of the composites of A[0..count) (count <= KMAX), padded to a
+// power of two P with composite 0, which no real element has (~pos != 0).
+// Pairs of a stage with stride s lie in aligned blocks of 2s elements, and thread i takes
+// the pair starting at 2i - (i mod s).  For s <= 64 the 64 threads of a wave (i in an
+// aligned run of 64, in every turn of the NT-strided loop) therefore cover one aligned
+// block of 128 elements that no other wave touches: such stages need only wave_lds_sync,
+// and a workgroup barrier is taken only where the next stage crosses waves.
+template <int NT, class List>
+__device__ __forceinline__ void bitonic_desc(const List& A, int count) {
+    static_assert(NT % 64 == 0, "whole waves");
     const int tid = opaque_tid();
     int P = 1;
     while (P < count) P <<= 1;
     for (int i = count + tid; i < P; i += NT) A.set_composite(i, 0);
     __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (P >> 1); i += NT) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const uint64_t a = A.composite(lo), b = A.composite(hi);
-                const bool desc = (lo & size) == 0;
-                if ((a < b) == desc) {
-                    A.set_composite(lo, b);
-                    A.set_composite(hi, a);
-                }
+    auto stage = [&](int size, int stride) {
+        for (int i = tid; i < (P >> 1); i += NT) {
+            const int lo = 2 * i - (i & (stride - 1));
+            const int hi = lo + stride;
+            const uint64_t a = A.composite(lo), b = A.composite(hi);
+            const bool desc = (lo & size) == 0;
+            if ((a < b) == desc) {
+                A.set_composite(lo, b);
+                A.set_composite(hi, a);
             }
+        }
+    };
+    for (int size = 2; size <= P; size <<= 1) {
+        int stride = size >> 1;
+        for (; stride >= 128; stride >>= 1) {
+            stage(size, stride);
             __syncthreads();
         }
+        for (; stride > 0; stride >>= 1) {
+            stage(size, stride);
+            wave_lds_sync();
+        }
+        if (size >= 128 || size == P) __syncthreads();  // the next stage (stride = size) crosses waves, or done
     }
 }
 
 // The same on a plain array of composites.
 template <int NT>
 __device__ __forceinline__ void bitonic_desc_u64(uint64_t* A, int count) {
-    const int tid = opaque_tid();
-    int P = 1;
-    while (P < count) P <<= 1;
-    for (int i = count + tid; i < P; i += NT) A[i] = 0;
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (P >> 1); i += NT) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const uint64_t a = A[lo], b = A[hi];
-                const bool desc = (lo & size) == 0;
-                if ((a < b) == desc) {
-                    A[lo] = b;
-                    A[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    bitonic_desc<NT>(U64List{A}, count);
 }
 
 // base[i] = v, addressed as a 32-bit byte offset from the (wave-uniform) row base, which
