@@ -224,6 +224,26 @@ def test_edge_lengths(dev, path):
 
 
 @pytest.mark.parametrize("path", [1, 2])
+def test_whole_rows_every_sort_size(dev, path):
+    """Rows output whole (n <= k) through the exact path, whose final order comes from the
+    bitonic sort of all n composites: every n from 1 to 130 and n around each power of two
+    up to 4096, so the sort runs with every padded size, with stages inside one wave only
+    and with stages that cross waves."""
+    k = 4096
+    L = 4096
+    lens = list(range(1, 131))
+    for e in range(8, 13):
+        lens += [(1 << e) - 1, 1 << e, (1 << e) + 1]
+    lens = [n for n in lens if n <= L]
+    wl = _edge_workload(L, k, lens, "whole_rows_sort_sizes")
+    log("whole rows, every sort size, path %d, B=%d" % (path, wl.B))
+    with debug_overrides(path=path, multi_tile=4096, fast=0):
+        gi, gv = run_gpu(wl, dev)
+    oi, ov = run_oracle(wl)
+    assert_same(gi, gv, oi, ov, "whole rows sort sizes path %d" % path)
+
+
+@pytest.mark.parametrize("path", [1, 2])
 def test_unaligned_packed_rows(dev, path):
     rng = np.random.default_rng(77)
     lens = rng.integers(0, 9000, 40).astype(np.int32)
