@@ -31,6 +31,27 @@ MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
+# Figures the pages report for other systems on other hardware.  They are carried beside
+# the measurement as context only: none of them is this metric on this workload.
+PAGES_CONTEXT = {
+    "note": "other hardware and other systems; context, not a baseline for this metric",
+    "qsa_prefill_tok_per_s_gb10": {
+        "stock_racy_topk": 2360,
+        "torch_topk_plus_canonical_sort": 1760,
+        "hardware": "NVIDIA GB10 (DGX Spark)",
+        "source": "docai.hu, Non-deterministic Qwen3.8-Flash-Next: summary; The price of the fix",
+    },
+    "flashinfer_filtered_topk_shared_mem_bytes": {
+        "value": 131072, "k_max": 2048,
+        "source": "vLLM PR #55872, GB10 failure trace and shared-memory comment",
+    },
+    "cutedsl_deterministic_topk_envelope": {
+        "topk_max": 4096, "row_len_below": 2 ** 24,
+        "source": "SGLang PR #31115, hardening commit",
+    },
+}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -333,6 +354,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(wl)
+    result["pages_context"] = PAGES_CONTEXT
     print(json.dumps(result))
 
 
