@@ -278,8 +278,10 @@ def copy_probe(nbytes: int, reps: int) -> None:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 200 untimed calls (about 25 ms of GPU work on the prefill workload) bring the GPU to
+    # its steady clocks; with 5, the timed calls ran about 15 % slower while it ramped.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefill_causal_8192x16384")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies cycled per step (0: enough to exceed the 256 MB MALL)")
