@@ -17,11 +17,13 @@ import ctypes
 import os
 
 __all__ = [
-    "topk_ragged", "workspace_size", "can_implement", "status_string", "debug_set",
-    "workspace_error", "library_path", "load_library", "DETK_MAX_K", "DetkError",
+    "topk_ragged", "workspace_size", "new_workspace", "can_implement", "status_string", "debug_set",
+    "library_path", "load_library", "DETK_MAX_K", "DETK_MAX_LEN", "DetkError",
 ]
 
 DETK_MAX_K = 4096
+DETK_MAX_LEN = 1 << 30
+DETK_WORKSPACE_UNSUPPORTED = (1 << 64) - 1  # SIZE_MAX: the configuration cannot run
 DETK_OK, DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, DETK_ERR_WORKSPACE, DETK_ERR_HIP = range(5)
 DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE, DETK_DEBUG_FAST = 1, 2, 3, 4
 
@@ -58,8 +60,6 @@ def load_library():
     lib.detk_topk_ragged.restype = ctypes.c_int
     lib.detk_status_string.argtypes = [ctypes.c_int]
     lib.detk_status_string.restype = ctypes.c_char_p
-    lib.detk_workspace_error.argtypes = [vp, sz, vp]
-    lib.detk_workspace_error.restype = ctypes.c_int
     lib.detk_debug_set.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.detk_read_probe.argtypes = [vp, sz, vp, vp]
     lib.detk_read_probe.restype = ctypes.c_int
@@ -77,7 +77,23 @@ def can_implement(k: int, max_len: int, device: int = 0) -> int:
 
 
 def workspace_size(B: int, k: int, max_len: int, device: int = 0) -> int:
-    return int(load_library().detk_workspace_size(int(device), int(B), int(k), int(max_len)))
+    """Bytes of workspace a call needs (0: none).  Raises DetkError when the configuration
+    cannot run (the library answers SIZE_MAX then)."""
+    need = int(load_library().detk_workspace_size(int(device), int(B), int(k), int(max_len)))
+    if need == DETK_WORKSPACE_UNSUPPORTED:
+        raise DetkError(can_implement(k, max_len, device) or DETK_ERR_UNSUPPORTED, "detk_workspace_size")
+    return need
+
+
+def new_workspace(B: int, k: int, max_len: int, device):
+    """A zero-filled uint8 CUDA tensor of the size a call with these sizes needs (at least
+    one byte).  The library requires a workspace to be zero-filled before its first use
+    and leaves it zero-filled after every call, so one allocated here is reused as is,
+    by calls of any shape that fits it."""
+    import torch
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    return torch.zeros(max(workspace_size(B, k, max_len, idx), 1), dtype=torch.uint8, device=dev)
 
 
 def debug_set(what: int, value: int) -> None:
@@ -106,14 +122,6 @@ def read_probe(data, out, stream=None) -> None:
         raise DetkError(st, "detk_read_probe")
 
 
-def workspace_error(workspace, stream=None) -> int:
-    import torch
-    if workspace is None or workspace.numel() == 0:
-        return 0
-    s = stream if stream is not None else torch.cuda.current_stream(workspace.device)
-    return int(load_library().detk_workspace_error(_ptr(workspace), workspace.numel(), ctypes.c_void_p(s.cuda_stream)))
-
-
 def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: int | None = None,
                 out_idx=None, out_val=None, workspace=None, with_values: bool = True, B: int | None = None,
                 stream=None):
@@ -126,6 +134,8 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
     lengths     int32 CUDA tensor (B,), or None (every row max_len long).
     k           1 <= k <= 4096.
     max_len     host-known bound on every row length (never read from the device).
+    workspace   uint8 CUDA tensor from new_workspace() (zero-filled before its first use;
+                every call leaves it zero-filled), or None to allocate one here.
     Returns (out_idx int32 (B, k), out_val float32 (B, k) or None).  All allocation
     happens here, before the call, so a captured graph can reuse preallocated
     out_idx / out_val / workspace passed in by the caller.
@@ -158,10 +168,10 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
         out_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
     if with_values and out_val is None:
         out_val = torch.empty((B, k), dtype=torch.float32, device=dev)
-    need = lib.detk_workspace_size(dev.index if dev.index is not None else torch.cuda.current_device(),
-                                   int(B), int(k), int(max_len))
+    need = workspace_size(B, k, max_len, dev.index if dev.index is not None else torch.cuda.current_device())
     if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        # (zero-filled: the library needs a workspace zeroed before its first use)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     st = lib.detk_topk_ragged(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len), int(k),
                               _ptr(out_idx), _ptr(out_val) if with_values else None,

@@ -19,30 +19,33 @@ using detk::SmemAll;
 
 // Workgroup tile shapes (elements = threads x elements per lane).  Tiles keep the row in
 // VGPRs; MINW is the waves per SIMD their register allocation must allow.
-//   one workgroup per row: 4096 = 256 x 16, 8192 = 512 x 16, 16384 = 512 x 32,
-//                          32768 = 1024 x 32
-//   several per row:       4096 = 256 x 16, 8192 = 512 x 16, 16384 = 512 x 32,
-//                          32768 = 1024 x 32
+//   one workgroup per row (rows up to 32768): 4096 = 256 x 16, 8192 = 512 x 16,
+//     16384 = 512 x 32 (four rows per CU), 32768 = 1024 x 32
+//   rows split over workgroups: 4096 = 256 x 16, 8192 = 1024 x 8, 16384 = 1024 x 16
+//     (default), 32768 = 1024 x 32; 1024 threads wherever the tile allows, for the
+//     last arriving workgroup, which orders the whole row's candidates
 constexpr int kSingleMaxLen = 32768;
+constexpr int kSplitTile = 16384;
 
-template <int TILE> struct Shape;
-template <> struct Shape<4096> { static constexpr int NT = 256, EPT = 16, MINW = 2, MINW_MULTI = 2; };
-template <> struct Shape<8192> { static constexpr int NT = 512, EPT = 16, MINW = 4, MINW_MULTI = 4; };
-template <> struct Shape<16384> { static constexpr int NT = 512, EPT = 32, MINW = 8, MINW_MULTI = 4; };
-template <> struct Shape<32768> { static constexpr int NT = 1024, EPT = 32, MINW = 4, MINW_MULTI = 4; };
-
-template <int TILE, bool MULTI>
-constexpr int min_waves() { return MULTI ? Shape<TILE>::MINW_MULTI : Shape<TILE>::MINW; }
+template <int TILE, bool MULTI> struct Shape;
+template <> struct Shape<4096, false> { static constexpr int NT = 256, EPT = 16, MINW = 2; };
+template <> struct Shape<8192, false> { static constexpr int NT = 512, EPT = 16, MINW = 4; };
+template <> struct Shape<16384, false> { static constexpr int NT = 512, EPT = 32, MINW = 8; };
+template <> struct Shape<32768, false> { static constexpr int NT = 1024, EPT = 32, MINW = 4; };
+template <> struct Shape<4096, true> { static constexpr int NT = 256, EPT = 16, MINW = 2; };
+template <> struct Shape<8192, true> { static constexpr int NT = 1024, EPT = 8, MINW = 4; };
+template <> struct Shape<16384, true> { static constexpr int NT = 1024, EPT = 16, MINW = 4; };
+template <> struct Shape<32768, true> { static constexpr int NT = 1024, EPT = 32, MINW = 4; };
 
 template <int TILE, int KMAX, bool MULTI>
 const void* kernel_ptr() {
-    using S = Shape<TILE>;
-    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, MULTI>()>);
+    using S = Shape<TILE, MULTI>;
+    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>);
 }
 
 template <int TILE, int KMAX, bool MULTI>
 constexpr size_t smem_bytes() {
-    return sizeof(SmemAll<Shape<TILE>::NT, Shape<TILE>::EPT, KMAX, MULTI>);
+    return sizeof(SmemAll<Shape<TILE, MULTI>::NT, Shape<TILE, MULTI>::EPT, KMAX, MULTI>);
 }
 
 struct DeviceInfo {
@@ -50,7 +53,7 @@ struct DeviceInfo {
     bool gfx950 = false;
     int cus = 0;
     size_t max_lds = 0;
-    int multi_occ[4][2] = {};   // [tile index][kmax index] co-resident workgroups per CU
+    int split_occ[2] = {};  // workgroups per CU of the 16K-element split tile, k <= 2048 / k <= 4096
 };
 
 std::mutex g_mu;
@@ -66,23 +69,22 @@ hipError_t prepare_kernel() {
                                (int)smem_bytes<TILE, KMAX, MULTI>());
 }
 
-template <int TILE, int KMAX, bool MULTI>
-int occupancy() {
-    if (prepare_kernel<TILE, KMAX, MULTI>() != hipSuccess) return 0;
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel_ptr<TILE, KMAX, MULTI>(), Shape<TILE>::NT,
-                                                     smem_bytes<TILE, KMAX, MULTI>()) != hipSuccess)
-        return 0;
-    return blocks;
-}
-template <int TILE, int KMAX>
-int multi_occupancy() { return occupancy<TILE, KMAX, true>(); }
-
 template <int TILE>
-void prepare_both(hipError_t* e) {
+void prepare_all(hipError_t* e) {
     hipError_t r;
     if ((r = prepare_kernel<TILE, 2048, false>()) != hipSuccess) *e = r;
     if ((r = prepare_kernel<TILE, 4096, false>()) != hipSuccess) *e = r;
+    if ((r = prepare_kernel<TILE, 2048, true>()) != hipSuccess) *e = r;
+    if ((r = prepare_kernel<TILE, 4096, true>()) != hipSuccess) *e = r;
+}
+
+template <int TILE, int KMAX>
+int split_occupancy() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel_ptr<TILE, KMAX, true>(), Shape<TILE, true>::NT,
+                                                     smem_bytes<TILE, KMAX, true>()) != hipSuccess)
+        return 0;
+    return blocks;
 }
 
 int device_info(int device, DeviceInfo* out) {
@@ -99,18 +101,12 @@ int device_info(int device, DeviceInfo* out) {
             d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
             d.cus = prop.multiProcessorCount;
             d.max_lds = prop.sharedMemPerBlock;
-            d.multi_occ[0][0] = multi_occupancy<4096, 2048>();
-            d.multi_occ[0][1] = multi_occupancy<4096, 4096>();
-            d.multi_occ[1][0] = multi_occupancy<8192, 2048>();
-            d.multi_occ[1][1] = multi_occupancy<8192, 4096>();
-            d.multi_occ[2][0] = multi_occupancy<16384, 2048>();
-            d.multi_occ[2][1] = multi_occupancy<16384, 4096>();
-            d.multi_occ[3][0] = multi_occupancy<32768, 2048>();
-            d.multi_occ[3][1] = multi_occupancy<32768, 4096>();
-            prepare_both<4096>(&e);
-            prepare_both<8192>(&e);
-            prepare_both<16384>(&e);
-            prepare_both<32768>(&e);
+            prepare_all<4096>(&e);
+            prepare_all<8192>(&e);
+            prepare_all<16384>(&e);
+            prepare_all<32768>(&e);
+            d.split_occ[0] = split_occupancy<kSplitTile, 2048>();
+            d.split_occ[1] = split_occupancy<kSplitTile, 4096>();
         }
         if (cur != device) (void)hipSetDevice(cur);
         if (e != hipSuccess) return DETK_ERR_HIP;
@@ -129,7 +125,7 @@ struct Plan {
     size_t lds = 0;
     size_t ws_bytes = 0;
     // workspace layout (bytes from the start)
-    size_t off_zero = 0, n_zero_words = 0, off_ecnt = 0, off_stage = 0, off_cand = 0;
+    size_t off_ctl = 0, off_ecnt = 0, off_cand = 0, off_tie = 0;
 };
 
 template <bool MULTI>
@@ -144,15 +140,20 @@ size_t lds_bytes_t(int tile, int kmax) {
 }
 size_t lds_bytes(int tile, int kmax, bool multi) { return multi ? lds_bytes_t<true>(tile, kmax) : lds_bytes_t<false>(tile, kmax); }
 
-int tile_index(int tile) { return tile == 4096 ? 0 : tile == 8192 ? 1 : tile == 16384 ? 2 : 3; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Most workgroups launched for the split-row kernel; more items are taken by a grid-stride
+// loop (the items never wait for one another, so any number may be resident).
+constexpr int64_t kMaxSplitGrid = 65536;
 
 // Decide the launch shape from host-known sizes only.
 int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
     if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
-    if (k > DETK_MAX_K) return DETK_ERR_UNSUPPORTED;
+    if (k > DETK_MAX_K || max_len > DETK_MAX_LEN) return DETK_ERR_UNSUPPORTED;
     if (!dev.gfx950) return DETK_ERR_UNSUPPORTED;
+    // int32 output offsets: b * k + t must be addressable.
+    if ((int64_t)B * k >= ((int64_t)1 << 31)) return DETK_ERR_UNSUPPORTED;
     pl->kmax = k <= 2048 ? 2048 : 4096;
-    const int ki = pl->kmax == 2048 ? 0 : 1;
 
     bool multi;
     if (g_force_path == 1) {
@@ -161,8 +162,7 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
     } else if (g_force_path == 2) {
         multi = true;
     } else {
-        // One workgroup per row whenever the row fits one tile (splitting a row costs row
-        // barriers, which outweigh the extra parallelism even for small batches).
+        // One workgroup per row whenever the row fits one tile.
         multi = max_len > kSingleMaxLen;
     }
     pl->multi = multi;
@@ -172,42 +172,37 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         pl->grid = B;  // one workgroup per row: the dispatcher balances rows of unequal length
         pl->ws_bytes = 0;
     } else {
-        pl->tile = g_multi_tile ? g_multi_tile : 32768;  // fewest tiles per row: fewest barrier arrivals
+        // 16K-element tiles spread a row over more CUs; when a batch has more of them than
+        // the GPU holds at once, 32K-element tiles (half as many workgroups, each ordering
+        // nothing more) finish in fewer rounds.
+        const int64_t tpr16 = ((int64_t)max_len + kSplitTile - 1) / kSplitTile;
+        const int64_t resident = (int64_t)dev.cus * dev.split_occ[pl->kmax == 2048 ? 0 : 1];
+        pl->tile = g_multi_tile ? g_multi_tile : ((int64_t)B * tpr16 <= resident ? kSplitTile : 2 * kSplitTile);
         const int64_t tpr = max_len == 0 ? 1 : ((int64_t)max_len + pl->tile - 1) / pl->tile;
-        const int occ = dev.multi_occ[tile_index(pl->tile)][ki];
-        const int64_t capacity = (int64_t)occ * dev.cus;
-        if (occ <= 0 || tpr > capacity) return DETK_ERR_UNSUPPORTED;
         pl->tiles_per_row = (int)tpr;
         const int64_t items = (int64_t)B * tpr;
-        const int64_t rows_resident = capacity / tpr;
-        int64_t grid = rows_resident * tpr;
-        if (grid > items) grid = items;
-        pl->grid = (int)grid;
-        pl->n_zero_words = 1 + (size_t)B * detk::kRowZeroWords;
-        pl->off_zero = 0;
-        size_t off = pl->n_zero_words * 4;
-        off = (off + 255) & ~(size_t)255;
+        pl->grid = (int)(items < kMaxSplitGrid ? items : kMaxSplitGrid);
+        const size_t cap = pl->kmax == 2048 ? detk::cand_cap<2048>() : detk::cand_cap<4096>();
+        size_t off = 0;
+        pl->off_ctl = off;
+        off = align256(off + (size_t)B * detk::kRowCtlWords * 4);
         pl->off_ecnt = off;
-        off += (size_t)B * (size_t)tpr * 4;
-        off = (off + 255) & ~(size_t)255;
-        pl->off_stage = off;
-        off += (size_t)B * (size_t)k * 8;
-        off = (off + 255) & ~(size_t)255;
+        off = align256(off + (size_t)B * (size_t)tpr * 4);
         pl->off_cand = off;
-        off += (size_t)B * (size_t)(pl->kmax == 2048 ? detk::cand_cap<2048>() : detk::cand_cap<4096>()) * 8;
+        off = align256(off + (size_t)B * cap * 8);
+        pl->off_tie = off;
+        off = align256(off + (size_t)B * (size_t)tpr * (size_t)(pl->tile / 32) * 4);
         pl->ws_bytes = off;
     }
     pl->lds = lds_bytes(pl->tile, pl->kmax, pl->multi);
     if (pl->lds > dev.max_lds) return DETK_ERR_UNSUPPORTED;
-    // int32 offsets: every window must be addressable with int32 row_starts + length.
-    if ((int64_t)B * k >= ((int64_t)1 << 31)) return DETK_ERR_UNSUPPORTED;
     return DETK_OK;
 }
 
 template <int TILE, int KMAX, bool MULTI>
 hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
-    using S = Shape<TILE>;
-    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, MULTI>()>), dim3(grid), dim3(S::NT), lds,
+    using S = Shape<TILE, MULTI>;
+    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>), dim3(grid), dim3(S::NT), lds,
                        stream, p);
     return hipGetLastError();
 }
@@ -274,9 +269,9 @@ int detk_can_implement(int device, int k, int32_t max_len) {
 
 size_t detk_workspace_size(int device, int B, int k, int32_t max_len) {
     DeviceInfo dev;
-    if (device_info(device, &dev) != DETK_OK) return 0;
+    if (device_info(device, &dev) != DETK_OK) return DETK_WORKSPACE_UNSUPPORTED;
     Plan pl;
-    if (make_plan(dev, B, k, max_len, &pl) != DETK_OK) return 0;
+    if (make_plan(dev, B, k, max_len, &pl) != DETK_OK) return DETK_WORKSPACE_UNSUPPORTED;
     return B == 0 ? 0 : pl.ws_bytes;
 }
 
@@ -285,7 +280,7 @@ int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32
                      size_t workspace_bytes, void* stream_ptr) {
     if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
     if (B > 0 && (!scores || !out_idx)) return DETK_ERR_INVALID_ARG;
-    if (k > DETK_MAX_K) return DETK_ERR_UNSUPPORTED;
+    if (k > DETK_MAX_K || max_len > DETK_MAX_LEN) return DETK_ERR_UNSUPPORTED;
     if (B == 0) return DETK_OK;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return DETK_ERR_HIP;
@@ -310,21 +305,16 @@ int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32
     p.fast = g_fast;
     p.out_idx = out_idx;
     p.out_val = reinterpret_cast<uint32_t*>(out_val);
-    p.ws_zero = nullptr;
+    p.ws_ctl = nullptr;
     p.ws_ecnt = nullptr;
-    p.ws_stage = nullptr;
     p.ws_cand = nullptr;
+    p.ws_tie = nullptr;
     if (pl.multi) {
         unsigned char* ws = static_cast<unsigned char*>(workspace);
-        p.ws_zero = reinterpret_cast<uint32_t*>(ws + pl.off_zero);
+        p.ws_ctl = reinterpret_cast<uint32_t*>(ws + pl.off_ctl);
         p.ws_ecnt = reinterpret_cast<uint32_t*>(ws + pl.off_ecnt);
-        p.ws_stage = reinterpret_cast<uint64_t*>(ws + pl.off_stage);
         p.ws_cand = reinterpret_cast<uint2*>(ws + pl.off_cand);
-        const int64_t nz = (int64_t)pl.n_zero_words;
-        int zgrid = (int)((nz + 255) / 256);
-        if (zgrid > 1024) zgrid = 1024;
-        hipLaunchKernelGGL(detk::zero_words_kernel, dim3(zgrid), dim3(256), 0, stream, p.ws_zero, nz);
-        if (hipGetLastError() != hipSuccess) return DETK_ERR_HIP;
+        p.ws_tie = reinterpret_cast<uint32_t*>(ws + pl.off_tie);
     }
     if (dispatch(pl, p, stream) != hipSuccess) return DETK_ERR_HIP;
     return DETK_OK;
@@ -333,23 +323,16 @@ int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32
 const char* detk_status_string(int status) {
     switch (status) {
     case DETK_OK: return "DETK_OK";
-    case DETK_ERR_INVALID_ARG: return "DETK_ERR_INVALID_ARG: null pointer, B < 0, k < 1 or max_len < 0";
+    case DETK_ERR_INVALID_ARG:
+        return "DETK_ERR_INVALID_ARG: a required pointer is NULL, or B < 0, k < 1 or max_len < 0";
     case DETK_ERR_UNSUPPORTED:
-        return "DETK_ERR_UNSUPPORTED: k > 4096, device is not gfx950, or the row is too long for the "
-               "co-resident multi-workgroup path";
-    case DETK_ERR_WORKSPACE: return "DETK_ERR_WORKSPACE: workspace missing or smaller than detk_workspace_size()";
+        return "DETK_ERR_UNSUPPORTED: k > 4096, max_len > 2^30, B * k >= 2^31, or the device is not gfx950";
+    case DETK_ERR_WORKSPACE:
+        return "DETK_ERR_WORKSPACE: workspace missing or smaller than detk_workspace_size() (it must also be "
+               "zero-filled before its first use)";
     case DETK_ERR_HIP: return "DETK_ERR_HIP: a HIP runtime call or kernel launch failed";
     default: return "unknown detk status";
     }
-}
-
-int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* stream_ptr) {
-    if (!workspace || workspace_bytes < 4) return 0;
-    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-    if (hipStreamSynchronize(stream) != hipSuccess) return -1;
-    uint32_t word = 0;
-    if (hipMemcpy(&word, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
-    return (int)word;
 }
 
 int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream_ptr) {

@@ -54,23 +54,17 @@ constexpr int kRankUnroll = 4;                  // composites compared per turn 
 template <bool LIMITED>
 constexpr int rank_pad() { return (LIMITED ? kBucketLimit : kBucketLimitRow) + kRankUnroll; }
 static_assert(kBuckets / 2 >= 4 * 256, "the packed bucket array doubles as the sample histograms");
+constexpr uint32_t pow2_floor(uint32_t x) { return x < 2 ? x : 2 * pow2_floor(x / 2); }
 constexpr int kSamplesPerLane = 2;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
-// Per-row workspace words of the multi-workgroup path, zeroed before each launch.
-constexpr int kRowHist = 0;                     // exact path: 4 pass histograms
-constexpr int kRowBar = 4 * kRadix;             // row barrier counter (both paths)
-constexpr int kRowArrive = kRowBar + 1;         // exact path: arrivals after staging
-constexpr int kRowStage = kRowBar + 2;          // exact path: staged composites
-constexpr int kRowSampHist = kRowBar + 4;       // pivot path: 4 sample-digit histograms
-constexpr int kRowFast = kRowSampHist + 4 * kRadix;  // pivot path control words:
-constexpr int kRowCgt = kRowFast + 0;           //   keys above P (claims candidate space)
-constexpr int kRowEq = kRowFast + 1;            //   keys equal to P
-constexpr int kRowNotLo = kRowFast + 2;         //   ~(least sample above P), by max
-constexpr int kRowUAll = kRowFast + 3;          //   largest sample
-constexpr int kRowUFin = kRowFast + 4;          //   largest sample below key(+inf)
-constexpr int kRowFastArrive = kRowFast + 5;    //   arrivals after writing candidates
-constexpr int kRowZeroWords = kRowFast + 12;
-constexpr uint32_t kSpinLimit = 1u << 21;       // bounded wait (polls, ~1 us each) at row barriers
+// Per-row control words of the split-row path (a row spread over several workgroups).
+// They are zero when a call starts, and the row's last arriving workgroup sets them back
+// to zero, so a workspace zero-filled once stays ready for every later call.
+constexpr int kRowCgt = 0;                      // candidates claimed (keys above P)
+constexpr int kRowEq = 1;                       // keys equal to P
+constexpr int kRowArrive = 2;                   // tiles done: the last to arrive orders the row
+constexpr int kRowCtlWords = 32;                // one 128-byte line per row
+constexpr int kSplitSamples = 8192;             // split rows: samples per row (4 per 16-byte load)
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer resource, gfx9-family data format
 
 struct Params {
@@ -80,15 +74,15 @@ struct Params {
     int32_t B;
     int32_t max_len;
     int32_t k;
-    int32_t tiles_per_row;      // multi path only
+    int32_t tiles_per_row;      // split-row kernel only
     int32_t stage_cap;          // <= kStageCap
-    int32_t fast;               // 1: try the pivot fast path on single-tile rows
+    int32_t fast;               // 1: try the pivot fast path first
     int32_t* out_idx;
     uint32_t* out_val;          // nullable
-    uint32_t* ws_zero;          // [0] error word, then B * kRowZeroWords (zeroed per call)
-    uint32_t* ws_ecnt;          // B * tiles_per_row
-    uint64_t* ws_stage;         // B * k
-    uint2* ws_cand;             // B * cand_cap(KMAX): pivot-path candidates (bits, position)
+    uint32_t* ws_ctl;           // B * kRowCtlWords, zero on entry and on exit
+    uint32_t* ws_ecnt;          // B * tiles_per_row: keys equal to P per tile
+    uint2* ws_cand;             // B * cand_cap(KMAX): candidates (bits, position in the row)
+    uint32_t* ws_tie;           // B * tiles_per_row * TILE / 32: per-tile bitmaps of keys == P
 };
 
 // ----------------------------------------------------------------------------- bits
@@ -183,6 +177,8 @@ __device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
 
 // Count one per active lane into h[d]; lanes sharing the first active lane's bin are
 // merged into one add.  Must be called from the lanes to count (divergence allowed).
+// (A second merge round, for the first lane outside that bin, measured slower: the extra
+// instructions cost more than the same-address atomics they save.)
 __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t d) {
     const uint32_t lead = __builtin_amdgcn_readfirstlane(d);
     const uint64_t same = __ballot(d == lead);
@@ -323,11 +319,11 @@ struct FastSmem {
     static_assert(sizeof(uint64_t) * SCAP >= sizeof(uint32_t) * 2 * kRadix, "S holds the sample histograms");
 };
 
-// Pivot path of a row split over several workgroups: candidates live in the workspace,
-// so LDS holds only the tile's tie bitmap, the buckets and the kept composites (the last
-// workgroup of the row ranks every candidate, so S takes the whole capacity).
+// A row split over several workgroups (one tile each): candidates live in the workspace,
+// so LDS holds only the tile's tie bitmap, the buckets (which first hold the sample-digit
+// histograms) and, in the row's last arriving workgroup, the kept composites it ranks.
 template <int NT, int EPT, int KMAX>
-struct MultiFastSmem {
+struct SplitSmem {
     static constexpr int TILE = NT * EPT;
     static constexpr int BWORDS = TILE / 32;
     static constexpr int SCAP = cand_cap<KMAX>();
@@ -338,23 +334,41 @@ struct MultiFastSmem {
     uint64_t S[SCAP + rank_pad<false>()];
 };
 
+// Exact radix select over a whole row read from global memory in chunks, by one
+// workgroup: the split row's fallback (its last arriving workgroup runs it alone).
+template <int NT, int KMAX, int STAGE>
+struct RowExactSmem {
+    static constexpr int NW = NT / 64;
+    static constexpr int STAGE_CAP = STAGE;
+    uint32_t whist[NW][kRadix];   // per-wave histograms
+    uint32_t hist[kRadix];        // merged histogram of the current pass
+    uint32_t wsum[32];
+    uint32_t sel[4];
+    uint32_t ctr[8];              // [0] staged, [1] A fill
+    uint32_t skey[STAGE];         // staged threshold-bin keys
+    uint32_t sidx[STAGE];         //   and their row positions
+    uint32_t akey[KMAX];          // selected elements above T: keys
+    uint32_t apos[KMAX];          //   and positions
+};
+
 struct NoSmem {};
 
 // Exact-path staging: smaller in one-workgroup-per-row kernels so that the LDS footprint
 // lets three rows share a CU, and four for the 16K-element tile (1,248 entries keep its
 // exact path at 40,880 bytes, the most that leaves room for four workgroups; more
 // survivors than that only fall back to a rescan).
-template <int NT, int EPT, bool MULTI>
-constexpr int stage_entries() { return MULTI ? 3072 : (NT == 512 && EPT == 32) ? 1248 : 2560; }
+template <int NT, int EPT>
+constexpr int stage_entries() { return (NT == 512 && EPT == 32) ? 1248 : 2560; }
+constexpr int kRowStageEntries = 3072;  // the whole-row exact fallback's staging
 
-// LDS of one workgroup: the exact path's, or the pivot path's of the kernel's kind (the
-// several-workgroups-per-row kernel takes its one-tile rows through the workspace
-// candidate list too, so its LDS never holds a whole candidate list).
+// LDS of one workgroup.  Both kernels hold the one-tile path (pivot path, exact fallback);
+// the split-row kernel also holds the split tile's and the whole-row fallback's layouts.
 template <int NT, int EPT, int KMAX, bool MULTI>
 union SmemAll {
-    ExactSmem<NT, EPT, KMAX, stage_entries<NT, EPT, MULTI>()> exact;
-    typename std::conditional<MULTI, NoSmem, FastSmem<NT, EPT, KMAX>>::type fast;
-    typename std::conditional<MULTI, MultiFastSmem<NT, EPT, KMAX>, NoSmem>::type mfast;
+    ExactSmem<NT, EPT, KMAX, stage_entries<NT, EPT>()> exact;
+    FastSmem<NT, EPT, KMAX> fast;
+    typename std::conditional<MULTI, SplitSmem<NT, EPT, KMAX>, NoSmem>::type split;
+    typename std::conditional<MULTI, RowExactSmem<NT, KMAX, kRowStageEntries>, NoSmem>::type rexact;
 };
 
 // ----------------------------------------------------------------------------- block helpers
@@ -544,7 +558,7 @@ __device__ __forceinline__ void write_padding(int32_t* oidx, uint32_t* oval, int
     }
 }
 
-// ----------------------------------------------------------------------------- row barrier
+// ----------------------------------------------------------------------------- row arrival
 
 // Wait until this wave's outstanding global stores and atomics have completed (reached
 // the L2, or memory for device-scope atomics), so that a release issued afterwards by
@@ -552,29 +566,22 @@ __device__ __forceinline__ void write_padding(int32_t* oidx, uint32_t* oval, int
 // for them.
 __device__ __forceinline__ void wait_global_writes() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Arrive at a row barrier and wait until `target` arrivals are counted.  Every wave
-// first waits for its own global writes; then one thread per workgroup talks to the
-// counter: a release add (one L2 write-back) makes the workgroup's global writes
-// visible device-wide, the wait polls with relaxed coherent loads (an acquire per poll
-// would invalidate the L2 each time), and one acquire fence after the wait makes the
-// other workgroups' writes visible.  The wait is bounded: past kSpinLimit polls it flags
-// `err` and returns.
-__device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+// One tile of a split row is done: count it on the row's ticket counter and return, in
+// every thread, whether this workgroup was the last of the row's `ntiles` to arrive.
+// Every wave first waits for its own global writes; then one thread adds one with
+// release semantics at device scope (the XCD's L2 is written back, so the workgroup's
+// writes reach the other XCDs) and acquire semantics (the last arriver then sees every
+// other tile's writes).  Nothing ever waits for another workgroup, so the launch needs
+// no co-residency and cannot stall.  flag: one LDS word.
+__device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t ntiles, uint32_t* flag) {
     wait_global_writes();
     __syncthreads();
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = old == ntiles - 1u ? 1u : 0u;
     }
     __syncthreads();
+    return *flag != 0u;
 }
 
 // ----------------------------------------------------------------------------- row context
@@ -583,7 +590,6 @@ struct RowCtx {
     int b, tile, ntiles;
     int32_t n, m, k, nt, j0;
     int64_t base;
-    bool multi;
     int32_t* oidx;
     uint32_t* oval;
 };
@@ -605,7 +611,7 @@ enum : int {
     kCtlSmaxFin = 10,   // largest sample key below key(+inf)
     kCtlBase = 11,      // several workgroups: this tile's first candidate slot in the row
     kCtlLast = 12,      // several workgroups: this tile arrived last
-    kCtlTieOff = 13,    // several workgroups: keys equal to P in earlier tiles
+    kCtlRowCgt = 13,    // several workgroups: the row's candidates (last arriver)
     kCtlPool = 15,      // one workgroup: slots claimed in the candidate pool
 };
 
@@ -658,8 +664,8 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 // over the row's tiles otherwise).  Every wave, and every workgroup of a row, takes the
 // same decisions.  With sel (three LDS words), wave 0 alone selects each digit and
 // publishes it behind one more barrier, instead of every wave repeating the selection.
-template <int NT, int NH, class Merge>
-__device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPerLane], uint32_t rr, uint32_t* hist,
+template <int NT, int NH, int SPL, class Merge>
+__device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[SPL], uint32_t rr, uint32_t* hist,
                                                  Merge&& merge, int* passes = nullptr, uint32_t* sel = nullptr) {
     const int tid = opaque_tid();
     uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
@@ -676,7 +682,7 @@ __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[kSamplesPe
         // (lanes sharing a bin merge into one atomic: scores concentrate on few digits,
         // and same-address LDS atomics serialise)
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i)
+        for (int i = 0; i < SPL; ++i)
             if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(h, (sk[i] >> shift) & 0xFFu);
         __syncthreads();
         merge(pass, h);
@@ -752,14 +758,29 @@ struct AboveP {
 
 // Bucket of a key: linear in the key over [L, U] (keys below L share bucket 0, keys
 // above U the top bucket); monotone, so bucket order never contradicts key order.
-struct BucketMap {
+// TOP (rows split over workgroups): keys of +inf and NaNs get the top kTopBuckets buckets
+// of their own -- +inf one, NaN payloads linear over the rest -- so a cluster of them
+// (equal bits are ranked against their whole bucket) is not one long bucket; the finite
+// keys share the others.
+constexpr int kTopBuckets = 64;
+template <bool TOP>
+struct BucketMapT {
+    static constexpr uint32_t NB = TOP ? kBuckets - kTopBuckets : kBuckets;  // buckets of finite keys
     uint32_t L;
     int sh;
-    __device__ BucketMap(uint32_t lo, uint32_t hi) : L(lo), sh(max(0, (32 - __clz(hi - lo)) - kBucketBits)) {}
+    __device__ BucketMapT(uint32_t lo, uint32_t hi) : L(lo), sh(max(0, (32 - __clz(hi - lo)) - kBucketBits)) {}
     __device__ __forceinline__ uint32_t operator()(uint32_t kx) const {
-        return min((max(kx, L) - L) >> sh, (uint32_t)(kBuckets - 1));
+        const uint32_t f = min((max(kx, L) - L) >> sh, NB - 1u);
+        if constexpr (!TOP) {
+            return f;
+        } else {
+            const uint32_t t =
+                NB + (kx == kKeyPosInf ? 0u : 1u + min((kx - kKeyPosInf - 1u) >> 17, (uint32_t)kTopBuckets - 2u));
+            return kx >= kKeyPosInf ? t : f;
+        }
     }
 };
+using BucketMap = BucketMapT<false>;
 // Count one key into the 16-bit bucket counters (bucket b lives in word b / 2, bits
 // 16 * (b % 2) and up).
 __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
@@ -791,11 +812,14 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // with its whole bucket).
 // bucket has kBuckets / 2 + 1 words (the last one is cleared here) and S has
 // SCAP + rank_pad<LIMITED>() entries (those past the kept ones are cleared here).
-template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Valid, class Live, class Emit,
-          class Scattered>
+// sort_long (LIMITED only): when a bucket is too long but at most SORT_MAX candidates are
+// kept, sort them instead of returning false (a row output whole keeps at most KMAX).
+template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Valid, class Live, class Map,
+          class Emit, class Scattered>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             Valid&& valid, Live&& live, uint32_t c_gt, uint32_t m, bool ties,
-                                            const BucketMap& bucket_of, Emit&& emit, Scattered&& scattered) {
+                                            const Map& bucket_of, Emit&& emit, Scattered&& scattered,
+                                            bool sort_long = false) {
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     const int tid = opaque_tid();
@@ -894,7 +918,10 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     const uint32_t bt = ties ? 0u : ctl[kCtlBt];
     const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
     const bool too_long = ctl[kCtlMaxBucket] != 0u;
-    if (LIMITED && (kept > (uint32_t)SCAP || too_long)) return false;  // uniform
+    // (the bitonic sort pads to a power of two, which must fit S)
+    constexpr uint32_t SORT_MAX = pow2_floor((uint32_t)(SCAP + rank_pad<LIMITED>()));
+    const bool sort_all = too_long && (!LIMITED || (sort_long && kept <= SORT_MAX));  // uniform
+    if (LIMITED && (kept > (uint32_t)SCAP || (too_long && !sort_all))) return false;  // uniform
 
     // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write).
     // A candidate that is not kept claims nothing: its claim word stays all ones, whose
@@ -928,7 +955,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     __syncthreads();
     scattered();  // past the point of falling back: the caller may reuse its registers
 
-    if (!LIMITED && too_long) {  // uniform
+    if (sort_all) {  // uniform
         static_assert(LIMITED || (SCAP & (SCAP - 1)) == 0, "the sort pads S to a power of two");
         bitonic_desc_u64<NT>(S, (int)kept);
         for (uint32_t q = tid; q < mlim; q += NT) emit(q, ~(uint32_t)S[q], bits_of((uint32_t)(S[q] >> 32)));
@@ -1182,7 +1209,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
                 store_at(r.oidx, slot, (int32_t)pos);
                 if (r.oval) store_at(r.oval, slot, bits);
             },
-            scattered))
+            scattered, m == nt))
         return false;
 
     // ------------------------------------------------ ties at P: smallest positions
@@ -1218,129 +1245,147 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     return true;
 }
 
-// Pivot path of a row split over several workgroups, one tile each (raw bits in u[]).
-// The tiles of a row meet at row barriers (bar_target counts them):
-//   - per sample digit, each tile adds its sample histogram into the row's and all tiles
-//     select the same digit, so every tile derives the same pivot P;
-//   - each tile counts its keys above and equal to P, claims space for its candidates in
-//     the row's workspace list and publishes its counts and sample extremes; after the
-//     barrier all tiles see the row's totals and take the same decision: fall back
-//     (returns false, registers untouched) when the list would overflow or fewer than m
-//     keys are >= P;
-//   - each tile writes its candidates (bits, row position) and, when keys equal to P
-//     fill the tail, the smallest-position ones straight to their output slots (its rank
-//     among them offset by the earlier tiles' counts);
-//   - the last tile to arrive orders the row's candidates (bucket_rank) into slots
-//     [0, min(m, candidates)).
+// Samples of a split row, the same in every tile of the row: 16-byte groups of 4
+// elements, evenly spread over the window.  The groups start at the window's first
+// 16-byte boundary (a0 = 0..3 elements in), so every load is an aligned 16-byte buffer
+// load and there is no alignment branch: the compiler counts the loads exactly, and the
+// pivot waits for them alone, not for the tile loads issued after them.  Lane t's g-th
+// group is group floor(q * G / (SL * NT)), q = g * NT + t, of the G = (n - a0) / 4 whole
+// groups (a row shorter than 4 * SL * NT elements repeats some, which only weakens the
+// pivot estimate).
+template <int NT, int SL>
+__device__ __forceinline__ void load_row_samples(uint32_t (&sk)[4 * SL], const uint32_t* row, int32_t n) {
+    const uint32_t a0 = ((16u - (uint32_t)((uintptr_t)row & 15u)) & 15u) >> 2;  // (rows start 4-byte aligned)
+    const uint32_t* base = row + a0;
+    const uint64_t groups = (uint64_t)((uint32_t)(n - (int32_t)a0) >> 2);
+    // (2^30 elements make 2^32 bytes: the range is clamped to 32 bits, and a sample group
+    // past it reads zeros, which only nudges the pivot estimate)
+    const uint64_t bytes = groups * 16u;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(base), (short)0, (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull),
+        kBufferWord3);
+    const uint32_t tid = (uint32_t)opaque_tid();
+#pragma unroll
+    for (int g = 0; g < SL; ++g) {
+        const uint32_t q = (uint32_t)g * NT + tid;
+        const uint32_t grp = (uint32_t)(((uint64_t)q * groups) / (uint64_t)(SL * NT));
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, grp * 16u, 0, 0);
+        sk[4 * g + 0] = v[0];
+        sk[4 * g + 1] = v[1];
+        sk[4 * g + 2] = v[2];
+        sk[4 * g + 3] = v[3];
+    }
+}
+
+template <int NT, int KMAX, int STAGE>
+__device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, uint32_t* oval,
+                          RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap);
+
+// One tile of a row split over several workgroups.  No workgroup ever waits for another:
+//   - every tile reads the same evenly spaced samples of the whole row and derives the
+//     same pivot P from them, as a one-tile row does from its own registers;
+//   - it counts its keys above and equal to P, claims room for its candidates in the
+//     row's workspace list with one atomic add and writes them there (raw bits, row
+//     position); when it holds keys equal to P it also stores its bitmap of their
+//     positions and their count;
+//   - it arrives at the row's ticket counter.  The last tile to arrive owns the row: it
+//     sets the row's counters back to zero, then orders the candidates when the list held
+//     them all and at least min(k, n) keys are >= P (keys equal to P fill the tail in
+//     index order, tile by tile), and otherwise selects the row exactly on its own.
 template <int NT, int EPT, int KMAX>
-__device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r, MultiFastSmem<NT, EPT, KMAX>& s,
-                                                const uint32_t (&u)[EPT], uint32_t& bar_target) {
-    using MS = MultiFastSmem<NT, EPT, KMAX>;
-    constexpr int BW = MS::BWORDS;
-    constexpr int TILE = MS::TILE;
-    constexpr uint32_t CAP = (uint32_t)MS::SCAP;
+__device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, SmemAll<NT, EPT, KMAX, true>& sa) {
+    using SS = SplitSmem<NT, EPT, KMAX>;
+    SS& s = sa.split;
+    constexpr int BW = SS::BWORDS;
+    constexpr int TILE = SS::TILE;
+    constexpr uint32_t CAP = (uint32_t)SS::SCAP;
+    constexpr int SL = kSplitSamples / (4 * NT);  // 16-byte sample loads per lane
+    static_assert(SL >= 1 && 4 * SL * NT == kSplitSamples, "whole sample groups per lane");
     const int tid = opaque_tid();
     const int lane = tid & 63;
     const int b = r.b, tile = r.tile, ntiles = r.ntiles;
     const int32_t nt = r.nt, m = r.m, n = r.n, j0 = r.j0;
-    uint32_t* rw = p.ws_zero + 1 + (int64_t)b * kRowZeroWords;
-    uint32_t* err = p.ws_zero;
-
-    // ------------------------------------------------ clear LDS state
-    block_zero<NT, BW>(s.bitmap);
-    block_zero<NT, 4 * kRadix>(s.bucket);  // the sample-digit histograms
-    if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
-
-    // ------------------------------------------------ sample -> pivot (row-wide)
-    uint32_t sk[kSamplesPerLane];
-    take_samples<NT, EPT>(u, nt, sk);
-    const int nsamp = (ntiles - 1) * tile_samples<NT, EPT>(TILE) + tile_samples<NT, EPT>(n - (ntiles - 1) * TILE);
-    {
-        uint32_t sa = 0, sf = 0;
-#pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) {
-            sa = max(sa, sk[i]);
-            sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
-        }
-        sa = wave_max(sa);
-        sf = wave_max(sf);
-        __syncthreads();
-        if (lane == 0) {
-            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxAll], sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-    }
+    const uint32_t* const row = p.scores + r.base;
+    uint32_t* const rw = p.ws_ctl + (int64_t)b * kRowCtlWords;
+    uint32_t* const ecnt = p.ws_ecnt + (int64_t)b * p.tiles_per_row;
     uint32_t P = 0;
-    {
-        const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
-        if (m == n && ntiles == 1 && p.fast != 2) {
-            // The whole row is output (and fits this tile): pivot on its least key, exact;
-            // the keys equal to it fill the tail in index order (see fast_tile).
-            P = tile_min_key<NT, EPT>(u, nt, s.ctl + kCtlSel);
-        } else if (rr < (uint32_t)nsamp) {
-            uint32_t* gsamp = rw + kRowSampHist;
-            P = pivot_passes<NT, 4>(sk, rr, s.bucket, [&](int pass, uint32_t* h) {
-                if (tid < kRadix) {
-                    const uint32_t c = h[tid];
-                    if (c) atomicAdd(&gsamp[pass * kRadix + tid], c);
-                }
-                bar_target += (uint32_t)ntiles;
-                row_barrier(&rw[kRowBar], bar_target, err);
-                if (tid < kRadix)
-                    h[tid] = __hip_atomic_load(&gsamp[pass * kRadix + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __syncthreads();
-            });
-        }
-    }
-    {
-        uint32_t lo = 0xFFFFFFFFu;
+
+    if (p.fast) {
+        uint32_t sk[4 * SL];
+        load_row_samples<NT, SL>(sk, row, n);  // (issued first: the pivot needs them first)
+        uint32_t u[EPT];
+        load_tile<NT, EPT>(u, row + j0, nt);
+
+        // ------------------------------------------------ pivot from the row's samples
+        block_zero<NT, 4 * kRadix>(s.bucket);  // the sample-digit histograms
+        if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
-        lo = wave_min(lo);
-        if (lane == 0) __hip_atomic_fetch_min(&s.ctl[kCtlLo], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    const AboveP ap(P);
+        for (int i = 0; i < 4 * SL; ++i) sk[i] = key_of(sk[i]);
+        {
+            uint32_t sx = 0, sf = 0;
+#pragma unroll
+            for (int i = 0; i < 4 * SL; ++i) {
+                sx = max(sx, sk[i]);
+                sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
+            }
+            sx = wave_max(sx);
+            sf = wave_max(sf);
+            __syncthreads();
+            if (lane == 0) {
+                __hip_atomic_fetch_max(&s.ctl[kCtlSmaxAll], sx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+        constexpr int nsamp = 4 * SL * NT;
+        // (fast == 2, a test setting, aims at the largest sample: the pivot misses.)
+        const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
+        if (rr < (uint32_t)nsamp) P = pivot_passes<NT, 4>(sk, rr, s.bucket, [](int, uint32_t*) {}, nullptr, s.ctl + kCtlSel);
+        {
+            uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+            for (int i = 0; i < 4 * SL; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
+            lo = wave_min(lo);
+            if (lane == 0) __hip_atomic_fetch_min(&s.ctl[kCtlLo], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        const AboveP ap(P);
 
-    // ------------------------------------------------ count, claim, publish
-    uint32_t cgt = 0, ceq = 0;
-    if (P >= 0x80000000u)
-        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
-            cgt += (ap.gt<true>(x) && ok) ? 1u : 0u;
-            ceq += (ap.eq<true>(x) && ok) ? 1u : 0u;
-        });
-    else
-        visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
-            cgt += (ap.gt<false>(x) && ok) ? 1u : 0u;
-            ceq += (ap.eq<false>(x) && ok) ? 1u : 0u;
-        });
-    uint32_t c_tile, e_tile;
-    uint32_t o = block_excl_scan<NT>(cgt, s.wsum, &c_tile);
-    (void)block_excl_scan<NT>(ceq, s.wsum + 16, &e_tile);
-    if (tid == 0) {
-        s.ctl[kCtlBase] = c_tile ? atomicAdd(&rw[kRowCgt], c_tile) : 0u;
-        if (e_tile) atomicAdd(&rw[kRowEq], e_tile);
-        __hip_atomic_store(&p.ws_ecnt[(int64_t)b * p.tiles_per_row + tile], e_tile, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        atomicMax(&rw[kRowNotLo], ~s.ctl[kCtlLo]);
-        atomicMax(&rw[kRowUAll], s.ctl[kCtlSmaxAll]);
-        atomicMax(&rw[kRowUFin], s.ctl[kCtlSmaxFin]);
-    }
-    bar_target += (uint32_t)ntiles;
-    row_barrier(&rw[kRowBar], bar_target, err);
-    const uint32_t c_gt = __hip_atomic_load(&rw[kRowCgt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t n_eq = __hip_atomic_load(&rw[kRowEq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c_gt > CAP || c_gt + n_eq < (uint32_t)m) return false;  // uniform across the row
-    const bool ties = c_gt < (uint32_t)m;
+        // ------------------------------------------------ count, claim
+        uint32_t cgt = 0, ceq = 0;
+        if (P >= 0x80000000u)
+            visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
+                cgt += (ap.gt<true>(x) && ok) ? 1u : 0u;
+                ceq += (ap.eq<true>(x) && ok) ? 1u : 0u;
+            });
+        else
+            visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int, int, bool ok, int) {
+                cgt += (ap.gt<false>(x) && ok) ? 1u : 0u;
+                ceq += (ap.eq<false>(x) && ok) ? 1u : 0u;
+            });
+        // (one scan for both counts: per-thread counts <= EPT and tile totals <= TILE < 2^16,
+        // so the two 16-bit halves never carry into each other)
+        uint32_t both;
+        uint32_t o = block_excl_scan<NT>(cgt | (ceq << 16), s.wsum, &both) & 0xFFFFu;
+        const uint32_t c_tile = both & 0xFFFFu, e_tile = both >> 16;
+        if (tid == 0) {
+            s.ctl[kCtlBase] = c_tile ? atomicAdd(&rw[kRowCgt], c_tile) : 0u;
+            if (e_tile) atomicAdd(&rw[kRowEq], e_tile);
+            ecnt[tile] = e_tile;
+        }
+        const bool mark = e_tile != 0;  // uniform
+        if (mark) block_zero<NT, BW>(s.bitmap);
+        __syncthreads();
+        const uint32_t base = s.ctl[kCtlBase];
+        const bool fits = base + c_tile <= CAP;  // uniform; otherwise the row falls back
 
-    // ------------------------------------------------ write candidates (+ tie bitmap)
-    {
-        uint2* gc = p.ws_cand + (int64_t)b * CAP + s.ctl[kCtlBase];
-        auto write_pass = [&](auto pos_tag, auto eq_tag) {
+        // ------------------------------------------------ write candidates (+ tie bitmap)
+        uint2* const gc = p.ws_cand + (int64_t)b * CAP + base;
+        auto write_pass = [&](auto pos_tag, auto eq_tag, auto cand_tag) {
             constexpr bool POS = decltype(pos_tag)::value;
             constexpr bool EQ = decltype(eq_tag)::value;
+            constexpr bool CAND = decltype(cand_tag)::value;
             uint32_t nib = 0;
             visit_slots<NT, EPT>(u, nt, [&](uint32_t x, int c, int v, bool ok, int t4) {
-                if (ap.gt<POS>(x) && ok) {
+                if (CAND && ap.gt<POS>(x) && ok) {
                     gc[o] = make_uint2(x, (uint32_t)(j0 + t4 + (v * NT * 4 + c)));
                     ++o;
                 }
@@ -1357,104 +1402,284 @@ __device__ __forceinline__ bool multi_fast_tile(const Params& p, const RowCtx& r
                 }
             });
         };
+        auto by_cand = [&](auto pos_tag, auto eq_tag) {
+            if (fits) write_pass(pos_tag, eq_tag, std::true_type{});
+            else if (decltype(eq_tag)::value) write_pass(pos_tag, eq_tag, std::false_type{});
+        };
         if (P >= 0x80000000u) {
-            if (ties) write_pass(std::true_type{}, std::true_type{});
-            else write_pass(std::true_type{}, std::false_type{});
+            if (mark) by_cand(std::true_type{}, std::true_type{});
+            else by_cand(std::true_type{}, std::false_type{});
         } else {
-            if (ties) write_pass(std::false_type{}, std::true_type{});
-            else write_pass(std::false_type{}, std::false_type{});
+            if (mark) by_cand(std::false_type{}, std::true_type{});
+            else by_cand(std::false_type{}, std::false_type{});
+        }
+        if (mark) {  // this tile's bitmap of keys == P, for the last arriver
+            __syncthreads();
+            uint32_t* const gt = p.ws_tie + ((int64_t)b * p.tiles_per_row + tile) * BW;
+            for (int w = tid; w < BW; w += NT) gt[w] = s.bitmap[w];
         }
     }
 
-    // ------------------------------------------------ ties at P: this tile's share
-    if (ties) {
-        if (tid == 0) {
-            uint32_t off = 0;
-            for (int t = 0; t < tile; ++t)
-                off += __hip_atomic_load(&p.ws_ecnt[(int64_t)b * p.tiles_per_row + t], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-            s.ctl[kCtlTieOff] = off;
-        }
-        __syncthreads();
-        const uint32_t need = (uint32_t)m - c_gt;
-        const uint32_t tie_off = s.ctl[kCtlTieOff];
-        if (tie_off < need) {
-            constexpr int WPT = (BW + NT - 1) / NT;
-            uint32_t tc = 0;
-#pragma unroll
-            for (int q = 0; q < WPT; ++q) {
-                const int w = tid * WPT + q;
-                if (w < BW) tc += (uint32_t)__popc(s.bitmap[w]);
-            }
-            uint32_t tot;
-            uint32_t rr = tie_off + block_excl_scan<NT>(tc, s.wsum, &tot);
-            const uint32_t vP = bits_of(P);
-#pragma unroll
-            for (int q = 0; q < WPT; ++q) {
-                const int w = tid * WPT + q;
-                if (w < BW) {
-                    uint32_t word = s.bitmap[w];
-                    while (word && rr < need) {
-                        const int bit = __ffs(word) - 1;
-                        word &= word - 1;
-                        r.oidx[c_gt + rr] = j0 + w * 32 + bit;
-                        if (r.oval) r.oval[c_gt + rr] = vP;
-                        ++rr;
-                    }
-                    rr += (uint32_t)__popc(word);
-                }
-            }
-        }
+    // ------------------------------------------------ arrive; the last tile owns the row
+    if (!arrive_last(&rw[kRowArrive], (uint32_t)ntiles, &s.ctl[kCtlLast])) return;
+    if (tid == 0) {
+        s.ctl[kCtlRowCgt] = __hip_atomic_load(&rw[kRowCgt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s.ctl[kCtlEq] = __hip_atomic_load(&rw[kRowEq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Every other tile has counted and arrived: the row's words are free for the next call.
+        __hip_atomic_store(&rw[kRowCgt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&rw[kRowEq], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&rw[kRowArrive], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-
-    // ------------------------------------------------ arrive; the last tile orders the row
-    wait_global_writes();
     __syncthreads();
-    if (tid == 0) {  // release this tile's candidates; the last arriver acquires all of them
-        const uint32_t old = __hip_atomic_fetch_add(&rw[kRowFastArrive], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s.ctl[kCtlLast] = old == (uint32_t)ntiles - 1u ? 1u : 0u;
+    const uint32_t c_gt = s.ctl[kCtlRowCgt];
+    const uint32_t n_eq = s.ctl[kCtlEq];
+    if (!p.fast || c_gt > CAP || c_gt + n_eq < (uint32_t)m) {  // uniform
+        __syncthreads();  // (the fallback's LDS overlays the words just read)
+        exact_row<NT, KMAX, kRowStageEntries>(row, n, m, r.k, r.oidx, r.oval, sa.rexact, p.stage_cap);
+        return;
     }
+    const bool ties = c_gt < (uint32_t)m;
     block_zero<NT, kBuckets / 2>(s.bucket);
     if (tid >= kCtlBt && tid <= kCtlMaxBucket) s.ctl[tid] = 0;
     __syncthreads();
-    if (s.ctl[kCtlLast] == 0) return true;
     uint32_t L, U;
-    bucket_range(P, ~__hip_atomic_load(&rw[kRowNotLo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                 __hip_atomic_load(&rw[kRowUAll], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                 __hip_atomic_load(&rw[kRowUFin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), &L, &U);
-    const uint2* gc = p.ws_cand + (int64_t)b * CAP;
-    bucket_rank<NT, MS::SCAP, (MS::SCAP + NT - 1) / NT, false, false>(
+    bucket_range(P, s.ctl[kCtlLo], s.ctl[kCtlSmaxAll], s.ctl[kCtlSmaxFin], &L, &U);
+    const uint2* const gc = p.ws_cand + (int64_t)b * CAP;
+    bucket_rank<NT, SS::SCAP, (SS::SCAP + NT - 1) / NT, false, false>(
         s.bucket, s.S, s.wsum, s.ctl, [&](int i) { return gc[tid + i * NT]; },
         [&](int i) { return (uint32_t)(tid + i * NT) < c_gt; }, [&](int i) { return (uint32_t)(i * NT) < c_gt; },
-        c_gt, (uint32_t)m, ties, BucketMap(L, U),
+        c_gt, (uint32_t)m, ties, BucketMapT<true>(L, U),
         [&](uint32_t slot, uint32_t pos, uint32_t bits) {
             r.oidx[slot] = (int32_t)pos;
             if (r.oval) r.oval[slot] = bits;
         },
         [] {});
+
+    // ------------------------------------------------ ties at P: smallest positions, tile by tile
+    if (ties) {
+        const uint32_t need = (uint32_t)m - c_gt;
+        const uint32_t vP = bits_of(P);
+        constexpr int WPT = (BW + NT - 1) / NT;
+        uint32_t off = 0;  // ties in earlier tiles (uniform)
+#pragma unroll 1
+        for (int t = 0; t < ntiles && off < need; ++t) {
+            const uint32_t e = ecnt[t];
+            if (e == 0) continue;  // uniform: that tile stored no bitmap
+            const uint32_t* const gt = p.ws_tie + ((int64_t)b * p.tiles_per_row + t) * BW;
+            uint32_t wv[WPT];
+            uint32_t tc = 0;
+#pragma unroll
+            for (int q = 0; q < WPT; ++q) {
+                const int w = tid * WPT + q;
+                wv[q] = w < BW ? gt[w] : 0u;
+                tc += (uint32_t)__popc(wv[q]);
+            }
+            uint32_t tot;
+            uint32_t rr2 = off + block_excl_scan<NT>(tc, s.wsum, &tot);
+#pragma unroll
+            for (int q = 0; q < WPT; ++q) {
+                uint32_t word = wv[q];
+                const int32_t wpos = t * TILE + (tid * WPT + q) * 32;
+                while (word && rr2 < need) {
+                    const int bit = __ffs(word) - 1;
+                    word &= word - 1;
+                    r.oidx[c_gt + rr2] = wpos + bit;
+                    if (r.oval) r.oval[c_gt + rr2] = vP;
+                    ++rr2;
+                }
+            }
+            off += e;
+            __syncthreads();  // (wsum is scanned again next turn)
+        }
+    }
     write_padding<NT>(r.oidx, r.oval, m, r.k);
-    return true;
+}
+
+// Exact selection of one whole row by one workgroup, reading the row from global memory
+// in chunks of NT * 16 elements (the next chunk's loads in flight while one is counted):
+// MSB-first 8-bit radix passes to the exact threshold key T -- threshold-bin survivors
+// staged in LDS when they fit, otherwise every later pass reads the row again, so no
+// candidate is ever dropped -- then the elements above T sorted as composites, then the
+// boundary ties at T taken in index order by an ordered scan of the row.
+template <int NT, int KMAX, int STAGE>
+__device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, uint32_t* oval,
+                          RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap) {
+    constexpr int EC = 16;
+    constexpr int CH = NT * EC;
+    constexpr int NW = NT / 64;
+    const int tid = opaque_tid();
+    const int wave = tid >> 6;
+    const PairList A{s.akey, s.apos};
+
+    // f(key, row position, valid) for every element of the row, in every lane.
+    auto sweep = [&](auto&& f) {
+        auto visit = [&](const uint32_t (&u)[EC], int32_t c0, int32_t nt) {
+            const int t4 = opaque_tid() * 4;
+#pragma unroll
+            for (int v = 0; v < EC / 4; ++v)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int32_t jl = v * NT * 4 + t4 + c;
+                    f(key_of(u[4 * v + c]), c0 + jl, jl < nt);
+                }
+        };
+        uint32_t ua[EC], ub[EC];
+        load_tile<NT, EC>(ua, row, min(CH, n));
+#pragma unroll 1
+        for (int32_t c0 = 0; c0 < n; c0 += 2 * CH) {
+            const int32_t c1 = c0 + CH;
+            if (c1 < n) load_tile<NT, EC>(ub, row + c1, min(CH, n - c1));
+            visit(ua, c0, min(CH, n - c0));
+            if (c1 >= n) break;
+            const int32_t c2 = c1 + CH;
+            if (c2 < n) load_tile<NT, EC>(ua, row + c2, min(CH, n - c2));
+            visit(ub, c1, min(CH, n - c1));
+        }
+    };
+    auto zero_whist = [&]() {
+        uint32_t* w = &s.whist[0][0];
+        for (int i = tid; i < NW * kRadix; i += NT) w[i] = 0;
+    };
+    auto merge = [&]() {
+        __syncthreads();
+        if (tid < kRadix) {
+            uint32_t h = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) h += s.whist[w][tid];
+            s.hist[tid] = h;
+        }
+        __syncthreads();
+    };
+
+    // ---------------------------------------------------------------- pass 0: top digit
+    if (tid < 8) s.ctr[tid] = 0;
+    zero_whist();
+    __syncthreads();
+    sweep([&](uint32_t kk, int32_t, bool ok) {
+        if (ok) hist_add(s.whist[wave], kk >> 24);
+    });
+    merge();
+    select_digit<NT>(s.hist, (uint32_t)m, s.wsum, s.sel);
+    uint32_t prefix = s.sel[0];
+    uint32_t k_rem = (uint32_t)m - s.sel[1];
+    const uint32_t d0 = prefix;
+    const uint32_t cap = (uint32_t)min(stage_cap, STAGE);
+    const bool staged = s.hist[d0] <= cap;
+    __syncthreads();
+
+    // Collect: digit > d0 selected outright (into A), digit == d0 staged when they fit.
+    sweep([&](uint32_t kk, int32_t j, bool ok) {
+        const uint32_t d = kk >> 24;
+        const bool g = ok && d > d0;
+        const uint32_t sa = claim_slot(g, &s.ctr[1]);
+        if (g && sa < (uint32_t)KMAX) A.put(sa, kk, (uint32_t)j);
+        if (staged) {
+            const bool cnd = ok && d == d0;
+            const uint32_t sc = claim_slot(cnd, &s.ctr[0]);
+            if (cnd && sc < cap) {
+                s.skey[sc] = kk;
+                s.sidx[sc] = (uint32_t)j;
+            }
+        }
+    });
+    __syncthreads();
+    const uint32_t nstaged = staged ? min(s.ctr[0], cap) : 0u;
+
+    // ---------------------------------------------------------------- passes 1..3: refine
+#pragma unroll 1
+    for (int pass = 1; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        zero_whist();
+        __syncthreads();
+        if (staged) {
+            for (uint32_t i = tid; i < nstaged; i += NT) {
+                const uint32_t kk = s.skey[i];
+                if ((kk >> (shift + 8)) == prefix) hist_add(s.whist[wave], (kk >> shift) & 0xFFu);
+            }
+        } else {
+            sweep([&](uint32_t kk, int32_t, bool ok) {
+                if (ok && (kk >> (shift + 8)) == prefix) hist_add(s.whist[wave], (kk >> shift) & 0xFFu);
+            });
+        }
+        merge();
+        select_digit<NT>(s.hist, k_rem, s.wsum, s.sel);
+        prefix = (prefix << 8) | s.sel[0];
+        k_rem -= s.sel[1];
+        __syncthreads();
+    }
+    const uint32_t T = prefix;                      // exact threshold key
+    const uint32_t need = min(k_rem, (uint32_t)m);  // ties at T to keep (>= 1)
+    const uint32_t cnt_gt = (uint32_t)m - need;     // selected elements strictly above T
+    const uint32_t vT = bits_of(T);
+
+    // ---------------------------------------------------------------- the rest above T
+    if (staged) {
+        for (uint32_t i0 = 0; i0 < nstaged; i0 += NT) {
+            const uint32_t i = i0 + tid;
+            const uint32_t kk = i < nstaged ? s.skey[i] : 0u;
+            const bool g = i < nstaged && kk > T;
+            const uint32_t sa = claim_slot(g, &s.ctr[1]);
+            if (g && sa < (uint32_t)KMAX) A.put(sa, kk, s.sidx[i]);
+        }
+    } else {
+        sweep([&](uint32_t kk, int32_t j, bool ok) {
+            const bool g = ok && (kk >> 24) == d0 && kk > T;
+            const uint32_t sa = claim_slot(g, &s.ctr[1]);
+            if (g && sa < (uint32_t)KMAX) A.put(sa, kk, (uint32_t)j);
+        });
+    }
+    __syncthreads();
+    const uint32_t nA = min(s.ctr[1], cnt_gt);
+    bitonic_desc<NT>(A, (int)nA);
+    for (uint32_t q = tid; q < nA; q += NT) {
+        oidx[q] = (int32_t)s.apos[q];
+        if (oval) oval[q] = bits_of(s.akey[q]);
+    }
+
+    // ---------------------------------------------------------------- boundary ties, in index order
+    {
+        constexpr int CT = NT * 4;
+        uint32_t got = 0;  // ties emitted so far (uniform)
+#pragma unroll 1
+        for (int32_t c0 = 0; c0 < n && got < need; c0 += CT) {
+            const int32_t nt = min(CT, n - c0);
+            uint32_t u4[4];
+            load_tile<NT, 4>(u4, row + c0, nt);
+            const int t4 = opaque_tid() * 4;
+            uint32_t mk = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) mk |= (t4 + c < nt && key_of(u4[c]) == T ? 1u : 0u) << c;
+            uint32_t tot;
+            uint32_t rr = got + block_excl_scan<NT>((uint32_t)__popc(mk), s.wsum, &tot);
+            while (mk && rr < need) {
+                const int c = __ffs(mk) - 1;
+                mk &= mk - 1;
+                oidx[cnt_gt + rr] = c0 + t4 + c;
+                if (oval) oval[cnt_gt + rr] = vT;
+                ++rr;
+            }
+            got += tot;
+            __syncthreads();  // (wsum is scanned again next turn)
+        }
+    }
+    write_padding<NT>(oidx, oval, m, k);
 }
 
 // ----------------------------------------------------------------------------- exact path
 
-template <int NT, int EPT, int KMAX, bool MULTI, typename ES>
-__device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES& s, const uint32_t (&key)[EPT],
-                                           uint32_t bar_target) {
+// Exact path of a row held whole by one workgroup (keys in key[]).
+template <int NT, int EPT, int KMAX, typename ES>
+__device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES& s, const uint32_t (&key)[EPT]) {
     constexpr int G4 = EPT / 4;
     constexpr int BW = ES::BWORDS;
     constexpr int NW = ES::NW;
     constexpr int SCAPX = ES::STAGE_CAP;
     const int tid = opaque_tid();
     const int wave = tid >> 6;
-    const bool multi = MULTI && r.multi;
-    const int b = r.b, tile = r.tile, ntiles = r.ntiles;
     const int32_t m = r.m, k = r.k, nt = r.nt, j0 = r.j0;
     int32_t* oidx = r.oidx;
     uint32_t* oval = r.oval;
 
-    uint32_t* rw = multi ? p.ws_zero + 1 + (int64_t)b * kRowZeroWords : nullptr;  // row words
-    uint32_t* err = p.ws_zero;
     const PairList A{s.akey, s.apos};
 
     // Visit every valid register element: f(key, local index).
@@ -1490,9 +1715,8 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
         for (int i = tid; i < NW * kRadix; i += NT) w[i] = 0;
     };
 
-    // Merge per-wave histograms; in multi mode also add into the row's global histogram
-    // for `pass` and read the merged result back after the row barrier.
-    auto merge_hist = [&](int pass) {
+    // Merge the per-wave histograms.
+    auto merge_hist = [&](int) {
         __syncthreads();
         if (tid < kRadix) {
             uint32_t h = 0;
@@ -1500,14 +1724,6 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
             for (int w = 0; w < NW; ++w) h += s.whist[w][tid];
             s.lhist[tid] = h;
             s.hist[tid] = h;
-            if (multi && h) atomicAdd(&rw[kRowHist + pass * kRadix + tid], h);
-        }
-        if (multi) {
-            bar_target += (uint32_t)ntiles;
-            row_barrier(&rw[kRowBar], bar_target, err);
-            if (tid < kRadix)
-                s.hist[tid] = __hip_atomic_load(&rw[kRowHist + pass * kRadix + tid], __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
     };
@@ -1591,8 +1807,8 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     }
 
     // ---------------------------------------------------------------- boundary ties
-    // Rank the tile's elements with key == T by index (bitmap over local positions),
-    // offset by the ties of earlier tiles, keep ranks < need at slots cnt_gt + rank.
+    // Rank the row's elements with key == T by index (bitmap over positions, popcount
+    // prefix over its words), keep ranks < need at slots cnt_gt + rank.
     for (int i = tid; i < BW; i += NT) s.bitmap[i] = 0;
     __syncthreads();
     auto mark = [&](uint32_t jl) {
@@ -1626,78 +1842,26 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
                 run += (uint32_t)__popc(s.bitmap[w]);
             }
         }
-        if (tid == 0) s.ctr[2] = total;
     }
     __syncthreads();
-    uint32_t tie_off = 0;
-    if (multi) {
-        if (tid == 0) p.ws_ecnt[(int64_t)b * p.tiles_per_row + tile] = s.ctr[2];
-        bar_target += (uint32_t)ntiles;
-        row_barrier(&rw[kRowBar], bar_target, err);
-        if (tid == 0) {
-            uint32_t o = 0;
-            for (int t = 0; t < tile; ++t)
-                o += __hip_atomic_load(&p.ws_ecnt[(int64_t)b * p.tiles_per_row + t], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            s.ctr[3] = o;
-        }
-        __syncthreads();
-        tie_off = s.ctr[3];
-    }
-    if (tie_off < need) {
-        for (int w = tid; w < BW; w += NT) {
-            uint32_t word = s.bitmap[w];
-            uint32_t rr = tie_off + s.wpre[w];
-            while (word && rr < need) {
-                const int bit = __ffs(word) - 1;
-                word &= word - 1;
-                const int32_t j = j0 + w * 32 + bit;
-                oidx[cnt_gt + rr] = j;
-                if (oval) oval[cnt_gt + rr] = vT;
-                ++rr;
-            }
+    for (int w = tid; w < BW; w += NT) {
+        uint32_t word = s.bitmap[w];
+        uint32_t rr = s.wpre[w];
+        while (word && rr < need) {
+            const int bit = __ffs(word) - 1;
+            word &= word - 1;
+            const int32_t j = j0 + w * 32 + bit;
+            oidx[cnt_gt + rr] = j;
+            if (oval) oval[cnt_gt + rr] = vT;
+            ++rr;
         }
     }
     __syncthreads();
 
     // ---------------------------------------------------------------- sort G and store
     const uint32_t nA = min(s.ctr[1], cnt_gt);
-    if (!multi) {
-        bitonic_desc<NT>(A, (int)nA);
-        for (uint32_t q = tid; q < nA; q += NT) {
-            oidx[q] = (int32_t)s.apos[q];
-            if (oval) oval[q] = bits_of(s.akey[q]);
-        }
-        write_padding<NT>(oidx, oval, m, k);
-        return;
-    }
-
-    // multi: publish this tile's G composites, last tile to arrive sorts the row.
-    if (tid == 0) s.ctr[2] = nA ? atomicAdd(&rw[kRowStage], nA) : 0u;
-    __syncthreads();
-    {
-        uint64_t* st = p.ws_stage + (int64_t)b * k;
-        const uint32_t gb = s.ctr[2];
-        for (uint32_t q = tid; q < nA; q += NT)
-            if (gb + q < cnt_gt) st[gb + q] = A.composite(q);
-    }
-    wait_global_writes();
-    __syncthreads();
-    if (tid == 0) {  // release this tile's stage writes; the last arriver acquires all of them
-        const uint32_t old = __hip_atomic_fetch_add(&rw[kRowArrive], 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        s.ctr[3] = (old == (uint32_t)ntiles - 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s.ctr[3] == 0) return;
-    {
-        const uint64_t* st = p.ws_stage + (int64_t)b * k;
-        for (uint32_t q = tid; q < cnt_gt; q += NT)
-            A.set_composite(q, __hip_atomic_load(&st[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    }
-    __syncthreads();
-    bitonic_desc<NT>(A, (int)cnt_gt);
-    for (uint32_t q = tid; q < cnt_gt; q += NT) {
+    bitonic_desc<NT>(A, (int)nA);
+    for (uint32_t q = tid; q < nA; q += NT) {
         oidx[q] = (int32_t)s.apos[q];
         if (oval) oval[q] = bits_of(s.akey[q]);
     }
@@ -1719,7 +1883,6 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     r.k = p.k;
     r.m = min(r.k, r.n);
     r.ntiles = MULTI ? max(1, (r.n + TILE - 1) / TILE) : 1;
-    r.multi = MULTI && r.ntiles > 1;
     r.oidx = p.out_idx + (int64_t)b * r.k;
     r.oval = p.out_val ? p.out_val + (int64_t)b * r.k : nullptr;
     r.j0 = tile * TILE;
@@ -1727,38 +1890,10 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     return r;
 }
 
-// One (row, tile) item of the several-workgroups-per-row kernel.
+// A row that fits one tile, held whole by this workgroup: the pivot path, and the exact
+// path when it misses.
 template <int NT, int EPT, int KMAX, bool MULTI>
-__device__ __forceinline__ void process_tile(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, int b, int tile) {
-    static_assert(MULTI, "one-workgroup-per-row kernels take single_row");
-    const RowCtx r = row_setup<NT * EPT, MULTI>(p, b, tile);
-    if (tile >= r.ntiles) return;
-
-    __syncthreads();  // previous item of a persistent workgroup is done with LDS
-
-    if (r.m == 0) {  // empty window: every slot is padding (single tile by construction)
-        write_padding<NT>(r.oidx, r.oval, 0, r.k);
-        return;
-    }
-
-    uint32_t u[EPT];
-    load_tile<NT, EPT>(u, p.scores + r.base + r.j0, r.nt);
-
-    uint32_t bar_target = 0;  // row barriers passed so far x tiles (several workgroups per row)
-    if (p.fast) {
-        if (multi_fast_tile<NT, EPT, KMAX>(p, r, s.mfast, u, bar_target)) return;
-        __syncthreads();  // fall back to the exact path on the same registers
-    }
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
-    exact_tile<NT, EPT, KMAX, MULTI>(p, r, s.exact, u, bar_target);
-}
-
-// One row of the one-workgroup-per-row kernel (grid = B: no row loop, so nothing
-// row-invariant is hoisted into registers that would stay live across the row).
-template <int NT, int EPT, int KMAX>
-__device__ __forceinline__ void single_row(const Params& p, SmemAll<NT, EPT, KMAX, false>& s, int b) {
-    const RowCtx r = row_setup<NT * EPT, false>(p, b, 0);
+__device__ __forceinline__ void whole_tile_row(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, const RowCtx& r) {
     if (r.m == 0) {  // empty window: every slot is padding
         write_padding<NT>(r.oidx, r.oval, 0, r.k);
         return;
@@ -1774,28 +1909,31 @@ __device__ __forceinline__ void single_row(const Params& p, SmemAll<NT, EPT, KMA
     }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
-    uint32_t bar_target = 0;
-    exact_tile<NT, EPT, KMAX, false>(p, r, s.exact, u, bar_target);
+    exact_tile<NT, EPT, KMAX>(p, r, s.exact, u);
 }
 
 // MINW: waves per SIMD the register allocation must allow (the LDS footprint fixes
 // how many workgroups share a CU, so more registers per wave would buy nothing).
+// One workgroup per row (MULTI false, grid = B: no row loop, so nothing row-invariant is
+// hoisted into registers that would stay live across rows), or one workgroup per
+// (row, tile) item (MULTI true; a grid-stride loop over the items, in any order: no item
+// waits for another).
 template <int NT, int EPT, int KMAX, bool MULTI, int MINW>
 __global__ __launch_bounds__(NT, MINW) void topk_ragged_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto& s = *reinterpret_cast<SmemAll<NT, EPT, KMAX, MULTI>*>(smem_raw);
     if constexpr (!MULTI) {
-        single_row<NT, EPT, KMAX>(p, s, (int)blockIdx.x);
+        whole_tile_row<NT, EPT, KMAX, false>(p, s, row_setup<NT * EPT, false>(p, (int)blockIdx.x, 0));
     } else {
         const int64_t items = (int64_t)p.B * p.tiles_per_row;
-        for (int64_t it = blockIdx.x; it < items; it += gridDim.x)
-            process_tile<NT, EPT, KMAX, MULTI>(p, s, (int)(it / p.tiles_per_row), (int)(it % p.tiles_per_row));
+        for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+            const RowCtx r = row_setup<NT * EPT, true>(p, (int)(it / p.tiles_per_row), (int)(it % p.tiles_per_row));
+            if (r.tile >= r.ntiles) continue;  // (uniform) the row is shorter than this tile
+            __syncthreads();                   // the previous item is done with LDS
+            if (r.ntiles == 1) whole_tile_row<NT, EPT, KMAX, true>(p, s, r);
+            else split_tile<NT, EPT, KMAX>(p, r, s);
+        }
     }
-}
-
-__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0;
 }
 
 }  // namespace detk

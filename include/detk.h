@@ -28,33 +28,52 @@
 extern "C" {
 #endif
 
-/* Status codes returned by every entry point. */
+/* Status codes returned by every entry point.  The pages' backend replaces asserts with
+ * actionable errors and makes out-of-envelope calls fail loudly (SGLang PR #31115,
+ * hardening commit); every code below is found on the host, before any launch. */
 typedef enum {
     DETK_OK = 0,
-    DETK_ERR_INVALID_ARG = 1, /* NULL required pointer, B < 0, k < 1, max_len < 0       */
-    DETK_ERR_UNSUPPORTED = 2, /* k > DETK_MAX_K, device not gfx950, row too long for the */
-                              /* co-resident multi-workgroup path, int32 offset overflow  */
-    DETK_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than detk_workspace_size()     */
-    DETK_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed               */
+    DETK_ERR_INVALID_ARG = 1, /* NULL required pointer, B < 0, k < 1, max_len < 0         */
+    DETK_ERR_UNSUPPORTED = 2, /* k > DETK_MAX_K, max_len > DETK_MAX_LEN, B * k >= 2^31,    */
+                              /* device not gfx950                                         */
+    DETK_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than detk_workspace_size()       */
+    DETK_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed                 */
 } detk_status;
 
 /* Largest k supported.  The pages' deterministic backend envelope is topk <= 4096
  * (SGLang PR #31115, "Modifications" and hardening commit). */
 #define DETK_MAX_K 4096
 
+/* Longest row window supported: 2^30 elements.  The pages' backend takes rows shorter
+ * than 2^24 (its composite keeps 24 index bits; SGLang PR #31115, hardening commit);
+ * here a composite keeps the full 32-bit index, and the bound comes from int32 window
+ * offsets (row_starts[b] + n_b < 2^31) with room for the per-row workspace.  Rows of any
+ * length up to this bound run on any number of free CUs: no part of a call waits for
+ * another workgroup. */
+#define DETK_MAX_LEN (1 << 30)
+
+/* What detk_workspace_size returns for a configuration detk_topk_ragged would refuse. */
+#define DETK_WORKSPACE_UNSUPPORTED ((size_t)-1)
+
 /*
  * detk_can_implement -- host-only capability query, no launch.
  * Returns DETK_OK when a call with this k and max_len can run on `device`, else the
- * status such a call would return.  Meant for construction time, so an unsupported
- * configuration is found before the first batch (the failure mode reported in vLLM
- * PR #55872's GB10 trace, where the check fired only inside warmup).
+ * status such a call would return (DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, or
+ * DETK_ERR_HIP if the device cannot be queried).  Meant for construction time, so an
+ * unsupported configuration is found before the first batch: vLLM PR #55872, GB10
+ * failure trace, shows the alternative, a shared-memory check that fired only inside
+ * the engine's warmup.
  */
 int detk_can_implement(int device, int k, int32_t max_len);
 
 /*
- * detk_workspace_size -- bytes of device workspace a call with these arguments needs
- * (0 when every row fits one workgroup).  The same value for the same (device, B, k,
- * max_len) in one process.
+ * detk_workspace_size -- bytes of device workspace a call with these arguments needs:
+ * 0 when every row fits one workgroup (max_len <= 32768) or B == 0, and
+ * DETK_WORKSPACE_UNSUPPORTED (SIZE_MAX) when detk_can_implement would refuse the
+ * configuration, so "needs none" and "cannot run" are told apart.  The same value for
+ * the same (device, B, k, max_len) in one process.  Sizing the workspace on the host
+ * ahead of time keeps the call free of allocation, so it can be captured into a graph
+ * (SGLang PR #31115, hardening commit: no first-touch allocation under graph capture).
  */
 size_t detk_workspace_size(int device, int B, int k, int32_t max_len);
 
@@ -65,60 +84,46 @@ size_t detk_workspace_size(int device, int B, int k, int32_t max_len);
  *               scores[s_b .. s_b + n_b) with s_b = row_starts[b] (or b * max_len
  *               when row_starts is NULL, i.e. a dense (B, max_len) matrix) and
  *               n_b = clamp(lengths[b], 0, max_len) (max_len when lengths is NULL).
- *               Metadata is trusted, as in the pages' backend: the windows must lie
- *               inside the allocation; the library does not check them.
+ *               Metadata is trusted, as in the pages' backend (SGLang PR #31115,
+ *               hardening commit): the windows must lie inside the allocation and
+ *               s_b + n_b < 2^31; the library does not check them.
  *   row_starts  device int32[B] absolute element offsets, or NULL.
  *   lengths     device int32[B], or NULL.
  *   B           rows (0 returns DETK_OK without launching anything).
- *   max_len     host-known upper bound of every n_b; fixes the launch shape so the
- *               call never reads device metadata on the host.
+ *   max_len     host-known upper bound of every n_b, <= DETK_MAX_LEN; fixes the launch
+ *               shape so the call never reads device metadata on the host.
  *   k           1 <= k <= DETK_MAX_K.
  *   out_idx     device int32[B * k], row-major: local indices, -1 after min(k, n_b).
  *   out_val     device float32[B * k] or NULL: the selected scores' exact bits
  *               (NaN payloads and -0.0 preserved; no floating-point op touches them),
  *               -inf in padded slots.
  *   workspace   device, at least detk_workspace_size() bytes (may be NULL when that
- *               is 0).  Scratch owned by the caller; contents need no initialisation
- *               and are undefined after the call.  Calls that share one workspace
- *               must be ordered (same stream, or synchronised).
+ *               is 0).  Owned by the caller.  It must be zero-filled before its first
+ *               use (any fill; once, at allocation); every call leaves it zero-filled
+ *               again, so it is reused without clearing, by calls of any shape.  Calls
+ *               that share one workspace must be ordered (same stream, or
+ *               synchronised); overlapping calls on one workspace race.
  *   stream      hipStream_t (NULL = default stream).
  *
  * The call allocates nothing, never synchronises and reads no device memory on the
- * host, so it can be captured into a HIP graph.  Argument errors are detected on
- * the host before any launch and leave every output untouched.
+ * host, so it can be captured into a HIP graph (SGLang PR #31115, "Modifications":
+ * graph replay bitwise equal to eager).  Argument errors are detected on the host before
+ * any launch and leave every output untouched.  Once launched, the call cannot fail or
+ * stall on the device: no workgroup waits for another, so it needs no co-residency and
+ * completes beside any other work on the GPU.
  */
 int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                      int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
                      size_t workspace_bytes, void* stream);
 
-/* Human-readable text for a status code (static storage). */
+/*
+ * detk_status_string -- human-readable text for a status code, naming the condition
+ * that produced it (static storage; "unknown detk status" for other values).  The pages'
+ * backend replaces bare asserts with actionable errors (SGLang PR #31115, hardening
+ * commit).
+ */
 const char* detk_status_string(int status);
 
-/*
- * detk_workspace_error -- DEBUG.  Synchronises `stream` and returns the error word the
- * last call on this workspace left behind: 0 when clean, non-zero when a
- * multi-workgroup row barrier gave up after its bounded wait (outputs of that call
- * are then undefined).  Not capturable.
- */
-int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* stream);
-
-/*
- * detk_debug_set -- TEST-ONLY process-wide overrides (not thread-safe; set them before
- * issuing calls).  Every override changes only how the result is computed, never the
- * result.
- *   what = DETK_DEBUG_PATH:        0 automatic, 1 one workgroup per row, 2 several
- *                                  workgroups per row (co-operating through workspace).
- *   what = DETK_DEBUG_STAGING_CAP: -1 default; else the largest threshold-bin
- *                                  candidate count staged in LDS (0 forces every
- *                                  refinement pass to rescan the register-resident row).
- *   what = DETK_DEBUG_MULTI_TILE:  0 default; else elements per workgroup tile of the
- *                                  multi-workgroup path (4096, 8192, 16384 or 32768).
- *   what = DETK_DEBUG_FAST:        1 default (sampled-pivot path, exact radix path when
- *                                  it misses); 0 exact radix path only; 2 pivot forced
- *                                  to miss, so every row starts on the pivot path and
- *                                  falls back.
- * Returns DETK_OK or DETK_ERR_INVALID_ARG.
- */
 /*
  * detk_read_probe -- MEASUREMENT, not part of the top-k path.  Reads the `bytes` bytes at
  * `data` (device memory) exactly once with 16-byte loads, a grid-stride loop spread over
@@ -129,6 +134,25 @@ int detk_workspace_error(const void* workspace, size_t workspace_bytes, void* st
  */
 int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream);
 
+/*
+ * detk_debug_set -- TEST-ONLY process-wide overrides (not thread-safe; set them before
+ * issuing calls).  Every override changes only how the result is computed, never the
+ * result, so tests can drive every fallback the pages require to exist (threshold-bin
+ * overflow falls back to rescans and never drops a candidate: SGLang PR #31115, PR
+ * summary).
+ *   what = DETK_DEBUG_PATH:        0 automatic, 1 one workgroup per row, 2 rows split
+ *                                  over several workgroups (one tile each).
+ *   what = DETK_DEBUG_STAGING_CAP: -1 default; else the largest threshold-bin
+ *                                  candidate count staged in LDS (0 forces every
+ *                                  refinement pass to rescan the row).
+ *   what = DETK_DEBUG_MULTI_TILE:  0 default; else elements per workgroup tile of the
+ *                                  split-row path (4096, 8192, 16384 or 32768).
+ *   what = DETK_DEBUG_FAST:        1 default (sampled-pivot path, exact radix path when
+ *                                  it misses); 0 exact radix path only; 2 pivot forced
+ *                                  to miss, so every row starts on the pivot path and
+ *                                  falls back.
+ * Returns DETK_OK or DETK_ERR_INVALID_ARG.
+ */
 #define DETK_DEBUG_PATH 1
 #define DETK_DEBUG_STAGING_CAP 2
 #define DETK_DEBUG_MULTI_TILE 3

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_entry_points():
     names = _declared()
     for n in ("detk_topk_ragged", "detk_workspace_size", "detk_can_implement", "detk_status_string",
-              "detk_workspace_error", "detk_debug_set", "detk_read_probe"):
+              "detk_debug_set", "detk_read_probe"):
         assert n in names
 
 
@@ -76,5 +76,11 @@ def test_status_strings_and_debug_overrides(lib):
         assert lib.detk_debug_set(what, val) == detk.DETK_OK
 
 
-def test_workspace_error_on_null_workspace(lib):
-    assert lib.detk_workspace_error(None, 0, None) == 0
+def test_workspace_size_refusal_is_size_max(lib):
+    # refused configurations answer SIZE_MAX, never 0 ("needs no workspace")
+    size_max = (1 << 64) - 1
+    assert lib.detk_workspace_size(0, 4, 0, 100) == size_max
+    assert lib.detk_workspace_size(0, -1, 16, 100) == size_max
+    assert lib.detk_workspace_size(0, 4, 16, -5) == size_max
+    assert lib.detk_workspace_size(0, 4, 4097, 100) == size_max
+    assert lib.detk_workspace_size(-1, 4, 16, 100) == size_max

@@ -27,9 +27,12 @@ def dev():
     return torch.device("cuda:0")
 
 
+# Every named workload at full size, plus a 16-row narrow batch.
 REPLAY = {
     "plateau": lambda: W.full("plateau_4x4096"),
     "decode_ragged": lambda: W.full("decode_ragged_64"),
+    "prefill_causal": lambda: W.full("prefill_causal_8192x16384"),
+    "narrow": lambda: W.full("narrow_128x65536"),
     "long_context": lambda: W.full("long_context_8x262144"),
     "narrow_small": lambda: W.narrow_range(B=16, L=65536, k=4096, name="replay_narrow"),
 }
@@ -37,21 +40,22 @@ REPLAY = {
 
 @pytest.mark.parametrize("name", sorted(REPLAY))
 def test_twenty_runs_identical(dev, name):
+    """20 calls on the same input into the same output buffers: every call's output is
+    byte-identical to the oracle's (which also makes them identical to each other)."""
     import torch
     wl = REPLAY[name]()
     scores, rs, ln = to_dev(wl, dev)
-    log("replay x20: %s" % name)
-    ref = None
-    for _ in range(20):
-        gi, gv = detk.topk_ragged(scores, rs, ln, wl.k, max_len=wl.max_len)
+    out_i = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
+    out_v = torch.empty((wl.B, wl.k), dtype=torch.float32, device=dev)
+    ws = detk.new_workspace(wl.B, wl.k, wl.max_len, dev)  # one workspace for every call
+    log("replay x20: %s B=%d max_len=%d k=%d" % (name, wl.B, wl.max_len, wl.k))
+    oi, ov = run_oracle(wl)
+    for rep in range(20):
+        out_i.fill_(-7)
+        out_v.fill_(7.0)
+        detk.topk_ragged(scores, rs, ln, wl.k, max_len=wl.max_len, out_idx=out_i, out_val=out_v, workspace=ws)
         torch.cuda.synchronize()
-        cur = (gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32))
-        if ref is None:
-            ref = cur
-            oi, ov = run_oracle(wl)
-            assert_same(cur[0], cur[1], oi, ov, name)
-        else:
-            assert np.array_equal(cur[0], ref[0]) and np.array_equal(cur[1], ref[1])
+        assert_same(out_i.cpu().numpy(), out_v.cpu().numpy().view(np.uint32), oi, ov, "%s rep %d" % (name, rep))
 
 
 def test_batch_composition_invariance(dev):
@@ -97,22 +101,60 @@ def detk_oracle_rows(buf, starts, lens, k, max_len):
     return oracle.topk_ragged(buf, starts.astype(np.int32), lens, k, max_len)
 
 
-def test_busy_sibling_stream(dev):
-    """Replays while another stream runs large matmuls that compete for the CUs."""
+BUSY = {
+    "plateau": "plateau_4x4096",          # boundary inside the 0.0 tie plateau
+    "narrow": "narrow_128x65536",         # top digits collide, bitwise duplicates
+    "long_context": "long_context_8x262144",
+}
+
+
+@pytest.mark.parametrize("name", sorted(BUSY))
+def test_busy_sibling_stream(dev, name):
+    """30 replays of one input while another stream runs large matmuls that compete for
+    the CUs (SGLang PR #31115, "Accuracy Tests": 30 repetitions per input with a busy
+    sibling stream); every replay must equal the oracle byte for byte."""
     import torch
-    wl = W.full("long_context_8x262144")
+    wl = W.full(BUSY[name])
     scores, rs, ln = to_dev(wl, dev)
     oi, ov = run_oracle(wl)
     side = torch.cuda.Stream()
     a = torch.randn(2048, 2048, device=dev)
-    log("busy sibling stream replay")
-    for rep in range(10):
+    ws = detk.new_workspace(wl.B, wl.k, wl.max_len, dev)
+    log("busy sibling stream replay x30: %s" % name)
+    for rep in range(30):
         with torch.cuda.stream(side):
             for _ in range(4):
                 a = (a @ a).clamp_(-1, 1)
-        gi, gv = detk.topk_ragged(scores, rs, ln, wl.k, max_len=wl.max_len)
+        gi, gv = detk.topk_ragged(scores, rs, ln, wl.k, max_len=wl.max_len, workspace=ws)
         torch.cuda.synchronize()
         assert_same(gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32), oi, ov, "busy rep %d" % rep)
+
+
+def test_split_calls_on_two_streams(dev):
+    """Split-row calls issued on two streams at once, each with a grid wider than the GPU
+    holds, plus a one-workgroup-per-row call on a third: no workgroup of a split row waits
+    for another, so the calls share the CUs in any proportion and all complete with the
+    oracle's answer."""
+    import torch
+    wls = [W.long_context(B=24, L=300000, k=2048, short_n=1700, name="two_streams_a"),
+           W.narrow_range(B=64, L=131072, k=4096, name="two_streams_b"),
+           W.decode_ragged(B=200, n_lo=1, n_hi=32768, k=2048, name="two_streams_c")]
+    refs = [run_oracle(w) for w in wls]
+    bufs = [to_dev(w, dev) for w in wls]
+    wss = [detk.new_workspace(w.B, w.k, w.max_len, dev) for w in wls]
+    streams = [torch.cuda.Stream() for _ in wls]
+    outs = [(torch.empty((w.B, w.k), dtype=torch.int32, device=dev),
+             torch.empty((w.B, w.k), dtype=torch.float32, device=dev)) for w in wls]
+    torch.cuda.synchronize()
+    for rep in range(10):
+        log("three streams, rep %d" % rep)
+        for w, (sc, rs, ln), ws, st, (oi_, ov_) in zip(wls, bufs, wss, streams, outs):
+            with torch.cuda.stream(st):
+                detk.topk_ragged(sc, rs, ln, w.k, max_len=w.max_len, out_idx=oi_, out_val=ov_, workspace=ws,
+                                 stream=st)
+        torch.cuda.synchronize()
+        for w, (oi, ov), (gi, gv) in zip(wls, refs, outs):
+            assert_same(gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32), oi, ov, "%s rep %d" % (w.name, rep))
 
 
 @pytest.mark.parametrize("shape", ["single", "multi"])
@@ -135,8 +177,7 @@ def test_hip_graph_replay_matches_eager(dev, shape):
     s_ln = torch.zeros(B, dtype=torch.int32, device=dev)
     out_i = torch.empty(B, 2048, dtype=torch.int32, device=dev)
     out_v = torch.empty(B, 2048, device=dev)
-    need = detk.workspace_size(B, 2048, max_len)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws = detk.new_workspace(B, 2048, max_len, dev)
 
     def load(w):
         s_buf[:w.scores.size].copy_(torch.from_numpy(w.scores))
