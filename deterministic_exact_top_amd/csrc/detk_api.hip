@@ -53,7 +53,7 @@ struct DeviceInfo {
     bool gfx950 = false;
     int cus = 0;
     size_t max_lds = 0;
-    int split_occ[2] = {};  // workgroups per CU of the 16K-element split tile, k <= 2048 / k <= 4096
+    int split_occ[2] = {};   // workgroups per CU of the 16K-element split tile, k <= 2048 / k <= 4096
 };
 
 std::mutex g_mu;
@@ -116,6 +116,8 @@ int device_info(int device, DeviceInfo* out) {
     return DETK_OK;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 struct Plan {
     bool multi = false;
     int tile = 0;         // elements per workgroup tile
@@ -124,9 +126,19 @@ struct Plan {
     int grid = 0;
     size_t lds = 0;
     size_t ws_bytes = 0;
-    // workspace layout (bytes from the start)
-    size_t off_ctl = 0, off_ecnt = 0, off_cand = 0, off_tie = 0;
+    // workspace layout: data regions, in bytes from the start of the data area
+    size_t data_bytes = 0, off_ecnt = 0, off_cand = 0, off_tie = 0;
 };
+
+// Workspace layout.  The per-row control words (which must be zero when a call starts,
+// and which every call leaves at zero) sit at the start, row b at byte b * kCtlRowBytes,
+// in a control area of the first 1/64 of the workspace; every data region comes after
+// it.  The area's size depends on the workspace's size alone, so calls of any shape on
+// one buffer (passed with the same size) never write data over another call's control
+// words, and a buffer zero-filled once stays ready.  A split row needs at least 32 KB of
+// data, so the area always holds every row's words.
+constexpr size_t kCtlRowBytes = detk::kRowCtlWords * 4;
+size_t data_offset(size_t workspace_bytes) { return align256(workspace_bytes / 64); }
 
 template <bool MULTI>
 size_t lds_bytes_t(int tile, int kmax) {
@@ -139,8 +151,6 @@ size_t lds_bytes_t(int tile, int kmax) {
     }
 }
 size_t lds_bytes(int tile, int kmax, bool multi) { return multi ? lds_bytes_t<true>(tile, kmax) : lds_bytes_t<false>(tile, kmax); }
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Most workgroups launched for the split-row kernel; more items are taken by a grid-stride
 // loop (the items never wait for one another, so any number may be resident).
@@ -182,17 +192,20 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         pl->tiles_per_row = (int)tpr;
         const int64_t items = (int64_t)B * tpr;
         pl->grid = (int)(items < kMaxSplitGrid ? items : kMaxSplitGrid);
+        // Data regions, from the start of the data area (see data_offset()).
         const size_t cap = pl->kmax == 2048 ? detk::cand_cap<2048>() : detk::cand_cap<4096>();
         size_t off = 0;
-        pl->off_ctl = off;
-        off = align256(off + (size_t)B * detk::kRowCtlWords * 4);
         pl->off_ecnt = off;
         off = align256(off + (size_t)B * (size_t)tpr * 4);
         pl->off_cand = off;
         off = align256(off + (size_t)B * cap * 8);
         pl->off_tie = off;
         off = align256(off + (size_t)B * (size_t)tpr * (size_t)(pl->tile / 32) * 4);
-        pl->ws_bytes = off;
+        pl->data_bytes = off;
+        // The smallest workspace whose control area and data area both fit.
+        size_t w = align256(off + off / 63 + 512);
+        while (data_offset(w) + off > w || (size_t)B * kCtlRowBytes > data_offset(w)) w += 256;
+        pl->ws_bytes = w;
     }
     pl->lds = lds_bytes(pl->tile, pl->kmax, pl->multi);
     if (pl->lds > dev.max_lds) return DETK_ERR_UNSUPPORTED;
@@ -231,6 +244,57 @@ hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
     default: return k2 ? launch<32768, 2048, true>(p, pl.grid, pl.lds, stream)
                        : launch<32768, 4096, true>(p, pl.grid, pl.lds, stream);
     }
+}
+
+// The operation on the caller's workspace.  Allocates nothing.
+int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B, int32_t max_len, int k,
+        int32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+    if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
+    if (B > 0 && (!scores || !out_idx)) return DETK_ERR_INVALID_ARG;
+    if (k > DETK_MAX_K || max_len > DETK_MAX_LEN) return DETK_ERR_UNSUPPORTED;
+    if (B == 0) return DETK_OK;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return DETK_ERR_HIP;
+    DeviceInfo dev;
+    int st = device_info(device, &dev);
+    if (st != DETK_OK) return st;
+    Plan pl;
+    st = make_plan(dev, B, k, max_len, &pl);
+    if (st != DETK_OK) return st;
+    size_t data_off = 0;
+    if (pl.multi) {
+        data_off = data_offset(workspace_bytes);
+        if (!workspace || workspace_bytes < pl.ws_bytes || data_off + pl.data_bytes > workspace_bytes ||
+            (size_t)B * kCtlRowBytes > data_off)
+            return DETK_ERR_WORKSPACE;
+    }
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    Params p;
+    p.scores = reinterpret_cast<const uint32_t*>(scores);
+    p.row_starts = row_starts;
+    p.lengths = lengths;
+    p.B = B;
+    p.max_len = max_len;
+    p.k = k;
+    p.tiles_per_row = pl.tiles_per_row;
+    p.stage_cap = g_stage_cap < 0 ? detk::kStageCap : (g_stage_cap > detk::kStageCap ? detk::kStageCap : g_stage_cap);
+    p.fast = g_fast;
+    p.out_idx = out_idx;
+    p.out_val = reinterpret_cast<uint32_t*>(out_val);
+    p.ws_ctl = nullptr;
+    p.ws_ecnt = nullptr;
+    p.ws_cand = nullptr;
+    p.ws_tie = nullptr;
+    if (pl.multi) {
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        p.ws_ctl = reinterpret_cast<uint32_t*>(ws);
+        p.ws_ecnt = reinterpret_cast<uint32_t*>(ws + data_off + pl.off_ecnt);
+        p.ws_cand = reinterpret_cast<uint2*>(ws + data_off + pl.off_cand);
+        p.ws_tie = reinterpret_cast<uint32_t*>(ws + data_off + pl.off_tie);
+    }
+    if (dispatch(pl, p, stream) != hipSuccess) return DETK_ERR_HIP;
+    return DETK_OK;
 }
 
 }  // namespace
@@ -278,46 +342,7 @@ size_t detk_workspace_size(int device, int B, int k, int32_t max_len) {
 int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                      int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
                      size_t workspace_bytes, void* stream_ptr) {
-    if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
-    if (B > 0 && (!scores || !out_idx)) return DETK_ERR_INVALID_ARG;
-    if (k > DETK_MAX_K || max_len > DETK_MAX_LEN) return DETK_ERR_UNSUPPORTED;
-    if (B == 0) return DETK_OK;
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) return DETK_ERR_HIP;
-    DeviceInfo dev;
-    int st = device_info(device, &dev);
-    if (st != DETK_OK) return st;
-    Plan pl;
-    st = make_plan(dev, B, k, max_len, &pl);
-    if (st != DETK_OK) return st;
-    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return DETK_ERR_WORKSPACE;
-
-    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-    Params p;
-    p.scores = reinterpret_cast<const uint32_t*>(scores);
-    p.row_starts = row_starts;
-    p.lengths = lengths;
-    p.B = B;
-    p.max_len = max_len;
-    p.k = k;
-    p.tiles_per_row = pl.tiles_per_row;
-    p.stage_cap = g_stage_cap < 0 ? detk::kStageCap : (g_stage_cap > detk::kStageCap ? detk::kStageCap : g_stage_cap);
-    p.fast = g_fast;
-    p.out_idx = out_idx;
-    p.out_val = reinterpret_cast<uint32_t*>(out_val);
-    p.ws_ctl = nullptr;
-    p.ws_ecnt = nullptr;
-    p.ws_cand = nullptr;
-    p.ws_tie = nullptr;
-    if (pl.multi) {
-        unsigned char* ws = static_cast<unsigned char*>(workspace);
-        p.ws_ctl = reinterpret_cast<uint32_t*>(ws + pl.off_ctl);
-        p.ws_ecnt = reinterpret_cast<uint32_t*>(ws + pl.off_ecnt);
-        p.ws_cand = reinterpret_cast<uint2*>(ws + pl.off_cand);
-        p.ws_tie = reinterpret_cast<uint32_t*>(ws + pl.off_tie);
-    }
-    if (dispatch(pl, p, stream) != hipSuccess) return DETK_ERR_HIP;
-    return DETK_OK;
+    return run(scores, row_starts, lengths, B, max_len, k, out_idx, out_val, workspace, workspace_bytes, stream_ptr);
 }
 
 const char* detk_status_string(int status) {

@@ -63,7 +63,7 @@ constexpr uint32_t kNegInfBits = 0xFF800000u;
 constexpr int kRowCgt = 0;                      // candidates claimed (keys above P)
 constexpr int kRowEq = 1;                       // keys equal to P
 constexpr int kRowArrive = 2;                   // tiles done: the last to arrive orders the row
-constexpr int kRowCtlWords = 32;                // one 128-byte line per row
+constexpr int kRowCtlWords = 4;                 // 16 bytes per row
 constexpr int kSplitSamples = 8192;             // split rows: samples per row (4 per 16-byte load)
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer resource, gfx9-family data format
 

@@ -98,11 +98,15 @@ size_t detk_workspace_size(int device, int B, int k, int32_t max_len);
  *               (NaN payloads and -0.0 preserved; no floating-point op touches them),
  *               -inf in padded slots.
  *   workspace   device, at least detk_workspace_size() bytes (may be NULL when that
- *               is 0).  Owned by the caller.  It must be zero-filled before its first
- *               use (any fill; once, at allocation); every call leaves it zero-filled
- *               again, so it is reused without clearing, by calls of any shape.  Calls
- *               that share one workspace must be ordered (same stream, or
- *               synchronised); overlapping calls on one workspace race.
+ *               is 0), workspace_bytes its size.  Owned by the caller.  It must be
+ *               zero-filled before its first use (any fill; once, at allocation).  The
+ *               words that must start at zero are the per-row counters at its start,
+ *               in a control area whose extent depends on workspace_bytes alone; every
+ *               call sets them back to zero, and no call writes anything else there.
+ *               So a buffer passed with the same workspace_bytes every time is reused
+ *               by calls of any shape without clearing (passed with another size, it
+ *               is zero-filled again first).  Calls that share one workspace must be
+ *               ordered (same stream, or synchronised); overlapping calls race.
  *   stream      hipStream_t (NULL = default stream).
  *
  * The call allocates nothing, never synchronises and reads no device memory on the

@@ -130,6 +130,30 @@ def test_busy_sibling_stream(dev, name):
         assert_same(gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32), oi, ov, "busy rep %d" % rep)
 
 
+def test_one_workspace_many_shapes(dev):
+    """One workspace buffer, zero-filled once and sized for the largest call, serves a
+    sequence of split-row calls of different shapes (rows, k, row length, tile count),
+    in an order where a call with more rows follows calls with fewer: the per-row counters
+    sit in a control area that no call's data ever overlaps, so each call still finds
+    them at zero."""
+    import torch
+    wls = [W.long_context(B=3, L=70000, k=2048, short_n=900, name="ws_shapes_a"),
+           W.narrow_range(B=24, L=65536, k=4096, name="ws_shapes_b"),
+           W.long_context(B=8, L=262144, k=2048, short_n=1500, name="ws_shapes_c"),
+           W.decode_ragged(B=64, n_lo=40000, n_hi=100000, k=1000, name="ws_shapes_d"),
+           W.long_context(B=3, L=70000, k=2048, short_n=900, name="ws_shapes_a")]
+    need = max(detk.workspace_size(w.B, w.k, w.max_len) for w in wls)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        for w in wls:
+            log("one workspace, rep %d: %s B=%d max_len=%d k=%d" % (rep, w.name, w.B, w.max_len, w.k))
+            scores, rs, ln = to_dev(w, dev)
+            gi, gv = detk.topk_ragged(scores, rs, ln, w.k, max_len=w.max_len, workspace=ws)
+            torch.cuda.synchronize()
+            oi, ov = run_oracle(w)
+            assert_same(gi.cpu().numpy(), gv.cpu().numpy().view(np.uint32), oi, ov, "%s rep %d" % (w.name, rep))
+
+
 def test_split_calls_on_two_streams(dev):
     """Split-row calls issued on two streams at once, each with a grid wider than the GPU
     holds, plus a one-workgroup-per-row call on a third: no workgroup of a split row waits
