@@ -17,13 +17,14 @@ import ctypes
 import os
 
 __all__ = [
-    "topk_ragged", "workspace_size", "new_workspace", "can_implement", "status_string", "debug_set",
+    "topk_ragged", "topk_ragged_noalloc", "workspace_size", "new_workspace", "can_implement", "status_string", "debug_set",
     "library_path", "load_library", "DETK_MAX_K", "DETK_MAX_LEN", "DetkError",
 ]
 
 DETK_MAX_K = 4096
 DETK_MAX_LEN = 1 << 30
 DETK_WORKSPACE_UNSUPPORTED = (1 << 64) - 1  # SIZE_MAX: the configuration cannot run
+DETK_SCRATCH_BYTES = 16 << 20  # the per-GPU scratch array behind topk_ragged_noalloc
 DETK_OK, DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, DETK_ERR_WORKSPACE, DETK_ERR_HIP = range(5)
 DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE, DETK_DEBUG_FAST = 1, 2, 3, 4
 
@@ -58,6 +59,8 @@ def load_library():
     lib.detk_workspace_size.restype = sz
     lib.detk_topk_ragged.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.detk_topk_ragged.restype = ctypes.c_int
+    lib.detk_topk_ragged_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp]
+    lib.detk_topk_ragged_noalloc.restype = ctypes.c_int
     lib.detk_status_string.argtypes = [ctypes.c_int]
     lib.detk_status_string.restype = ctypes.c_char_p
     lib.detk_debug_set.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -180,3 +183,23 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
     if st != DETK_OK:
         raise DetkError(st, "detk_topk_ragged")
     return out_idx, (out_val if with_values else None)
+
+
+def topk_ragged_noalloc(scores, row_starts, lengths, k: int, max_len: int, out_idx, out_val=None, B: int | None = None,
+                        stream=None):
+    """detk_topk_ragged_noalloc: the same operation with no workspace argument (the library's
+    per-GPU scratch array serves rows split over workgroups).  Nothing is allocated here
+    either: the caller passes the outputs (out_idx int32 (B, k), out_val float32 (B, k) or
+    None).  Calls overlapping on one GPU race."""
+    import torch
+    lib = load_library()
+    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 CUDA tensor")
+    if B is None:
+        B = int(out_idx.shape[0])
+    s = stream if stream is not None else torch.cuda.current_stream(scores.device)
+    st = lib.detk_topk_ragged_noalloc(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len), int(k),
+                                      _ptr(out_idx), _ptr(out_val), ctypes.c_void_p(s.cuda_stream))
+    if st != DETK_OK:
+        raise DetkError(st, "detk_topk_ragged_noalloc")
+    return out_idx, out_val

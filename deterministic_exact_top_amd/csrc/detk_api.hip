@@ -12,6 +12,13 @@
 #include "../../include/detk.h"
 #include "topk_device.hpp"
 
+// Workspace of detk_topk_ragged_noalloc: one array per GPU the library runs on, held until
+// the process ends.  Zero when the code object loads; every call leaves the words that
+// must start at zero (the per-row counters) at zero again, so it is always ready.  In
+// host code the name is a stand-in, never a device address: kernels get the address
+// hipGetSymbolAddress returned for the current device (DeviceInfo::scratch).
+static __device__ __align__(256) unsigned char scratch[DETK_SCRATCH_BYTES];
+
 namespace {
 
 using detk::Params;
@@ -54,6 +61,7 @@ struct DeviceInfo {
     int cus = 0;
     size_t max_lds = 0;
     int split_occ[2] = {};   // workgroups per CU of the 16K-element split tile, k <= 2048 / k <= 4096
+    void* scratch = nullptr; // this device's copy of `scratch` (device address)
 };
 
 std::mutex g_mu;
@@ -107,6 +115,9 @@ int device_info(int device, DeviceInfo* out) {
             prepare_all<32768>(&e);
             d.split_occ[0] = split_occupancy<kSplitTile, 2048>();
             d.split_occ[1] = split_occupancy<kSplitTile, 4096>();
+            // (with this device current: each GPU holds its own copy at its own address)
+            if (e == hipSuccess) e = hipGetSymbolAddress(&d.scratch, HIP_SYMBOL(scratch));
+            if (e == hipSuccess && d.scratch == nullptr) e = hipErrorInvalidSymbol;
         }
         if (cur != device) (void)hipSetDevice(cur);
         if (e != hipSuccess) return DETK_ERR_HIP;
@@ -246,9 +257,10 @@ hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
     }
 }
 
-// The operation on the caller's workspace.  Allocates nothing.
+// The operation, on the caller's workspace or (use_scratch) on the device's scratch array.
+// Allocates nothing in either case.
 int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B, int32_t max_len, int k,
-        int32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+        int32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes, bool use_scratch, void* stream_ptr) {
     if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
     if (B > 0 && (!scores || !out_idx)) return DETK_ERR_INVALID_ARG;
     if (k > DETK_MAX_K || max_len > DETK_MAX_LEN) return DETK_ERR_UNSUPPORTED;
@@ -261,6 +273,10 @@ int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, 
     Plan pl;
     st = make_plan(dev, B, k, max_len, &pl);
     if (st != DETK_OK) return st;
+    if (use_scratch) {
+        workspace = dev.scratch;
+        workspace_bytes = DETK_SCRATCH_BYTES;
+    }
     size_t data_off = 0;
     if (pl.multi) {
         data_off = data_offset(workspace_bytes);
@@ -342,7 +358,13 @@ size_t detk_workspace_size(int device, int B, int k, int32_t max_len) {
 int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                      int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
                      size_t workspace_bytes, void* stream_ptr) {
-    return run(scores, row_starts, lengths, B, max_len, k, out_idx, out_val, workspace, workspace_bytes, stream_ptr);
+    return run(scores, row_starts, lengths, B, max_len, k, out_idx, out_val, workspace, workspace_bytes, false,
+               stream_ptr);
+}
+
+int detk_topk_ragged_noalloc(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
+                             int32_t max_len, int k, int32_t* out_idx, float* out_val, void* stream_ptr) {
+    return run(scores, row_starts, lengths, B, max_len, k, out_idx, out_val, nullptr, 0, true, stream_ptr);
 }
 
 const char* detk_status_string(int status) {

@@ -120,6 +120,29 @@ int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32
                      int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Bytes of the per-GPU scratch array behind detk_topk_ragged_noalloc (16 MiB). */
+#define DETK_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * detk_topk_ragged_noalloc -- detk_topk_ragged without a workspace argument, for callers
+ * that cannot allocate device memory at all (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It computes the same result with the same
+ * kernels; rows longer than one workgroup tile use a scratch array of
+ * DETK_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
+ * ends (its address is taken once per device at the library's first call there).  No
+ * call allocates or frees anything, and the call is enqueued on `stream` like
+ * detk_topk_ragged.
+ *   Arguments, outputs and errors are those of detk_topk_ragged, except:
+ *   DETK_ERR_WORKSPACE  the call would need more workspace than DETK_SCRATCH_BYTES
+ *                       (detk_workspace_size() > DETK_SCRATCH_BYTES), found on the host
+ *                       before any launch; every output is left untouched.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ *   streams, or two host threads, without ordering between them) race and give
+ *   undefined results.  Each call leaves the array ready for the next one.
+ */
+int detk_topk_ragged_noalloc(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
+                             int32_t max_len, int k, int32_t* out_idx, float* out_val, void* stream);
+
 /*
  * detk_status_string -- human-readable text for a status code, naming the condition
  * that produced it (static storage; "unknown detk status" for other values).  The pages'
