@@ -48,6 +48,11 @@ def _load():
         ]
         lib.detk_oracle_key.restype = ctypes.c_uint32
         lib.detk_oracle_key.argtypes = [ctypes.c_uint32]
+        lib.detk_oracle_index_transform.restype = ctypes.c_int
+        lib.detk_oracle_index_transform.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+        ]
         _lib = lib
     return _lib
 
@@ -108,3 +113,25 @@ def topk_ragged(scores, row_starts, lengths, k: int, max_len: int | None = None,
 def key_of_bits(bits: int) -> int:
     """The oracle's total-order key of one float32 bit pattern."""
     return int(_load().detk_oracle_key(ctypes.c_uint32(bits & 0xFFFFFFFF)))
+
+
+INDEX_LOCAL, INDEX_OFFSET, INDEX_PAGE_TABLE = 0, 1, 2
+
+
+def index_transform(local_idx, mode: int, offsets=None, page_table=None, page_size: int = 1):
+    """Transform a selection's local indices (``(B, k)`` int32, -1 padding), as the oracle
+    writes it out (see ``detk_oracle_index_transform``): mode 1 adds ``offsets[b]``; mode 2
+    maps through ``page_table`` (``(B, pages)`` int32, pages of ``page_size`` tokens).
+    Returns a new ``(B, k)`` int32 array; -1 stays -1."""
+    li = np.ascontiguousarray(local_idx, dtype=np.int32)
+    B, k = li.shape
+    off = None if offsets is None else np.ascontiguousarray(offsets, dtype=np.int32)
+    pt = None if page_table is None else np.ascontiguousarray(page_table, dtype=np.int32)
+    stride = 0 if pt is None else (int(pt.shape[1]) if pt.ndim == 2 else 0)
+    out = np.empty_like(li)
+    rc = _load().detk_oracle_index_transform(
+        li.ctypes.data, int(B), int(k), int(mode), None if off is None else off.ctypes.data,
+        None if pt is None else pt.ctypes.data, int(stride), int(page_size), out.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle index transform: bad arguments")
+    return out

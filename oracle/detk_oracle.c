@@ -185,3 +185,43 @@ int detk_oracle_topk_ragged(const uint32_t* scores, const int32_t* row_starts, c
 
 /* The key of one bit pattern, exported so tests can pin the mapping itself. */
 uint32_t detk_oracle_key(uint32_t bits) { return oracle_total_order_key(bits); }
+
+/*
+ * Index transform of a selection -- the serving stacks' step right after top-k selection
+ * (SGLang PR #31115, "Modifications": the deterministic backend returns local indices and
+ * leaves the fused page-table transforms to a separate step; vLLM PR #55872, GB10 failure
+ * trace: FlashInfer's ragged top-k with its transform, top_k_ragged_transform).  Written
+ * out slot by slot, for a slot of row b holding a local index j >= 0:
+ *   mode 1 (offset):     offsets[b] + j                      (an index into a packed buffer)
+ *   mode 2 (page table): page_table[b * stride + j / page_size] * page_size + j % page_size
+ *                        (the physical slot of the row's j-th logical token, pages of
+ *                        page_size tokens)
+ *   mode 0:              j
+ * A slot holding -1 (padding) stays -1.
+ * Returns 0, or 1 on bad arguments.
+ */
+int detk_oracle_index_transform(const int32_t* local_idx, int B, int k, int mode, const int32_t* offsets,
+                                const int32_t* page_table, int64_t stride, int32_t page_size, int32_t* out)
+{
+    if (B < 0 || k < 1 || !local_idx || !out || mode < 0 || mode > 2)
+        return 1;
+    if (mode == 1 && !offsets)
+        return 1;
+    if (mode == 2 && (!page_table || page_size < 1 || stride < 0))
+        return 1;
+    for (int b = 0; b < B; ++b) {
+        for (int t = 0; t < k; ++t) {
+            int32_t j = local_idx[(int64_t)b * k + t];
+            int32_t v = j;
+            if (j >= 0 && mode == 1)
+                v = offsets[b] + j;
+            if (j >= 0 && mode == 2) {
+                int32_t page = j / page_size;
+                int32_t within = j % page_size;
+                v = page_table[(int64_t)b * stride + page] * page_size + within;
+            }
+            out[(int64_t)b * k + t] = v;
+        }
+    }
+    return 0;
+}
