@@ -81,7 +81,7 @@ def cpu_threads() -> int:
 ROUNDS = 7  # timed rounds of `steps` calls: the first is the headline, all give median and min
 
 
-def time_gpu(wl, steps, warmup, rotate, rounds=ROUNDS):
+def time_gpu(wl, steps, warmup, rotate, rounds=ROUNDS, call_kw=None):
     """Warm up, then time `rounds` rounds of `steps` back-to-back calls.  Round 1 -- the
     `steps` calls right after the `warmup` calls -- is the headline figure; the later
     rounds give the median and the min per call.  Returns the timings and the outputs of
@@ -100,9 +100,11 @@ def time_gpu(wl, steps, warmup, rotate, rounds=ROUNDS):
     ws = detk.new_workspace(wl.B, wl.k, wl.max_len, dev)
     stream = torch.cuda.current_stream(dev)
 
+    kw = {key: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v) for key, v in (call_kw or {}).items()}
+
     def step(i):
         detk.topk_ragged(copies[i % rotate], rs, ln, wl.k, max_len=wl.max_len, out_idx=out_i, out_val=out_v,
-                         workspace=ws, stream=stream)
+                         workspace=ws, stream=stream, **kw)
 
     for i in range(warmup):
         step(i)
@@ -289,12 +291,15 @@ def copy_probe(nbytes: int, reps: int) -> None:
 SECONDARY = "long_context_8x262144"
 
 
-def parity_check(wl, outputs) -> dict:
+def parity_check(wl, outputs, transform=None) -> dict:
     """The timed calls' outputs (last call of the first round) against the oracle's, byte
-    for byte, on every row."""
+    for byte, on every row (after the oracle's index transform when one is fused)."""
     import oracle
     gi, gv = outputs
     oi, ov = oracle.topk_ragged(wl.scores, wl.row_starts, wl.lengths, wl.k, wl.max_len, threads=cpu_threads())
+    if transform is not None:
+        oi = oracle.index_transform(oi, transform["mode"], offsets=transform.get("index_offsets"),
+                                    page_table=transform.get("page_table"), page_size=transform.get("page_size", 1))
     same_i, same_v = bool(np.array_equal(gi, oi)), bool(np.array_equal(gv, ov))
     digest = lambda a, b: hashlib.sha256(np.ascontiguousarray(a).tobytes() + np.ascontiguousarray(b).tobytes()
                                          ).hexdigest()[:16]
@@ -302,16 +307,32 @@ def parity_check(wl, outputs) -> dict:
             "oracle_sha256_16": digest(oi, ov), "what": "out_idx and out_val bits of the last call of round 1"}
 
 
-def measure(wl, steps, warmup, rotate) -> dict:
+def make_transform(wl, kind: str, page_size: int):
+    """The fused index transform for a workload: offsets = the rows' starts in the packed
+    buffer (absolute indices), or one shared page table of randomly placed pages (the query
+    rows of one sequence).  Returns (keyword arguments for the call, oracle description)."""
+    if kind == "none":
+        return None, None
+    rng = np.random.default_rng(17)
+    if kind == "offset":
+        offs = wl.row_starts.astype(np.int32)
+        return {"index_offsets": offs}, {"mode": 1, "index_offsets": offs}
+    pages = -(-wl.max_len // page_size)
+    pt = rng.permutation(pages + 64)[:pages].astype(np.int32)
+    return {"page_table": pt, "page_size": page_size}, {"mode": 2, "page_table": pt, "page_size": page_size}
+
+
+def measure(wl, steps, warmup, rotate, transform_kind="none", page_size=64) -> dict:
     """Time one workload (rounds of `steps` calls after `warmup` calls) and check the timed
     outputs; the roofline object comes from round 1."""
+    call_kw, xf = make_transform(wl, transform_kind, page_size)
     algo = wl.algorithmic_bytes()
     rotate = rotate or max(1, -(-2 * MALL_BYTES // max(wl.scores.nbytes, 1)))
     rotate = min(rotate, 200)
     log("timing %s: %d rounds of %d steps (+%d warmup), %d input copies" % (wl.name, ROUNDS, steps, warmup, rotate))
-    walls, avgs, launch_ms, ws_bytes, outputs = time_gpu(wl, steps, warmup, rotate)
+    walls, avgs, launch_ms, ws_bytes, outputs = time_gpu(wl, steps, warmup, rotate, call_kw=call_kw)
     log("checking the timed outputs against the oracle")
-    parity = parity_check(wl, outputs)
+    parity = parity_check(wl, outputs, xf)
     per_round_us = [a * 1e3 for a in avgs]
     achieved = algo / (avgs[0] * 1e-3) / 1e9
     return {
@@ -353,6 +374,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=0,
                     help="input copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--index-transform", choices=["none", "offset", "page_table"], default="none",
+                    help="fuse the index transform into the call (offsets: the rows' starts; page table: one "
+                         "shared table of randomly placed pages)")
+    ap.add_argument("--page-size", type=int, default=64)
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the long-context workload measured beside the headline one")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
@@ -373,7 +398,7 @@ def main():
     import workloads as W
     log("generating %s" % args.workload)
     wl = W.full(args.workload)
-    m = measure(wl, args.steps, args.warmup, args.rotate)
+    m = measure(wl, args.steps, args.warmup, args.rotate, args.index_transform, args.page_size)
     ms_per_step = m["ms_per_step"]
     score_gbps = 4.0 * wl.sum_n / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -392,6 +417,8 @@ def main():
         "config": {
             "workload": wl.name, "B": wl.B, "max_len": wl.max_len, "k": wl.k, "sum_n": wl.sum_n,
             "input_copies_rotated": m["rotate"], "parallelism": "none (1 GPU)",
+            "index_transform": args.index_transform if args.index_transform == "none" else
+            "%s%s" % (args.index_transform, " (page size %d)" % args.page_size if args.index_transform == "page_table" else ""),
         },
         "score_gbps": score_gbps,
         "score_frac_of_hbm_peak": score_gbps / HBM_PEAK_GBPS,
@@ -402,7 +429,7 @@ def main():
     if args.workload != SECONDARY and not args.no_secondary:
         log("generating %s (secondary)" % SECONDARY)
         wl2 = W.full(SECONDARY)
-        m2 = measure(wl2, max(args.steps, 200), args.warmup, 0)
+        m2 = measure(wl2, max(args.steps, 200), args.warmup, 0, args.index_transform, args.page_size)
         result["secondary"] = {
             "workload": wl2.name, "B": wl2.B, "max_len": wl2.max_len, "k": wl2.k, "sum_n": wl2.sum_n,
             "steps": max(args.steps, 200), "warmup": args.warmup, "input_copies_rotated": m2["rotate"],

@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = [
-    "topk_ragged", "topk_ragged_noalloc", "workspace_size", "new_workspace", "can_implement", "status_string", "debug_set",
+    "topk_ragged", "topk_ragged_noalloc", "workspace_size", "IndexTransform", "new_workspace", "can_implement", "status_string", "debug_set",
     "library_path", "load_library", "DETK_MAX_K", "DETK_MAX_LEN", "DetkError",
 ]
 
@@ -27,6 +27,13 @@ DETK_WORKSPACE_UNSUPPORTED = (1 << 64) - 1  # SIZE_MAX: the configuration cannot
 DETK_SCRATCH_BYTES = 16 << 20  # the per-GPU scratch array behind topk_ragged_noalloc
 DETK_OK, DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, DETK_ERR_WORKSPACE, DETK_ERR_HIP = range(5)
 DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE, DETK_DEBUG_FAST = 1, 2, 3, 4
+DETK_INDEX_LOCAL, DETK_INDEX_OFFSET, DETK_INDEX_PAGE_TABLE = 0, 1, 2
+
+
+class IndexTransform(ctypes.Structure):
+    """detk_index_transform (include/detk.h): the index each selected local index j becomes."""
+    _fields_ = [("mode", ctypes.c_int32), ("page_size", ctypes.c_int32), ("offsets", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("page_table_stride", ctypes.c_int64)]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -59,6 +66,9 @@ def load_library():
     lib.detk_workspace_size.restype = sz
     lib.detk_topk_ragged.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.detk_topk_ragged.restype = ctypes.c_int
+    lib.detk_topk_ragged_transform.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int,
+                                               ctypes.POINTER(IndexTransform), vp, vp, vp, sz, vp]
+    lib.detk_topk_ragged_transform.restype = ctypes.c_int
     lib.detk_topk_ragged_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp]
     lib.detk_topk_ragged_noalloc.restype = ctypes.c_int
     lib.detk_status_string.argtypes = [ctypes.c_int]
@@ -127,7 +137,7 @@ def read_probe(data, out, stream=None) -> None:
 
 def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: int | None = None,
                 out_idx=None, out_val=None, workspace=None, with_values: bool = True, B: int | None = None,
-                stream=None):
+                stream=None, index_offsets=None, page_table=None, page_size: int = 1):
     """Exact canonical top-k of each ragged row.
 
     scores      float32 CUDA tensor, contiguous.  2-D (B, L): rows are the matrix rows
@@ -139,6 +149,11 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
     max_len     host-known bound on every row length (never read from the device).
     workspace   uint8 CUDA tensor from new_workspace() (zero-filled before its first use;
                 every call leaves it zero-filled), or None to allocate one here.
+    index_offsets  int32 CUDA tensor (B,): write index_offsets[b] + j for a selected local j
+                (detk_topk_ragged_transform, DETK_INDEX_OFFSET).
+    page_table  int32 CUDA tensor (B, pages), or (pages,) shared by every row: write the
+                physical slot page_table[b, j // page_size] * page_size + j % page_size
+                instead (DETK_INDEX_PAGE_TABLE).  At most one of the two.
     Returns (out_idx int32 (B, k), out_val float32 (B, k) or None).  All allocation
     happens here, before the call, so a captured graph can reuse preallocated
     out_idx / out_val / workspace passed in by the caller.
@@ -176,12 +191,28 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
         # (zero-filled: the library needs a workspace zeroed before its first use)
         workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
-    st = lib.detk_topk_ragged(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len), int(k),
-                              _ptr(out_idx), _ptr(out_val) if with_values else None,
-                              _ptr(workspace) if need else None, int(workspace.numel()) if need else 0,
-                              ctypes.c_void_p(s.cuda_stream))
+    args = (_ptr(out_idx), _ptr(out_val) if with_values else None, _ptr(workspace) if need else None,
+            int(workspace.numel()) if need else 0, ctypes.c_void_p(s.cuda_stream))
+    if index_offsets is None and page_table is None:
+        st = lib.detk_topk_ragged(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len), int(k), *args)
+        what = "detk_topk_ragged"
+    else:
+        if index_offsets is not None and page_table is not None:
+            raise ValueError("pass index_offsets or page_table, not both")
+        xf = IndexTransform()
+        for name, t in (("index_offsets", index_offsets), ("page_table", page_table)):
+            if t is not None and (t.dtype != torch.int32 or t.device != dev or not t.is_contiguous()):
+                raise ValueError("%s must be a contiguous int32 tensor on the scores' device" % name)
+        if index_offsets is not None:
+            xf.mode, xf.page_size, xf.offsets = DETK_INDEX_OFFSET, 1, index_offsets.data_ptr()
+        else:
+            xf.mode, xf.page_size, xf.page_table = DETK_INDEX_PAGE_TABLE, int(page_size), page_table.data_ptr()
+            xf.page_table_stride = int(page_table.shape[1]) if page_table.dim() == 2 else 0
+        st = lib.detk_topk_ragged_transform(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len),
+                                            int(k), ctypes.byref(xf), *args)
+        what = "detk_topk_ragged_transform"
     if st != DETK_OK:
-        raise DetkError(st, "detk_topk_ragged")
+        raise DetkError(st, what)
     return out_idx, (out_val if with_values else None)
 
 

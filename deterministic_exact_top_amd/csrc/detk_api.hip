@@ -44,10 +44,16 @@ template <> struct Shape<8192, true> { static constexpr int NT = 1024, EPT = 8, 
 template <> struct Shape<16384, true> { static constexpr int NT = 1024, EPT = 16, MINW = 4; };
 template <> struct Shape<32768, true> { static constexpr int NT = 1024, EPT = 32, MINW = 4; };
 
+// Waves per SIMD a kernel's registers must allow: the shape's, except where the LDS of the
+// k <= 4096 layouts already limits a CU to two 512-thread workgroups (4 waves per SIMD), so a
+// tighter register cap would only spill.
+template <int TILE, int KMAX, bool MULTI>
+constexpr int min_waves() { return (!MULTI && TILE == 16384 && KMAX == 4096) ? 4 : Shape<TILE, MULTI>::MINW; }
+
 template <int TILE, int KMAX, bool MULTI>
 const void* kernel_ptr() {
     using S = Shape<TILE, MULTI>;
-    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>);
+    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>()>);
 }
 
 template <int TILE, int KMAX, bool MULTI>
@@ -226,8 +232,8 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
 template <int TILE, int KMAX, bool MULTI>
 hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
     using S = Shape<TILE, MULTI>;
-    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, S::MINW>), dim3(grid), dim3(S::NT), lds,
-                       stream, p);
+    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>()>), dim3(grid),
+                       dim3(S::NT), lds, stream, p);
     return hipGetLastError();
 }
 
@@ -260,10 +266,26 @@ hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
 // The operation, on the caller's workspace or (use_scratch) on the device's scratch array.
 // Allocates nothing in either case.
 int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B, int32_t max_len, int k,
-        int32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes, bool use_scratch, void* stream_ptr) {
+        const detk_index_transform* xf, int32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes,
+        bool use_scratch, void* stream_ptr) {
     if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
     if (B > 0 && (!scores || !out_idx)) return DETK_ERR_INVALID_ARG;
     if (k > DETK_MAX_K || max_len > DETK_MAX_LEN) return DETK_ERR_UNSUPPORTED;
+    int32_t xf_shift = -1;
+    if (xf) {
+        if (xf->mode < DETK_INDEX_LOCAL || xf->mode > DETK_INDEX_PAGE_TABLE) return DETK_ERR_INVALID_ARG;
+        if (xf->mode == DETK_INDEX_OFFSET && B > 0 && !xf->offsets) return DETK_ERR_INVALID_ARG;
+        if (xf->mode == DETK_INDEX_PAGE_TABLE) {
+            if ((B > 0 && !xf->page_table) || xf->page_size < 1) return DETK_ERR_INVALID_ARG;
+            // every page any window can touch must be in the row's part of the table (stride 0:
+            // every row reads the same table)
+            if (xf->page_table_stride < 0 ||
+                (xf->page_table_stride != 0 &&
+                 xf->page_table_stride < ((int64_t)max_len + xf->page_size - 1) / xf->page_size))
+                return DETK_ERR_INVALID_ARG;
+            if ((xf->page_size & (xf->page_size - 1)) == 0) xf_shift = __builtin_ctz((unsigned)xf->page_size);
+        }
+    }
     if (B == 0) return DETK_OK;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return DETK_ERR_HIP;
@@ -298,6 +320,12 @@ int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, 
     p.fast = g_fast;
     p.out_idx = out_idx;
     p.out_val = reinterpret_cast<uint32_t*>(out_val);
+    p.xf_mode = xf ? xf->mode : DETK_INDEX_LOCAL;
+    p.xf_page = xf && xf->mode == DETK_INDEX_PAGE_TABLE ? xf->page_size : 1;
+    p.xf_shift = xf_shift;
+    p.xf_offsets = xf && xf->mode == DETK_INDEX_OFFSET ? xf->offsets : nullptr;
+    p.xf_table = xf && xf->mode == DETK_INDEX_PAGE_TABLE ? xf->page_table : nullptr;
+    p.xf_stride = xf && xf->mode == DETK_INDEX_PAGE_TABLE ? xf->page_table_stride : 0;
     p.ws_ctl = nullptr;
     p.ws_ecnt = nullptr;
     p.ws_cand = nullptr;
@@ -358,13 +386,20 @@ size_t detk_workspace_size(int device, int B, int k, int32_t max_len) {
 int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                      int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
                      size_t workspace_bytes, void* stream_ptr) {
-    return run(scores, row_starts, lengths, B, max_len, k, out_idx, out_val, workspace, workspace_bytes, false,
-               stream_ptr);
+    return run(scores, row_starts, lengths, B, max_len, k, nullptr, out_idx, out_val, workspace, workspace_bytes,
+               false, stream_ptr);
+}
+
+int detk_topk_ragged_transform(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
+                               int32_t max_len, int k, const detk_index_transform* transform, int32_t* out_idx,
+                               float* out_val, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+    return run(scores, row_starts, lengths, B, max_len, k, transform, out_idx, out_val, workspace, workspace_bytes,
+               false, stream_ptr);
 }
 
 int detk_topk_ragged_noalloc(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                              int32_t max_len, int k, int32_t* out_idx, float* out_val, void* stream_ptr) {
-    return run(scores, row_starts, lengths, B, max_len, k, out_idx, out_val, nullptr, 0, true, stream_ptr);
+    return run(scores, row_starts, lengths, B, max_len, k, nullptr, out_idx, out_val, nullptr, 0, true, stream_ptr);
 }
 
 const char* detk_status_string(int status) {

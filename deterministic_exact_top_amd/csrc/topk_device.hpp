@@ -83,6 +83,13 @@ struct Params {
     uint32_t* ws_ecnt;          // B * tiles_per_row: keys equal to P per tile
     uint2* ws_cand;             // B * cand_cap(KMAX): candidates (bits, position in the row)
     uint32_t* ws_tie;           // B * tiles_per_row * TILE / 32: per-tile bitmaps of keys == P
+    // index written for a selected local index j (0 local, 1 offset, 2 page table)
+    int32_t xf_mode;
+    int32_t xf_page;            // page table: tokens per page
+    int32_t xf_shift;           // page table: log2(tokens per page), or -1
+    const int32_t* xf_offsets;  // offset: int32[B]
+    const int32_t* xf_table;    // page table: row b's pages at xf_table[b * xf_stride ...]
+    int64_t xf_stride;
 };
 
 // ----------------------------------------------------------------------------- bits
@@ -586,12 +593,31 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ctr, uint32_t ntiles, uint
 
 // ----------------------------------------------------------------------------- row context
 
+// The index a row writes for its selected local index j: j itself, an offset plus j (an
+// index into a packed buffer), or the physical slot of the row's j-th token through its
+// page table (pages of `ps` tokens).  The mode is uniform across the launch.
+struct IndexOut {
+    int32_t mode;
+    int32_t off;
+    int32_t ps;
+    int32_t shift;
+    const int32_t* pt;
+    __device__ __forceinline__ int32_t operator()(uint32_t j) const {
+        if (mode == 0) return (int32_t)j;
+        if (mode == 1) return off + (int32_t)j;
+        const uint32_t page = shift >= 0 ? j >> shift : j / (uint32_t)ps;
+        const uint32_t within = j - page * (uint32_t)ps;
+        return pt[page] * ps + (int32_t)within;
+    }
+};
+
 struct RowCtx {
     int b, tile, ntiles;
     int32_t n, m, k, nt, j0;
     int64_t base;
     int32_t* oidx;
     uint32_t* oval;
+    IndexOut xo;
 };
 
 // ----------------------------------------------------------------------------- fast path
@@ -789,7 +815,7 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 
 // Order the candidates: the m largest of the c_gt candidates (all of them when
 // c_gt <= m) go to slots [0, min(m, c_gt)) in canonical order through
-// emit(slot, position, bits).  Each thread owns up to CPT candidates: valid(i) says
+// emit(slot, xo(position), bits).  Each thread owns up to CPT candidates: valid(i) says
 // whether its i-th exists, src(i) gives it as (raw bits, position), and live(i)
 // (wave-uniform) whether some lane of the wave has an i-th candidate.
 // The bucket (BucketMap) holding the m-th largest is the threshold; kept candidates
@@ -818,8 +844,8 @@ template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, clas
           class Emit, class Scattered>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             Valid&& valid, Live&& live, uint32_t c_gt, uint32_t m, bool ties,
-                                            const Map& bucket_of, Emit&& emit, Scattered&& scattered,
-                                            bool sort_long = false) {
+                                            const Map& bucket_of, const IndexOut& xo, Emit&& emit,
+                                            Scattered&& scattered, bool sort_long = false) {
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     const int tid = opaque_tid();
@@ -958,7 +984,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     if (sort_all) {  // uniform
         static_assert(LIMITED || (SCAP & (SCAP - 1)) == 0, "the sort pads S to a power of two");
         bitonic_desc_u64<NT>(S, (int)kept);
-        for (uint32_t q = tid; q < mlim; q += NT) emit(q, ~(uint32_t)S[q], bits_of((uint32_t)(S[q] >> 32)));
+        for (uint32_t q = tid; q < mlim; q += NT) emit(q, xo(~(uint32_t)S[q]), bits_of((uint32_t)(S[q] >> 32)));
         return true;
     }
 
@@ -974,12 +1000,15 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         if (q0 + wbase >= kept) break;  // nothing left for this wave
         uint64_t cc[RUNR];
         uint32_t st[RUNR], rank[RUNR];
+        int32_t ox[RUNR];  // the index written for the element (a page-table load is issued here,
+                           // so its latency hides behind the comparisons)
         uint32_t lmax = 0;
 #pragma unroll
         for (int i = 0; i < RUNR; ++i) {
             const uint32_t q = q0 + i * NT + tid;
             const bool in = q < kept;
             cc[i] = S[min(q, kept)];  // S[kept] is zero: no branch around the read
+            ox[i] = in ? xo(~(uint32_t)cc[i]) : 0;
             const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
             const uint32_t en = min((uint32_t)b16[bk], kept);
             const uint32_t s0 = b16[bk + 1];
@@ -999,7 +1028,7 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
 #pragma unroll
         for (int i = 0; i < RUNR; ++i) {
             const uint32_t slot = st[i] + rank[i];
-            if (q0 + i * NT + tid < kept && slot < mlim) emit(slot, ~(uint32_t)cc[i], bits_of((uint32_t)(cc[i] >> 32)));
+            if (q0 + i * NT + tid < kept && slot < mlim) emit(slot, ox[i], bits_of((uint32_t)(cc[i] >> 32)));
         }
     }
     return true;
@@ -1205,8 +1234,9 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
             },
             [&](int i) { return i < RC ? (uint32_t)(64 * i) < c_w : (uint32_t)((i - RC) * NT) < pooled; },
             c_gt, (uint32_t)m, ties, bucket_of,
-            [&](uint32_t slot, uint32_t pos, uint32_t bits) {
-                store_at(r.oidx, slot, (int32_t)pos);
+            r.xo,
+            [&](uint32_t slot, int32_t idx, uint32_t bits) {
+                store_at(r.oidx, slot, idx);
                 if (r.oval) store_at(r.oval, slot, bits);
             },
             scattered, m == nt))
@@ -1233,7 +1263,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
                 while (word && rr < need) {
                     const int bit = __ffs(word) - 1;
                     word &= word - 1;
-                    r.oidx[c_gt + rr] = w * 32 + bit;
+                    r.oidx[c_gt + rr] = r.xo((uint32_t)(w * 32 + bit));
                     if (r.oval) r.oval[c_gt + rr] = vP;
                     ++rr;
                 }
@@ -1279,7 +1309,7 @@ __device__ __forceinline__ void load_row_samples(uint32_t (&sk)[4 * SL], const u
 
 template <int NT, int KMAX, int STAGE>
 __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, uint32_t* oval,
-                          RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap);
+                          IndexOut xo, RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap);
 
 // One tile of a row split over several workgroups.  No workgroup ever waits for another:
 //   - every tile reads the same evenly spaced samples of the whole row and derives the
@@ -1435,7 +1465,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     const uint32_t n_eq = s.ctl[kCtlEq];
     if (!p.fast || c_gt > CAP || c_gt + n_eq < (uint32_t)m) {  // uniform
         __syncthreads();  // (the fallback's LDS overlays the words just read)
-        exact_row<NT, KMAX, kRowStageEntries>(row, n, m, r.k, r.oidx, r.oval, sa.rexact, p.stage_cap);
+        exact_row<NT, KMAX, kRowStageEntries>(row, n, m, r.k, r.oidx, r.oval, r.xo, sa.rexact, p.stage_cap);
         return;
     }
     const bool ties = c_gt < (uint32_t)m;
@@ -1448,9 +1478,9 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     bucket_rank<NT, SS::SCAP, (SS::SCAP + NT - 1) / NT, false, false>(
         s.bucket, s.S, s.wsum, s.ctl, [&](int i) { return gc[tid + i * NT]; },
         [&](int i) { return (uint32_t)(tid + i * NT) < c_gt; }, [&](int i) { return (uint32_t)(i * NT) < c_gt; },
-        c_gt, (uint32_t)m, ties, BucketMapT<true>(L, U),
-        [&](uint32_t slot, uint32_t pos, uint32_t bits) {
-            r.oidx[slot] = (int32_t)pos;
+        c_gt, (uint32_t)m, ties, BucketMapT<true>(L, U), r.xo,
+        [&](uint32_t slot, int32_t idx, uint32_t bits) {
+            r.oidx[slot] = idx;
             if (r.oval) r.oval[slot] = bits;
         },
         [] {});
@@ -1483,7 +1513,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
                 while (word && rr2 < need) {
                     const int bit = __ffs(word) - 1;
                     word &= word - 1;
-                    r.oidx[c_gt + rr2] = wpos + bit;
+                    r.oidx[c_gt + rr2] = r.xo((uint32_t)(wpos + bit));
                     if (r.oval) r.oval[c_gt + rr2] = vP;
                     ++rr2;
                 }
@@ -1503,7 +1533,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
 // boundary ties at T taken in index order by an ordered scan of the row.
 template <int NT, int KMAX, int STAGE>
 __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, uint32_t* oval,
-                          RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap) {
+                          IndexOut xo, RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap) {
     constexpr int EC = 16;
     constexpr int CH = NT * EC;
     constexpr int NW = NT / 64;
@@ -1632,7 +1662,7 @@ __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, 
     const uint32_t nA = min(s.ctr[1], cnt_gt);
     bitonic_desc<NT>(A, (int)nA);
     for (uint32_t q = tid; q < nA; q += NT) {
-        oidx[q] = (int32_t)s.apos[q];
+        oidx[q] = xo(s.apos[q]);
         if (oval) oval[q] = bits_of(s.akey[q]);
     }
 
@@ -1654,7 +1684,7 @@ __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, 
             while (mk && rr < need) {
                 const int c = __ffs(mk) - 1;
                 mk &= mk - 1;
-                oidx[cnt_gt + rr] = c0 + t4 + c;
+                oidx[cnt_gt + rr] = xo((uint32_t)(c0 + t4 + c));
                 if (oval) oval[cnt_gt + rr] = vT;
                 ++rr;
             }
@@ -1851,7 +1881,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
             const int bit = __ffs(word) - 1;
             word &= word - 1;
             const int32_t j = j0 + w * 32 + bit;
-            oidx[cnt_gt + rr] = j;
+            oidx[cnt_gt + rr] = r.xo((uint32_t)j);
             if (oval) oval[cnt_gt + rr] = vT;
             ++rr;
         }
@@ -1862,7 +1892,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     const uint32_t nA = min(s.ctr[1], cnt_gt);
     bitonic_desc<NT>(A, (int)nA);
     for (uint32_t q = tid; q < nA; q += NT) {
-        oidx[q] = (int32_t)s.apos[q];
+        oidx[q] = r.xo(s.apos[q]);
         if (oval) oval[q] = bits_of(s.akey[q]);
     }
     write_padding<NT>(oidx, oval, m, k);
@@ -1887,6 +1917,11 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     r.oval = p.out_val ? p.out_val + (int64_t)b * r.k : nullptr;
     r.j0 = tile * TILE;
     r.nt = min(TILE, r.n - r.j0);
+    r.xo.mode = p.xf_mode;
+    r.xo.off = p.xf_mode == 1 ? p.xf_offsets[b] : 0;
+    r.xo.ps = p.xf_page;
+    r.xo.shift = p.xf_shift;
+    r.xo.pt = p.xf_mode == 2 ? p.xf_table + (int64_t)b * p.xf_stride : nullptr;
     return r;
 }
 

@@ -120,6 +120,45 @@ int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32
                      int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * Index transform fused into the stores of a call (detk_topk_ragged_transform): the
+ * serving stacks turn a row's selected local indices into buffer positions right after
+ * selection -- SGLang PR #31115, "Modifications" (the fused page-table transforms that
+ * follow the selection step) and vLLM PR #55872, GB10 failure trace (FlashInfer's
+ * top_k_ragged_transform).  For a selected local index j of row b the call writes
+ *   DETK_INDEX_LOCAL       j
+ *   DETK_INDEX_OFFSET      offsets[b] + j   (an index into a packed buffer of all rows)
+ *   DETK_INDEX_PAGE_TABLE  page_table[b * page_table_stride + j / page_size] * page_size
+ *                          + j % page_size  (the physical slot of the row's j-th token)
+ * in place of j; -1 padding and out_val are unchanged, and so is the order.
+ */
+#define DETK_INDEX_LOCAL 0
+#define DETK_INDEX_OFFSET 1
+#define DETK_INDEX_PAGE_TABLE 2
+typedef struct detk_index_transform {
+    int32_t mode;              /* DETK_INDEX_LOCAL, DETK_INDEX_OFFSET or DETK_INDEX_PAGE_TABLE        */
+    int32_t page_size;         /* DETK_INDEX_PAGE_TABLE: tokens per page, >= 1 (powers of two shift) */
+    const int32_t* offsets;    /* DETK_INDEX_OFFSET: device int32[B]                                 */
+    const int32_t* page_table; /* DETK_INDEX_PAGE_TABLE: device int32, row b's pages at
+                                  page_table[b * page_table_stride ...]                              */
+    int64_t page_table_stride; /* entries per row, >= ceil(max_len / page_size); 0: every row reads
+                                  the same table (the query rows of one sequence)                    */
+} detk_index_transform;
+
+/*
+ * detk_topk_ragged_transform -- detk_topk_ragged with the index transform above applied in
+ * the kernels' own stores (one pass: no second kernel rewrites out_idx).  `transform` is a
+ * host pointer read during the call (NULL = DETK_INDEX_LOCAL); the offsets and page table
+ * it names are device arrays owned by the caller and trusted like the row metadata (every
+ * entry a window reaches must exist, and the written index must fit int32).  Errors are
+ * those of detk_topk_ragged, plus DETK_ERR_INVALID_ARG for an unknown mode, a NULL array
+ * the mode needs, page_size < 1, or a page_table_stride that is negative or neither 0 nor
+ * >= ceil(max_len / page_size), all found on the host before any launch.
+ */
+int detk_topk_ragged_transform(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
+                               int32_t max_len, int k, const detk_index_transform* transform, int32_t* out_idx,
+                               float* out_val, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the per-GPU scratch array behind detk_topk_ragged_noalloc (16 MiB). */
 #define DETK_SCRATCH_BYTES ((size_t)16 << 20)
 
