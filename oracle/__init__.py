@@ -48,6 +48,13 @@ def _load():
         ]
         lib.detk_oracle_key.restype = ctypes.c_uint32
         lib.detk_oracle_key.argtypes = [ctypes.c_uint32]
+        lib.detk_oracle_key16.restype = ctypes.c_uint32
+        lib.detk_oracle_key16.argtypes = [ctypes.c_uint16]
+        lib.detk_oracle_topk_ragged16.restype = ctypes.c_int
+        lib.detk_oracle_topk_ragged16.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint16, ctypes.c_int,
+        ]
         lib.detk_oracle_index_transform.restype = ctypes.c_int
         lib.detk_oracle_index_transform.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -135,3 +142,38 @@ def index_transform(local_idx, mode: int, offsets=None, page_table=None, page_si
     if rc != 0:
         raise RuntimeError("oracle index transform: bad arguments")
     return out
+
+
+PAD16 = {"f16": 0xFC00, "bf16": 0xFF80}  # -inf of each 16-bit format
+
+
+def topk_ragged16(scores, row_starts, lengths, k: int, max_len: int | None = None, fmt: str = "bf16",
+                  B: int | None = None, threads: int | None = None):
+    """The oracle on 16-bit floats (``fmt`` "f16" or "bf16"; ``scores`` float16 or uint16 bit
+    patterns).  Returns ``(out_idx int32 (B, k), out_val uint16 bits (B, k))``; padded value
+    slots hold the format's -inf."""
+    a = np.ascontiguousarray(scores).reshape(-1)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("scores must be float16 or uint16 bit patterns, got %s" % a.dtype)
+    rs = None if row_starts is None else np.ascontiguousarray(row_starts, dtype=np.int32)
+    ln = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32)
+    if B is None:
+        B = int(ln.shape[0]) if ln is not None else int(rs.shape[0])
+    if max_len is None:
+        max_len = int(ln.max()) if ln is not None and ln.size else 0
+    out_idx = np.empty((B, k), dtype=np.int32)
+    out_val = np.empty((B, k), dtype=np.uint16)
+    rc = _load().detk_oracle_topk_ragged16(
+        a.ctypes.data if a.size else None, None if rs is None else rs.ctypes.data,
+        None if ln is None else ln.ctypes.data, int(B), int(max_len), int(k), out_idx.ctypes.data,
+        out_val.ctypes.data, PAD16[fmt], int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle failed (status %d)" % rc)
+    return out_idx, out_val
+
+
+def key16_of_bits(bits: int) -> int:
+    """The oracle's total-order key of one 16-bit float pattern."""
+    return int(_load().detk_oracle_key16(ctypes.c_uint16(bits & 0xFFFF)))

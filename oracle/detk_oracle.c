@@ -29,6 +29,7 @@
  *   m = min(k, n), write -1 / -inf after them.
  *
  * No floating-point operation ever touches a score: values are copied as bits.
+ * 16-bit rows (binary16 or bfloat16) are ordered the same way on their 16 bits.
  * Rows are split over POSIX threads in contiguous blocks; each row is
  * independent, so the thread count does not change the result.
  */
@@ -62,14 +63,27 @@ static int oracle_cmp(const void* pa, const void* pb)
     return 0;
 }
 
+/* The same order for 16-bit floats (binary16 or bfloat16; both keep the sign in the top
+ * bit): a negative pattern is complemented, a positive one gets its sign bit set, so
+ * unsigned order is IEEE totalOrder on the 16-bit patterns. */
+static uint32_t oracle_total_order_key16(uint16_t bits)
+{
+    if (bits & 0x8000u)
+        return (uint16_t)~bits;
+    return bits | 0x8000u;
+}
+
 typedef struct {
     const uint32_t* scores;
+    const uint16_t* scores16;   /* 16-bit rows instead of scores (then out_val16, pad16) */
     const int32_t* row_starts;
     const int32_t* lengths;
     int32_t max_len;
     int k;
     int32_t* out_idx;
     uint32_t* out_val;
+    uint16_t* out_val16;
+    uint16_t pad16;
     int row_begin;
     int row_end;
     int status;
@@ -84,6 +98,23 @@ static void oracle_row(const oracle_job* job, int b, oracle_item* items)
         len = job->max_len;
     int32_t n = (int32_t)len;
     int64_t start = job->row_starts ? (int64_t)job->row_starts[b] : (int64_t)b * job->max_len;
+    if (job->scores16) {
+        const uint16_t* row16 = job->scores16 + start;
+        for (int32_t j = 0; j < n; ++j) {
+            items[j].key = oracle_total_order_key16(row16[j]);
+            items[j].pos = j;
+        }
+        qsort(items, (size_t)n, sizeof(oracle_item), oracle_cmp);
+        int32_t m = n < job->k ? n : job->k;
+        int32_t* oi = job->out_idx + (int64_t)b * job->k;
+        uint16_t* ov = job->out_val16 ? job->out_val16 + (int64_t)b * job->k : NULL;
+        for (int t = 0; t < job->k; ++t) {
+            oi[t] = t < m ? items[t].pos : -1;
+            if (ov)
+                ov[t] = t < m ? row16[items[t].pos] : job->pad16;
+        }
+        return;
+    }
     const uint32_t* row = job->scores + start;
 
     for (int32_t j = 0; j < n; ++j) {
@@ -124,15 +155,12 @@ static void* oracle_worker(void* arg)
     return NULL;
 }
 
-/*
- * Host pointers only.  scores: float32 bit patterns; out_val may be NULL.
- * Returns 0 on success, 1 on bad arguments or allocation failure.
- */
-int detk_oracle_topk_ragged(const uint32_t* scores, const int32_t* row_starts, const int32_t* lengths,
-                            int B, int32_t max_len, int k, int32_t* out_idx, uint32_t* out_val,
-                            int nthreads)
+/* Both entry points: 32-bit rows (scores, out_val) or 16-bit rows (scores16, out_val16). */
+static int oracle_run(const uint32_t* scores, const uint16_t* scores16, const int32_t* row_starts,
+                      const int32_t* lengths, int B, int32_t max_len, int k, int32_t* out_idx,
+                      uint32_t* out_val, uint16_t* out_val16, uint16_t pad16, int nthreads)
 {
-    if (B < 0 || k < 1 || max_len < 0 || !out_idx || (B > 0 && !scores))
+    if (B < 0 || k < 1 || max_len < 0 || !out_idx || (B > 0 && !scores && !scores16))
         return 1;
     if (B == 0)
         return 0;
@@ -152,6 +180,9 @@ int detk_oracle_topk_ragged(const uint32_t* scores, const int32_t* row_starts, c
     for (int t = 0; t < nthreads; ++t) {
         oracle_job* j = &jobs[t];
         j->scores = scores;
+        j->scores16 = scores16;
+        j->out_val16 = out_val16;
+        j->pad16 = pad16;
         j->row_starts = row_starts;
         j->lengths = lengths;
         j->max_len = max_len;
@@ -183,8 +214,32 @@ int detk_oracle_topk_ragged(const uint32_t* scores, const int32_t* row_starts, c
     return status;
 }
 
+/*
+ * Host pointers only.  scores: float32 bit patterns; out_val may be NULL.
+ * Returns 0 on success, 1 on bad arguments or allocation failure.
+ */
+int detk_oracle_topk_ragged(const uint32_t* scores, const int32_t* row_starts, const int32_t* lengths,
+                            int B, int32_t max_len, int k, int32_t* out_idx, uint32_t* out_val,
+                            int nthreads)
+{
+    return oracle_run(scores, NULL, row_starts, lengths, B, max_len, k, out_idx, out_val, NULL, 0, nthreads);
+}
+
+/*
+ * The same for 16-bit floats (binary16 or bfloat16 bit patterns): the order is IEEE
+ * totalOrder on the 16 bits, values are copied as 16 bits, and padded value slots get
+ * pad16 (the format's -inf: 0xFC00 for binary16, 0xFF80 for bfloat16).
+ */
+int detk_oracle_topk_ragged16(const uint16_t* scores, const int32_t* row_starts, const int32_t* lengths,
+                              int B, int32_t max_len, int k, int32_t* out_idx, uint16_t* out_val,
+                              uint16_t pad16, int nthreads)
+{
+    return oracle_run(NULL, scores, row_starts, lengths, B, max_len, k, out_idx, NULL, out_val, pad16, nthreads);
+}
+
 /* The key of one bit pattern, exported so tests can pin the mapping itself. */
 uint32_t detk_oracle_key(uint32_t bits) { return oracle_total_order_key(bits); }
+uint32_t detk_oracle_key16(uint16_t bits) { return oracle_total_order_key16(bits); }
 
 /*
  * Index transform of a selection -- the serving stacks' step right after top-k selection

@@ -222,6 +222,49 @@ def long_context(B: int = 8, L: int = 262144, k: int = 2048, p: float = 0.8, sho
     return Workload(name, buf, starts, lens, L, k)
 
 
+def round_to_16bit(x32: np.ndarray, fmt: str) -> np.ndarray:
+    """float32 values rounded to a 16-bit float format, as uint16 bit patterns: binary16
+    ("f16", numpy's conversion, round to nearest even) or bfloat16 ("bf16": the top half of
+    the float32 bits after round to nearest even; NaNs stay NaN with their sign, quieted)."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    if fmt == "f16":
+        return x32.astype(np.float16).view(np.uint16)
+    u = x32.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x32)
+    rounded[nan] = ((u[nan] >> 16) | 0x0040).astype(np.uint16)
+    return rounded
+
+
+@dataclasses.dataclass
+class Workload16:
+    """A workload's scores rounded to a 16-bit format (same windows, k and row layout)."""
+    name: str
+    fmt: str
+    scores: np.ndarray          # uint16 bit patterns, flat buffer
+    row_starts: np.ndarray
+    lengths: np.ndarray
+    max_len: int
+    k: int
+
+    @property
+    def B(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def sum_n(self) -> int:
+        return int(np.clip(self.lengths.astype(np.int64), 0, self.max_len).sum())
+
+    def algorithmic_bytes(self) -> int:
+        """Scores read once (2 bytes each) + out_idx (4) and out_val (2) written + 8 B metadata per row."""
+        return 2 * self.sum_n + 6 * self.B * self.k + 8 * self.B
+
+
+def to16(wl: Workload, fmt: str) -> Workload16:
+    return Workload16(wl.name + "_" + fmt, fmt, round_to_16bit(wl.scores, fmt), wl.row_starts, wl.lengths,
+                      wl.max_len, wl.k)
+
+
 FULL = {
     "plateau_4x4096": plateau_abs,
     "decode_ragged_64": decode_ragged,
