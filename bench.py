@@ -60,7 +60,7 @@ def kernel_source_sha() -> str:
     """Hash of the kernel sources with comments and whitespace taken out, so that a
     comment edit does not mark counters taken on the same code as stale."""
     h = hashlib.sha256()
-    for name in ("detk_api.hip", "topk_device.hpp"):
+    for name in ("detk_api.hip", "topk_device.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "deterministic_exact_top_amd", "csrc", name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -81,6 +81,17 @@ def cpu_threads() -> int:
 ROUNDS = 7  # timed rounds of `steps` calls: the first is the headline, all give median and min
 
 
+def scores_to_device(wl, dev):
+    """The workload's scores as a CUDA tensor: float32, or float16 / bfloat16 for a 16-bit
+    workload (its uint16 bit patterns reinterpreted)."""
+    import torch
+    fmt = getattr(wl, "fmt", None)
+    if fmt is None:
+        return torch.from_numpy(wl.scores).to(dev)
+    t = torch.from_numpy(wl.scores.view(np.int16)).to(dev)
+    return t.view(torch.float16 if fmt == "f16" else torch.bfloat16)
+
+
 def time_gpu(wl, steps, warmup, rotate, rounds=ROUNDS, call_kw=None):
     """Warm up, then time `rounds` rounds of `steps` back-to-back calls.  Round 1 -- the
     `steps` calls right after the `warmup` calls -- is the headline figure; the later
@@ -92,11 +103,11 @@ def time_gpu(wl, steps, warmup, rotate, rounds=ROUNDS, call_kw=None):
     dev = torch.device("cuda:0")
     copies = []
     for _ in range(rotate):
-        copies.append(torch.from_numpy(wl.scores).to(dev))
+        copies.append(scores_to_device(wl, dev))
     rs = torch.from_numpy(wl.row_starts).to(dev)
     ln = torch.from_numpy(wl.lengths).to(dev)
     out_i = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
-    out_v = torch.empty((wl.B, wl.k), dtype=torch.float32, device=dev)
+    out_v = torch.empty((wl.B, wl.k), dtype=copies[0].dtype, device=dev)
     ws = detk.new_workspace(wl.B, wl.k, wl.max_len, dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -126,7 +137,8 @@ def time_gpu(wl, steps, warmup, rotate, rounds=ROUNDS, call_kw=None):
         walls.append(time.perf_counter() - t0)
         avgs.append(e0.elapsed_time(e1) / steps)
         if r == 0:
-            outputs = (out_i.cpu().numpy(), out_v.cpu().numpy().view(np.uint32))
+            outputs = (out_i.cpu().numpy(), out_v.view(torch.int32 if out_v.element_size() == 4 else torch.int16)
+                       .cpu().numpy().view(np.uint32 if out_v.element_size() == 4 else np.uint16))
     # Then each launch bracketed on its own (for the fastest launch; the event pair around
     # every call adds a little to each).
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -151,25 +163,32 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def oracle_rows(wl, rs, ln, threads):
+    """The oracle (float32 or 16-bit, as the workload is) on the rows (rs, ln)."""
+    import oracle
+    if getattr(wl, "fmt", None) is None:
+        return oracle.topk_ragged(wl.scores, rs, ln, wl.k, wl.max_len, threads=threads)
+    return oracle.topk_ragged16(wl.scores, rs, ln, wl.k, wl.max_len, fmt=wl.fmt, threads=threads)
+
+
 def cpu_baseline(wl, budget_s: float = 15.0):
     """The oracle as it stands, on the host cores, over rows of the same workload."""
-    import oracle
     threads = cpu_threads()
     # Calibrate on a small slice, then size the sample to ~budget_s of CPU work.
     probe = min(wl.B, 64)
     t0 = time.perf_counter()
-    oracle.topk_ragged(wl.scores, wl.row_starts[:probe], wl.lengths[:probe], wl.k, wl.max_len, threads=1)
+    oracle_rows(wl, wl.row_starts[:probe], wl.lengths[:probe], threads=1)
     per_row_cpu = (time.perf_counter() - t0) / probe
     rows = int(min(wl.B, max(probe, budget_s / max(per_row_cpu, 1e-9))))
     sel = np.linspace(0, wl.B - 1, rows).astype(np.int64) if rows < wl.B else np.arange(wl.B)
     rs, ln = wl.row_starts[sel], wl.lengths[sel]
     t0 = time.perf_counter()
-    oracle.topk_ragged(wl.scores, rs, ln, wl.k, wl.max_len, threads=threads)
+    oracle_rows(wl, rs, ln, threads=threads)
     dt = time.perf_counter() - t0
     extra = {}
     if wl.B <= 64 and threads > 1:  # small batches: the single-thread figure as well
         t0 = time.perf_counter()
-        oracle.topk_ragged(wl.scores, rs, ln, wl.k, wl.max_len, threads=1)
+        oracle_rows(wl, rs, ln, threads=1)
         extra["value_1thread"] = rows / (time.perf_counter() - t0)
     return {
         "value": rows / dt,
@@ -296,7 +315,11 @@ def parity_check(wl, outputs, transform=None) -> dict:
     for byte, on every row (after the oracle's index transform when one is fused)."""
     import oracle
     gi, gv = outputs
-    oi, ov = oracle.topk_ragged(wl.scores, wl.row_starts, wl.lengths, wl.k, wl.max_len, threads=cpu_threads())
+    if getattr(wl, "fmt", None) is None:
+        oi, ov = oracle.topk_ragged(wl.scores, wl.row_starts, wl.lengths, wl.k, wl.max_len, threads=cpu_threads())
+    else:
+        oi, ov = oracle.topk_ragged16(wl.scores, wl.row_starts, wl.lengths, wl.k, wl.max_len, fmt=wl.fmt,
+                                      threads=cpu_threads())
     if transform is not None:
         oi = oracle.index_transform(oi, transform["mode"], offsets=transform.get("index_offsets"),
                                     page_table=transform.get("page_table"), page_size=transform.get("page_size", 1))
@@ -378,6 +401,8 @@ def main():
                     help="fuse the index transform into the call (offsets: the rows' starts; page table: one "
                          "shared table of randomly placed pages)")
     ap.add_argument("--page-size", type=int, default=64)
+    ap.add_argument("--dtype", choices=["f32", "f16", "bf16"], default="f32",
+                    help="score format: the workload's float32 scores, or rounded to binary16 / bfloat16")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the long-context workload measured beside the headline one")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
@@ -398,9 +423,12 @@ def main():
     import workloads as W
     log("generating %s" % args.workload)
     wl = W.full(args.workload)
+    if args.dtype != "f32":
+        wl = W.to16(wl, args.dtype)
     m = measure(wl, args.steps, args.warmup, args.rotate, args.index_transform, args.page_size)
     ms_per_step = m["ms_per_step"]
-    score_gbps = 4.0 * wl.sum_n / (ms_per_step * 1e-3) / 1e9
+    score_bytes = 4 if args.dtype == "f32" else 2
+    score_gbps = score_bytes * wl.sum_n / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": wl.B / (ms_per_step * 1e-3),
@@ -412,7 +440,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32",
+        "dtype": "u32" if args.dtype == "f32" else "u16",
         "data": "synthetic",
         "config": {
             "workload": wl.name, "B": wl.B, "max_len": wl.max_len, "k": wl.k, "sum_n": wl.sum_n,
@@ -429,6 +457,8 @@ def main():
     if args.workload != SECONDARY and not args.no_secondary:
         log("generating %s (secondary)" % SECONDARY)
         wl2 = W.full(SECONDARY)
+        if args.dtype != "f32":
+            wl2 = W.to16(wl2, args.dtype)
         m2 = measure(wl2, max(args.steps, 200), args.warmup, 0, args.index_transform, args.page_size)
         result["secondary"] = {
             "workload": wl2.name, "B": wl2.B, "max_len": wl2.max_len, "k": wl2.k, "sum_n": wl2.sum_n,

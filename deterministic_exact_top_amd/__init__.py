@@ -28,6 +28,7 @@ DETK_SCRATCH_BYTES = 16 << 20  # the per-GPU scratch array behind topk_ragged_no
 DETK_OK, DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, DETK_ERR_WORKSPACE, DETK_ERR_HIP = range(5)
 DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE, DETK_DEBUG_FAST = 1, 2, 3, 4
 DETK_INDEX_LOCAL, DETK_INDEX_OFFSET, DETK_INDEX_PAGE_TABLE = 0, 1, 2
+DETK_DTYPE_F32, DETK_DTYPE_F16, DETK_DTYPE_BF16 = 0, 1, 2
 
 
 class IndexTransform(ctypes.Structure):
@@ -69,6 +70,9 @@ def load_library():
     lib.detk_topk_ragged_transform.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int,
                                                ctypes.POINTER(IndexTransform), vp, vp, vp, sz, vp]
     lib.detk_topk_ragged_transform.restype = ctypes.c_int
+    lib.detk_topk_ragged_16bit.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, i32, ctypes.c_int,
+                                           ctypes.POINTER(IndexTransform), vp, vp, vp, sz, vp]
+    lib.detk_topk_ragged_16bit.restype = ctypes.c_int
     lib.detk_topk_ragged_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, i32, ctypes.c_int, vp, vp, vp]
     lib.detk_topk_ragged_noalloc.restype = ctypes.c_int
     lib.detk_status_string.argtypes = [ctypes.c_int]
@@ -140,7 +144,8 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
                 stream=None, index_offsets=None, page_table=None, page_size: int = 1):
     """Exact canonical top-k of each ragged row.
 
-    scores      float32 CUDA tensor, contiguous.  2-D (B, L): rows are the matrix rows
+    scores      float32, float16 or bfloat16 CUDA tensor, contiguous (16-bit scores run
+                detk_topk_ragged_16bit; their out_val has the scores' dtype).  2-D (B, L): rows are the matrix rows
                 by default (row_starts None -> b * L, max_len defaults to L).  1-D:
                 a packed buffer; pass row_starts and max_len.
     row_starts  int32 CUDA tensor (B,) of absolute element offsets, or None.
@@ -160,8 +165,10 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
     """
     import torch
     lib = load_library()
-    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 CUDA tensor")
+    dtypes = {torch.float32: DETK_DTYPE_F32, torch.float16: DETK_DTYPE_F16, torch.bfloat16: DETK_DTYPE_BF16}
+    if scores.dtype not in dtypes or not scores.is_cuda or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32, float16 or bfloat16 CUDA tensor")
+    dtype = dtypes[scores.dtype]
     if max_len is None:
         if scores.dim() != 2:
             raise ValueError("max_len is required unless scores is 2-D")
@@ -185,7 +192,7 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
     if out_idx is None:
         out_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
     if with_values and out_val is None:
-        out_val = torch.empty((B, k), dtype=torch.float32, device=dev)
+        out_val = torch.empty((B, k), dtype=scores.dtype, device=dev)
     need = workspace_size(B, k, max_len, dev.index if dev.index is not None else torch.cuda.current_device())
     if need and (workspace is None or workspace.numel() < need):
         # (zero-filled: the library needs a workspace zeroed before its first use)
@@ -193,9 +200,13 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     args = (_ptr(out_idx), _ptr(out_val) if with_values else None, _ptr(workspace) if need else None,
             int(workspace.numel()) if need else 0, ctypes.c_void_p(s.cuda_stream))
-    if index_offsets is None and page_table is None:
+    if index_offsets is None and page_table is None and dtype == DETK_DTYPE_F32:
         st = lib.detk_topk_ragged(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len), int(k), *args)
         what = "detk_topk_ragged"
+    elif index_offsets is None and page_table is None:
+        st = lib.detk_topk_ragged_16bit(_ptr(scores), dtype, _ptr(row_starts), _ptr(lengths), int(B), int(max_len),
+                                        int(k), None, *args)
+        what = "detk_topk_ragged_16bit"
     else:
         if index_offsets is not None and page_table is not None:
             raise ValueError("pass index_offsets or page_table, not both")
@@ -208,9 +219,14 @@ def topk_ragged(scores, row_starts=None, lengths=None, k: int = 2048, max_len: i
         else:
             xf.mode, xf.page_size, xf.page_table = DETK_INDEX_PAGE_TABLE, int(page_size), page_table.data_ptr()
             xf.page_table_stride = int(page_table.shape[1]) if page_table.dim() == 2 else 0
-        st = lib.detk_topk_ragged_transform(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len),
-                                            int(k), ctypes.byref(xf), *args)
-        what = "detk_topk_ragged_transform"
+        if dtype == DETK_DTYPE_F32:
+            st = lib.detk_topk_ragged_transform(_ptr(scores), _ptr(row_starts), _ptr(lengths), int(B), int(max_len),
+                                                int(k), ctypes.byref(xf), *args)
+            what = "detk_topk_ragged_transform"
+        else:
+            st = lib.detk_topk_ragged_16bit(_ptr(scores), dtype, _ptr(row_starts), _ptr(lengths), int(B),
+                                            int(max_len), int(k), ctypes.byref(xf), *args)
+            what = "detk_topk_ragged_16bit"
     if st != DETK_OK:
         raise DetkError(st, what)
     return out_idx, (out_val if with_values else None)

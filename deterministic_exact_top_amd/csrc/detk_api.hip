@@ -10,7 +10,7 @@
 #include <string.h>
 
 #include "../../include/detk.h"
-#include "topk_device.hpp"
+#include "kernels.hpp"
 
 // Workspace of detk_topk_ragged_noalloc: one array per GPU the library runs on, held until
 // the process ends.  Zero when the code object loads; every call leaves the words that
@@ -23,37 +23,16 @@ namespace {
 
 using detk::Params;
 using detk::SmemAll;
+using detk::Shape;
+using detk::min_waves;
+using detk::kSingleMaxLen;
+using detk::kSplitTile;
 
-// Workgroup tile shapes (elements = threads x elements per lane).  Tiles keep the row in
-// VGPRs; MINW is the waves per SIMD their register allocation must allow.
-//   one workgroup per row (rows up to 32768): 4096 = 256 x 16, 8192 = 512 x 16,
-//     16384 = 512 x 32 (four rows per CU), 32768 = 1024 x 32
-//   rows split over workgroups: 4096 = 256 x 16, 8192 = 1024 x 8, 16384 = 1024 x 16
-//     (default), 32768 = 1024 x 32; 1024 threads wherever the tile allows, for the
-//     last arriving workgroup, which orders the whole row's candidates
-constexpr int kSingleMaxLen = 32768;
-constexpr int kSplitTile = 16384;
-
-template <int TILE, bool MULTI> struct Shape;
-template <> struct Shape<4096, false> { static constexpr int NT = 256, EPT = 16, MINW = 2; };
-template <> struct Shape<8192, false> { static constexpr int NT = 512, EPT = 16, MINW = 4; };
-template <> struct Shape<16384, false> { static constexpr int NT = 512, EPT = 32, MINW = 8; };
-template <> struct Shape<32768, false> { static constexpr int NT = 1024, EPT = 32, MINW = 4; };
-template <> struct Shape<4096, true> { static constexpr int NT = 256, EPT = 16, MINW = 2; };
-template <> struct Shape<8192, true> { static constexpr int NT = 1024, EPT = 8, MINW = 4; };
-template <> struct Shape<16384, true> { static constexpr int NT = 1024, EPT = 16, MINW = 4; };
-template <> struct Shape<32768, true> { static constexpr int NT = 1024, EPT = 32, MINW = 4; };
-
-// Waves per SIMD a kernel's registers must allow: the shape's, except where the LDS of the
-// k <= 4096 layouts already limits a CU to two 512-thread workgroups (4 waves per SIMD), so a
-// tighter register cap would only spill.
-template <int TILE, int KMAX, bool MULTI>
-constexpr int min_waves() { return (!MULTI && TILE == 16384 && KMAX == 4096) ? 4 : Shape<TILE, MULTI>::MINW; }
-
-template <int TILE, int KMAX, bool MULTI>
+template <int TILE, int KMAX, bool MULTI, int VB = 4>
 const void* kernel_ptr() {
     using S = Shape<TILE, MULTI>;
-    return reinterpret_cast<const void*>(&detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>()>);
+    return reinterpret_cast<const void*>(
+        &detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>(), VB>);
 }
 
 template <int TILE, int KMAX, bool MULTI>
@@ -77,19 +56,19 @@ int g_stage_cap = -1;       // -1 default
 int g_multi_tile = 0;       // 0 default
 int g_fast = 1;             // 0 off, 1 on, 2 on with a pivot that always misses
 
-template <int TILE, int KMAX, bool MULTI>
+template <int TILE, int KMAX, bool MULTI, int VB>
 hipError_t prepare_kernel() {
-    return hipFuncSetAttribute(kernel_ptr<TILE, KMAX, MULTI>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+    return hipFuncSetAttribute(kernel_ptr<TILE, KMAX, MULTI, VB>(), hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)smem_bytes<TILE, KMAX, MULTI>());
 }
 
-template <int TILE>
+template <int TILE, int VB>
 void prepare_all(hipError_t* e) {
     hipError_t r;
-    if ((r = prepare_kernel<TILE, 2048, false>()) != hipSuccess) *e = r;
-    if ((r = prepare_kernel<TILE, 4096, false>()) != hipSuccess) *e = r;
-    if ((r = prepare_kernel<TILE, 2048, true>()) != hipSuccess) *e = r;
-    if ((r = prepare_kernel<TILE, 4096, true>()) != hipSuccess) *e = r;
+    if ((r = prepare_kernel<TILE, 2048, false, VB>()) != hipSuccess) *e = r;
+    if ((r = prepare_kernel<TILE, 4096, false, VB>()) != hipSuccess) *e = r;
+    if ((r = prepare_kernel<TILE, 2048, true, VB>()) != hipSuccess) *e = r;
+    if ((r = prepare_kernel<TILE, 4096, true, VB>()) != hipSuccess) *e = r;
 }
 
 template <int TILE, int KMAX>
@@ -115,10 +94,14 @@ int device_info(int device, DeviceInfo* out) {
             d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
             d.cus = prop.multiProcessorCount;
             d.max_lds = prop.sharedMemPerBlock;
-            prepare_all<4096>(&e);
-            prepare_all<8192>(&e);
-            prepare_all<16384>(&e);
-            prepare_all<32768>(&e);
+            prepare_all<4096, 4>(&e);
+            prepare_all<8192, 4>(&e);
+            prepare_all<16384, 4>(&e);
+            prepare_all<32768, 4>(&e);
+            prepare_all<4096, 2>(&e);
+            prepare_all<8192, 2>(&e);
+            prepare_all<16384, 2>(&e);
+            prepare_all<32768, 2>(&e);
             d.split_occ[0] = split_occupancy<kSplitTile, 2048>();
             d.split_occ[1] = split_occupancy<kSplitTile, 4096>();
             // (with this device current: each GPU holds its own copy at its own address)
@@ -229,45 +212,51 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
     return DETK_OK;
 }
 
-template <int TILE, int KMAX, bool MULTI>
+template <int TILE, int KMAX, bool MULTI, int VB>
 hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
     using S = Shape<TILE, MULTI>;
-    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>()>), dim3(grid),
-                       dim3(S::NT), lds, stream, p);
+    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>(), VB>),
+                       dim3(grid), dim3(S::NT), lds, stream, p);
     return hipGetLastError();
 }
 
-hipError_t dispatch(const Plan& pl, const Params& p, hipStream_t stream) {
+template <int VB>
+hipError_t dispatch_vb(const Plan& pl, const Params& p, hipStream_t stream) {
     const bool k2 = pl.kmax == 2048;
     if (!pl.multi) {
         switch (pl.tile) {
-        case 4096: return k2 ? launch<4096, 2048, false>(p, pl.grid, pl.lds, stream)
-                             : launch<4096, 4096, false>(p, pl.grid, pl.lds, stream);
-        case 8192: return k2 ? launch<8192, 2048, false>(p, pl.grid, pl.lds, stream)
-                             : launch<8192, 4096, false>(p, pl.grid, pl.lds, stream);
-        case 16384: return k2 ? launch<16384, 2048, false>(p, pl.grid, pl.lds, stream)
-                              : launch<16384, 4096, false>(p, pl.grid, pl.lds, stream);
-        default: return k2 ? launch<32768, 2048, false>(p, pl.grid, pl.lds, stream)
-                           : launch<32768, 4096, false>(p, pl.grid, pl.lds, stream);
+        case 4096: return k2 ? launch<4096, 2048, false, VB>(p, pl.grid, pl.lds, stream)
+                             : launch<4096, 4096, false, VB>(p, pl.grid, pl.lds, stream);
+        case 8192: return k2 ? launch<8192, 2048, false, VB>(p, pl.grid, pl.lds, stream)
+                             : launch<8192, 4096, false, VB>(p, pl.grid, pl.lds, stream);
+        case 16384: return k2 ? launch<16384, 2048, false, VB>(p, pl.grid, pl.lds, stream)
+                              : launch<16384, 4096, false, VB>(p, pl.grid, pl.lds, stream);
+        default: return k2 ? launch<32768, 2048, false, VB>(p, pl.grid, pl.lds, stream)
+                           : launch<32768, 4096, false, VB>(p, pl.grid, pl.lds, stream);
         }
     }
     switch (pl.tile) {
-    case 4096: return k2 ? launch<4096, 2048, true>(p, pl.grid, pl.lds, stream)
-                         : launch<4096, 4096, true>(p, pl.grid, pl.lds, stream);
-    case 8192: return k2 ? launch<8192, 2048, true>(p, pl.grid, pl.lds, stream)
-                         : launch<8192, 4096, true>(p, pl.grid, pl.lds, stream);
-    case 16384: return k2 ? launch<16384, 2048, true>(p, pl.grid, pl.lds, stream)
-                          : launch<16384, 4096, true>(p, pl.grid, pl.lds, stream);
-    default: return k2 ? launch<32768, 2048, true>(p, pl.grid, pl.lds, stream)
-                       : launch<32768, 4096, true>(p, pl.grid, pl.lds, stream);
+    case 4096: return k2 ? launch<4096, 2048, true, VB>(p, pl.grid, pl.lds, stream)
+                         : launch<4096, 4096, true, VB>(p, pl.grid, pl.lds, stream);
+    case 8192: return k2 ? launch<8192, 2048, true, VB>(p, pl.grid, pl.lds, stream)
+                         : launch<8192, 4096, true, VB>(p, pl.grid, pl.lds, stream);
+    case 16384: return k2 ? launch<16384, 2048, true, VB>(p, pl.grid, pl.lds, stream)
+                          : launch<16384, 4096, true, VB>(p, pl.grid, pl.lds, stream);
+    default: return k2 ? launch<32768, 2048, true, VB>(p, pl.grid, pl.lds, stream)
+                       : launch<32768, 4096, true, VB>(p, pl.grid, pl.lds, stream);
     }
+}
+
+hipError_t dispatch(const Plan& pl, const Params& p, int vb, hipStream_t stream) {
+    return vb == 2 ? dispatch_vb<2>(pl, p, stream) : dispatch_vb<4>(pl, p, stream);
 }
 
 // The operation, on the caller's workspace or (use_scratch) on the device's scratch array.
 // Allocates nothing in either case.
-int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B, int32_t max_len, int k,
-        const detk_index_transform* xf, int32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes,
-        bool use_scratch, void* stream_ptr) {
+// dtype: DETK_DTYPE_F32, DETK_DTYPE_F16 or DETK_DTYPE_BF16 (checked by the caller).
+int run(const void* scores, int dtype, const int32_t* row_starts, const int32_t* lengths, int B, int32_t max_len,
+        int k, const detk_index_transform* xf, int32_t* out_idx, void* out_val, void* workspace,
+        size_t workspace_bytes, bool use_scratch, void* stream_ptr) {
     if (B < 0 || k < 1 || max_len < 0) return DETK_ERR_INVALID_ARG;
     if (B > 0 && (!scores || !out_idx)) return DETK_ERR_INVALID_ARG;
     if (k > DETK_MAX_K || max_len > DETK_MAX_LEN) return DETK_ERR_UNSUPPORTED;
@@ -309,7 +298,7 @@ int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, 
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
     Params p;
-    p.scores = reinterpret_cast<const uint32_t*>(scores);
+    p.scores = scores;
     p.row_starts = row_starts;
     p.lengths = lengths;
     p.B = B;
@@ -319,7 +308,8 @@ int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, 
     p.stage_cap = g_stage_cap < 0 ? detk::kStageCap : (g_stage_cap > detk::kStageCap ? detk::kStageCap : g_stage_cap);
     p.fast = g_fast;
     p.out_idx = out_idx;
-    p.out_val = reinterpret_cast<uint32_t*>(out_val);
+    p.out_val = out_val;
+    p.val_pad = dtype == DETK_DTYPE_F16 ? 0xFC00u : dtype == DETK_DTYPE_BF16 ? 0xFF80u : detk::kNegInfBits;
     p.xf_mode = xf ? xf->mode : DETK_INDEX_LOCAL;
     p.xf_page = xf && xf->mode == DETK_INDEX_PAGE_TABLE ? xf->page_size : 1;
     p.xf_shift = xf_shift;
@@ -337,7 +327,7 @@ int run(const float* scores, const int32_t* row_starts, const int32_t* lengths, 
         p.ws_cand = reinterpret_cast<uint2*>(ws + data_off + pl.off_cand);
         p.ws_tie = reinterpret_cast<uint32_t*>(ws + data_off + pl.off_tie);
     }
-    if (dispatch(pl, p, stream) != hipSuccess) return DETK_ERR_HIP;
+    if (dispatch(pl, p, dtype == DETK_DTYPE_F32 ? 4 : 2, stream) != hipSuccess) return DETK_ERR_HIP;
     return DETK_OK;
 }
 
@@ -386,20 +376,29 @@ size_t detk_workspace_size(int device, int B, int k, int32_t max_len) {
 int detk_topk_ragged(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                      int32_t max_len, int k, int32_t* out_idx, float* out_val, void* workspace,
                      size_t workspace_bytes, void* stream_ptr) {
-    return run(scores, row_starts, lengths, B, max_len, k, nullptr, out_idx, out_val, workspace, workspace_bytes,
-               false, stream_ptr);
+    return run(scores, DETK_DTYPE_F32, row_starts, lengths, B, max_len, k, nullptr, out_idx, out_val, workspace,
+               workspace_bytes, false, stream_ptr);
+}
+
+int detk_topk_ragged_16bit(const void* scores, int dtype, const int32_t* row_starts, const int32_t* lengths, int B,
+                           int32_t max_len, int k, const detk_index_transform* transform, int32_t* out_idx,
+                           void* out_val, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+    if (dtype != DETK_DTYPE_F16 && dtype != DETK_DTYPE_BF16) return DETK_ERR_INVALID_ARG;
+    return run(scores, dtype, row_starts, lengths, B, max_len, k, transform, out_idx, out_val, workspace,
+               workspace_bytes, false, stream_ptr);
 }
 
 int detk_topk_ragged_transform(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                                int32_t max_len, int k, const detk_index_transform* transform, int32_t* out_idx,
                                float* out_val, void* workspace, size_t workspace_bytes, void* stream_ptr) {
-    return run(scores, row_starts, lengths, B, max_len, k, transform, out_idx, out_val, workspace, workspace_bytes,
-               false, stream_ptr);
+    return run(scores, DETK_DTYPE_F32, row_starts, lengths, B, max_len, k, transform, out_idx, out_val, workspace,
+               workspace_bytes, false, stream_ptr);
 }
 
 int detk_topk_ragged_noalloc(const float* scores, const int32_t* row_starts, const int32_t* lengths, int B,
                              int32_t max_len, int k, int32_t* out_idx, float* out_val, void* stream_ptr) {
-    return run(scores, row_starts, lengths, B, max_len, k, nullptr, out_idx, out_val, nullptr, 0, true, stream_ptr);
+    return run(scores, DETK_DTYPE_F32, row_starts, lengths, B, max_len, k, nullptr, out_idx, out_val, nullptr, 0,
+               true, stream_ptr);
 }
 
 const char* detk_status_string(int status) {

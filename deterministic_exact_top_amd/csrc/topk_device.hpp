@@ -68,7 +68,7 @@ constexpr int kSplitSamples = 8192;             // split rows: samples per row (
 constexpr int kBufferWord3 = 0x00020000;        // raw buffer resource, gfx9-family data format
 
 struct Params {
-    const uint32_t* scores;
+    const void* scores;         // float32 bits (VB 4) or 16-bit float bits (VB 2)
     const int32_t* row_starts;  // nullable
     const int32_t* lengths;     // nullable
     int32_t B;
@@ -78,7 +78,8 @@ struct Params {
     int32_t stage_cap;          // <= kStageCap
     int32_t fast;               // 1: try the pivot fast path first
     int32_t* out_idx;
-    uint32_t* out_val;          // nullable
+    void* out_val;              // nullable: VB-byte values
+    uint32_t val_pad;           // the value written in padded slots (-inf of the format)
     uint32_t* ws_ctl;           // B * kRowCtlWords, zero on entry and on exit
     uint32_t* ws_ecnt;          // B * tiles_per_row: keys equal to P per tile
     uint2* ws_cand;             // B * cand_cap(KMAX): candidates (bits, position in the row)
@@ -214,24 +215,28 @@ __device__ __forceinline__ uint32_t claim_slot(bool pred, uint32_t* counter) {
 
 // Load one tile's raw bits: slot (v, c) of lane t holds window position
 // (v * NT + t) * 4 + c.  The buffer resource covers exactly the tile's valid bytes, so
-// slots past the window read 0 (callers mask them by position).  A 16-byte aligned tile
-// uses 16-byte loads (a partially valid one never leaves the 16-byte chunk holding valid
-// data); otherwise 4-byte loads.  PART 0 loads the groups holding the pivot samples,
-// PART 1 the others, PART 2 all of them (sample groups issued first).
+// slots past the window read 0 (callers mask them by position).  VB = 4: float32 bits,
+// with 16-byte loads for a 16-byte aligned tile (a partially valid one never leaves the
+// 16-byte chunk holding valid data), else 4-byte loads.  VB = 2: 16-bit float bits, each
+// widened to (bits << 16) -- that 32-bit pattern keeps the 16-bit value's place in the
+// total order and its ties (the key map's low half is fixed by the sign) -- with 8-byte
+// loads for an 8-byte aligned tile, else 2-byte loads.  PART 0 loads the groups holding
+// the pivot samples, PART 1 the others, PART 2 all of them (sample groups issued first).
 template <int NT, int EPT>
 constexpr bool sample_group(int v) {
     return v % (EPT / 4 >= kSamplesPerLane ? EPT / 4 / kSamplesPerLane : 1) == 0;
 }
 
-template <int NT, int EPT, int PART>
-__device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const uint32_t* src, int nt) {
+template <int NT, int EPT, int PART, int VB>
+__device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const void* src, int nt) {
+    static_assert(VB == 4 || VB == 2, "float32 or 16-bit scores");
     const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src), (short)0, nt * 4, kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, nt * VB, kBufferWord3);
     const int tid = opaque_tid();
     constexpr int G4 = EPT / 4;
     // (one branch around all the loads: with a branch per load the compiler's wait counts
     // turn conservative, and the samples would wait for the whole tile)
-    if ((((uintptr_t)src) & 15u) == 0) {
+    if ((((uintptr_t)src) & (4u * VB - 1u)) == 0) {
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             if ((PART == 0 && pass == 1) || (PART == 1 && pass == 0)) continue;
@@ -239,11 +244,35 @@ __device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const uint32_
             for (int v = 0; v < G4; ++v) {
                 if (sample_group<NT, EPT>(v) != (pass == 0)) continue;
                 // (the per-group offset rides in the scalar offset: one address VGPR for all)
-                const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, tid * 16, v * NT * 16, 0);
-                u[4 * v + 0] = q[0];
-                u[4 * v + 1] = q[1];
-                u[4 * v + 2] = q[2];
-                u[4 * v + 3] = q[3];
+                if constexpr (VB == 4) {
+                    const auto q = __builtin_amdgcn_raw_buffer_load_b128(rsrc, tid * 16, v * NT * 16, 0);
+                    u[4 * v + 0] = q[0];
+                    u[4 * v + 1] = q[1];
+                    u[4 * v + 2] = q[2];
+                    u[4 * v + 3] = q[3];
+                } else {
+                    const auto q = __builtin_amdgcn_raw_buffer_load_b64(rsrc, tid * 8, v * NT * 8, 0);
+                    u[4 * v + 0] = q[0] << 16;
+                    u[4 * v + 1] = q[0] & 0xFFFF0000u;
+                    u[4 * v + 2] = q[1] << 16;
+                    u[4 * v + 3] = q[1] & 0xFFFF0000u;
+                }
+            }
+        }
+        if constexpr (VB == 2) {
+            // With an odd element count the last element shares its 4-byte word with the two
+            // bytes past the window; the range check zeroes such a word whole, so the lane
+            // holding that element reloads it alone (never reading past the window).
+            static_assert(VB == 4 || PART == 2, "16-bit tiles load whole");
+            if (nt & 1) {  // uniform
+                const int pl = nt - 1;
+                const int slot = (pl / (NT * 4)) * 4 + (pl & 3);  // uniform register slot
+                if (tid == (pl >> 2) % NT) {
+                    const uint32_t x = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, pl * 2, 0, 0) << 16;
+#pragma unroll
+                    for (int i = 0; i < EPT; ++i)
+                        if (i == slot) u[i] = x;
+                }
             }
         }
     } else {
@@ -254,16 +283,21 @@ __device__ __forceinline__ void load_tile_part(uint32_t (&u)[EPT], const uint32_
             for (int v = 0; v < G4; ++v) {
                 if (sample_group<NT, EPT>(v) != (pass == 0)) continue;
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 16 + c * 4, v * NT * 16, 0);
+                for (int c = 0; c < 4; ++c) {
+                    if constexpr (VB == 4)
+                        u[4 * v + c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 16 + c * 4, v * NT * 16, 0);
+                    else
+                        u[4 * v + c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, tid * 8 + c * 2, v * NT * 8, 0)
+                                       << 16;
+                }
             }
         }
     }
 }
 
-template <int NT, int EPT>
-__device__ __forceinline__ void load_tile(uint32_t (&u)[EPT], const uint32_t* src, int nt) {
-    load_tile_part<NT, EPT, 2>(u, src, nt);
+template <int NT, int EPT, int VB>
+__device__ __forceinline__ void load_tile(uint32_t (&u)[EPT], const void* src, int nt) {
+    load_tile_part<NT, EPT, 2, VB>(u, src, nt);
 }
 
 // ----------------------------------------------------------------------------- shared memory
@@ -556,12 +590,30 @@ __device__ __forceinline__ void store_at(T* base, uint32_t i, T v) {
     *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T)) = v;
 }
 
+// A row's output values: put(slot, bits) writes a selected score from its 32-bit register
+// pattern (16-bit scores sit in the top half of theirs), pad(slot) the padding value.
+// Uniform across the launch.
+struct ValOut {
+    void* base;     // nullptr: the caller wants no values
+    uint32_t padv;  // the padding pattern (the format's -inf)
+    bool half;      // 16-bit values
+    __device__ __forceinline__ explicit operator bool() const { return base != nullptr; }
+    __device__ __forceinline__ void put(uint32_t slot, uint32_t bits32) const {
+        if (half) store_at(static_cast<uint16_t*>(base), slot, (uint16_t)(bits32 >> 16));
+        else store_at(static_cast<uint32_t*>(base), slot, bits32);
+    }
+    __device__ __forceinline__ void pad(uint32_t slot) const {
+        if (half) store_at(static_cast<uint16_t*>(base), slot, (uint16_t)padv);
+        else store_at(static_cast<uint32_t*>(base), slot, padv);
+    }
+};
+
 // Write the padding slots [m, k) of one output row.
 template <int NT>
-__device__ __forceinline__ void write_padding(int32_t* oidx, uint32_t* oval, int m, int k) {
+__device__ __forceinline__ void write_padding(int32_t* oidx, const ValOut& ov, int m, int k) {
     for (int q = m + opaque_tid(); q < k; q += NT) {
         store_at(oidx, (uint32_t)q, -1);
-        if (oval) store_at(oval, (uint32_t)q, kNegInfBits);
+        if (ov) ov.pad((uint32_t)q);
     }
 }
 
@@ -616,7 +668,7 @@ struct RowCtx {
     int32_t n, m, k, nt, j0;
     int64_t base;
     int32_t* oidx;
-    uint32_t* oval;
+    ValOut ov;
     IndexOut xo;
 };
 
@@ -1237,7 +1289,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
             r.xo,
             [&](uint32_t slot, int32_t idx, uint32_t bits) {
                 store_at(r.oidx, slot, idx);
-                if (r.oval) store_at(r.oval, slot, bits);
+                if (r.ov) r.ov.put(slot, bits);
             },
             scattered, m == nt))
         return false;
@@ -1264,52 +1316,62 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
                     const int bit = __ffs(word) - 1;
                     word &= word - 1;
                     r.oidx[c_gt + rr] = r.xo((uint32_t)(w * 32 + bit));
-                    if (r.oval) r.oval[c_gt + rr] = vP;
+                    if (r.ov) r.ov.put(c_gt + rr, vP);
                     ++rr;
                 }
                 rr += (uint32_t)__popc(word);
             }
         }
     }
-    write_padding<NT>(r.oidx, r.oval, m, r.k);
+    write_padding<NT>(r.oidx, r.ov, m, r.k);
     return true;
 }
 
-// Samples of a split row, the same in every tile of the row: 16-byte groups of 4
-// elements, evenly spread over the window.  The groups start at the window's first
-// 16-byte boundary (a0 = 0..3 elements in), so every load is an aligned 16-byte buffer
-// load and there is no alignment branch: the compiler counts the loads exactly, and the
+// Samples of a split row, the same in every tile of the row: groups of 4 elements
+// (16 bytes of float32, 8 of 16-bit floats, widened as the tile loads widen them), evenly
+// spread over the window.  The groups start at the window's first group-size boundary
+// (a0 = 0..3 elements in), so every load is an aligned buffer load and there is no
+// alignment branch: the compiler counts the loads exactly, and the
 // pivot waits for them alone, not for the tile loads issued after them.  Lane t's g-th
 // group is group floor(q * G / (SL * NT)), q = g * NT + t, of the G = (n - a0) / 4 whole
 // groups (a row shorter than 4 * SL * NT elements repeats some, which only weakens the
 // pivot estimate).
-template <int NT, int SL>
-__device__ __forceinline__ void load_row_samples(uint32_t (&sk)[4 * SL], const uint32_t* row, int32_t n) {
-    const uint32_t a0 = ((16u - (uint32_t)((uintptr_t)row & 15u)) & 15u) >> 2;  // (rows start 4-byte aligned)
-    const uint32_t* base = row + a0;
+template <int NT, int SL, int VB>
+__device__ __forceinline__ void load_row_samples(uint32_t (&sk)[4 * SL], const char* row, int32_t n) {
+    // a0: elements before the first (4 * VB)-byte boundary (rows start VB-byte aligned)
+    const uint32_t a0 = ((4u * VB - (uint32_t)((uintptr_t)row & (4u * VB - 1u))) & (4u * VB - 1u)) / VB;
+    const char* base = row + (size_t)a0 * VB;
     const uint64_t groups = (uint64_t)((uint32_t)(n - (int32_t)a0) >> 2);
-    // (2^30 elements make 2^32 bytes: the range is clamped to 32 bits, and a sample group
-    // past it reads zeros, which only nudges the pivot estimate)
-    const uint64_t bytes = groups * 16u;
+    // (2^30 float32 elements make 2^32 bytes: the range is clamped to 32 bits, and a sample
+    // group past it reads zeros, which only nudges the pivot estimate)
+    const uint64_t bytes = groups * 4u * VB;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint32_t*>(base), (short)0, (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull),
+        const_cast<char*>(base), (short)0, (int)(uint32_t)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull),
         kBufferWord3);
     const uint32_t tid = (uint32_t)opaque_tid();
 #pragma unroll
     for (int g = 0; g < SL; ++g) {
         const uint32_t q = (uint32_t)g * NT + tid;
         const uint32_t grp = (uint32_t)(((uint64_t)q * groups) / (uint64_t)(SL * NT));
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, grp * 16u, 0, 0);
-        sk[4 * g + 0] = v[0];
-        sk[4 * g + 1] = v[1];
-        sk[4 * g + 2] = v[2];
-        sk[4 * g + 3] = v[3];
+        if constexpr (VB == 4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, grp * 16u, 0, 0);
+            sk[4 * g + 0] = v[0];
+            sk[4 * g + 1] = v[1];
+            sk[4 * g + 2] = v[2];
+            sk[4 * g + 3] = v[3];
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, grp * 8u, 0, 0);
+            sk[4 * g + 0] = v[0] << 16;
+            sk[4 * g + 1] = v[0] & 0xFFFF0000u;
+            sk[4 * g + 2] = v[1] << 16;
+            sk[4 * g + 3] = v[1] & 0xFFFF0000u;
+        }
     }
 }
 
-template <int NT, int KMAX, int STAGE>
-__device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, uint32_t* oval,
-                          IndexOut xo, RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap);
+template <int NT, int KMAX, int STAGE, int VB>
+__device__ void exact_row(const char* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, ValOut ov, IndexOut xo,
+                          RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap);
 
 // One tile of a row split over several workgroups.  No workgroup ever waits for another:
 //   - every tile reads the same evenly spaced samples of the whole row and derives the
@@ -1322,7 +1384,7 @@ __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, 
 //     sets the row's counters back to zero, then orders the candidates when the list held
 //     them all and at least min(k, n) keys are >= P (keys equal to P fill the tail in
 //     index order, tile by tile), and otherwise selects the row exactly on its own.
-template <int NT, int EPT, int KMAX>
+template <int NT, int EPT, int KMAX, int VB>
 __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, SmemAll<NT, EPT, KMAX, true>& sa) {
     using SS = SplitSmem<NT, EPT, KMAX>;
     SS& s = sa.split;
@@ -1335,16 +1397,16 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     const int lane = tid & 63;
     const int b = r.b, tile = r.tile, ntiles = r.ntiles;
     const int32_t nt = r.nt, m = r.m, n = r.n, j0 = r.j0;
-    const uint32_t* const row = p.scores + r.base;
+    const char* const row = static_cast<const char*>(p.scores) + r.base * VB;
     uint32_t* const rw = p.ws_ctl + (int64_t)b * kRowCtlWords;
     uint32_t* const ecnt = p.ws_ecnt + (int64_t)b * p.tiles_per_row;
     uint32_t P = 0;
 
     if (p.fast) {
         uint32_t sk[4 * SL];
-        load_row_samples<NT, SL>(sk, row, n);  // (issued first: the pivot needs them first)
+        load_row_samples<NT, SL, VB>(sk, row, n);  // (issued first: the pivot needs them first)
         uint32_t u[EPT];
-        load_tile<NT, EPT>(u, row + j0, nt);
+        load_tile<NT, EPT, VB>(u, row + (size_t)j0 * VB, nt);
 
         // ------------------------------------------------ pivot from the row's samples
         block_zero<NT, 4 * kRadix>(s.bucket);  // the sample-digit histograms
@@ -1465,7 +1527,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     const uint32_t n_eq = s.ctl[kCtlEq];
     if (!p.fast || c_gt > CAP || c_gt + n_eq < (uint32_t)m) {  // uniform
         __syncthreads();  // (the fallback's LDS overlays the words just read)
-        exact_row<NT, KMAX, kRowStageEntries>(row, n, m, r.k, r.oidx, r.oval, r.xo, sa.rexact, p.stage_cap);
+        exact_row<NT, KMAX, kRowStageEntries, VB>(row, n, m, r.k, r.oidx, r.ov, r.xo, sa.rexact, p.stage_cap);
         return;
     }
     const bool ties = c_gt < (uint32_t)m;
@@ -1481,7 +1543,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
         c_gt, (uint32_t)m, ties, BucketMapT<true>(L, U), r.xo,
         [&](uint32_t slot, int32_t idx, uint32_t bits) {
             r.oidx[slot] = idx;
-            if (r.oval) r.oval[slot] = bits;
+            if (r.ov) r.ov.put(slot, bits);
         },
         [] {});
 
@@ -1514,7 +1576,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
                     const int bit = __ffs(word) - 1;
                     word &= word - 1;
                     r.oidx[c_gt + rr2] = r.xo((uint32_t)(wpos + bit));
-                    if (r.oval) r.oval[c_gt + rr2] = vP;
+                    if (r.ov) r.ov.put(c_gt + rr2, vP);
                     ++rr2;
                 }
             }
@@ -1522,7 +1584,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
             __syncthreads();  // (wsum is scanned again next turn)
         }
     }
-    write_padding<NT>(r.oidx, r.oval, m, r.k);
+    write_padding<NT>(r.oidx, r.ov, m, r.k);
 }
 
 // Exact selection of one whole row by one workgroup, reading the row from global memory
@@ -1531,9 +1593,9 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
 // staged in LDS when they fit, otherwise every later pass reads the row again, so no
 // candidate is ever dropped -- then the elements above T sorted as composites, then the
 // boundary ties at T taken in index order by an ordered scan of the row.
-template <int NT, int KMAX, int STAGE>
-__device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, uint32_t* oval,
-                          IndexOut xo, RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap) {
+template <int NT, int KMAX, int STAGE, int VB>
+__device__ void exact_row(const char* row, int32_t n, int32_t m, int32_t k, int32_t* oidx, ValOut ov, IndexOut xo,
+                          RowExactSmem<NT, KMAX, STAGE>& s, int stage_cap) {
     constexpr int EC = 16;
     constexpr int CH = NT * EC;
     constexpr int NW = NT / 64;
@@ -1554,15 +1616,15 @@ __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, 
                 }
         };
         uint32_t ua[EC], ub[EC];
-        load_tile<NT, EC>(ua, row, min(CH, n));
+        load_tile<NT, EC, VB>(ua, row, min(CH, n));
 #pragma unroll 1
         for (int32_t c0 = 0; c0 < n; c0 += 2 * CH) {
             const int32_t c1 = c0 + CH;
-            if (c1 < n) load_tile<NT, EC>(ub, row + c1, min(CH, n - c1));
+            if (c1 < n) load_tile<NT, EC, VB>(ub, row + (size_t)c1 * VB, min(CH, n - c1));
             visit(ua, c0, min(CH, n - c0));
             if (c1 >= n) break;
             const int32_t c2 = c1 + CH;
-            if (c2 < n) load_tile<NT, EC>(ua, row + c2, min(CH, n - c2));
+            if (c2 < n) load_tile<NT, EC, VB>(ua, row + (size_t)c2 * VB, min(CH, n - c2));
             visit(ub, c1, min(CH, n - c1));
         }
     };
@@ -1663,7 +1725,7 @@ __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, 
     bitonic_desc<NT>(A, (int)nA);
     for (uint32_t q = tid; q < nA; q += NT) {
         oidx[q] = xo(s.apos[q]);
-        if (oval) oval[q] = bits_of(s.akey[q]);
+        if (ov) ov.put(q, bits_of(s.akey[q]));
     }
 
     // ---------------------------------------------------------------- boundary ties, in index order
@@ -1674,7 +1736,7 @@ __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, 
         for (int32_t c0 = 0; c0 < n && got < need; c0 += CT) {
             const int32_t nt = min(CT, n - c0);
             uint32_t u4[4];
-            load_tile<NT, 4>(u4, row + c0, nt);
+            load_tile<NT, 4, VB>(u4, row + (size_t)c0 * VB, nt);
             const int t4 = opaque_tid() * 4;
             uint32_t mk = 0;
 #pragma unroll
@@ -1685,14 +1747,14 @@ __device__ void exact_row(const uint32_t* row, int32_t n, int32_t m, int32_t k, 
                 const int c = __ffs(mk) - 1;
                 mk &= mk - 1;
                 oidx[cnt_gt + rr] = xo((uint32_t)(c0 + t4 + c));
-                if (oval) oval[cnt_gt + rr] = vT;
+                if (ov) ov.put(cnt_gt + rr, vT);
                 ++rr;
             }
             got += tot;
             __syncthreads();  // (wsum is scanned again next turn)
         }
     }
-    write_padding<NT>(oidx, oval, m, k);
+    write_padding<NT>(oidx, ov, m, k);
 }
 
 // ----------------------------------------------------------------------------- exact path
@@ -1708,7 +1770,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     const int wave = tid >> 6;
     const int32_t m = r.m, k = r.k, nt = r.nt, j0 = r.j0;
     int32_t* oidx = r.oidx;
-    uint32_t* oval = r.oval;
+    const ValOut& ov = r.ov;
 
     const PairList A{s.akey, s.apos};
 
@@ -1882,7 +1944,7 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
             word &= word - 1;
             const int32_t j = j0 + w * 32 + bit;
             oidx[cnt_gt + rr] = r.xo((uint32_t)j);
-            if (oval) oval[cnt_gt + rr] = vT;
+            if (ov) ov.put(cnt_gt + rr, vT);
             ++rr;
         }
     }
@@ -1893,16 +1955,16 @@ __device__ __forceinline__ void exact_tile(const Params& p, const RowCtx& r, ES&
     bitonic_desc<NT>(A, (int)nA);
     for (uint32_t q = tid; q < nA; q += NT) {
         oidx[q] = r.xo(s.apos[q]);
-        if (oval) oval[q] = bits_of(s.akey[q]);
+        if (ov) ov.put(q, bits_of(s.akey[q]));
     }
-    write_padding<NT>(oidx, oval, m, k);
+    write_padding<NT>(oidx, ov, m, k);
 }
 
 // ----------------------------------------------------------------------------- rows
 
 // Row setup: window (clamped length, start), output rows, and the tile of it this
 // workgroup item covers (nt <= 0 when the row has no such tile).
-template <int TILE, bool MULTI>
+template <int TILE, bool MULTI, int VB>
 __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     RowCtx r;
     const int32_t len = p.lengths ? p.lengths[b] : p.max_len;
@@ -1914,7 +1976,9 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     r.m = min(r.k, r.n);
     r.ntiles = MULTI ? max(1, (r.n + TILE - 1) / TILE) : 1;
     r.oidx = p.out_idx + (int64_t)b * r.k;
-    r.oval = p.out_val ? p.out_val + (int64_t)b * r.k : nullptr;
+    r.ov.half = VB == 2;
+    r.ov.padv = p.val_pad;
+    r.ov.base = p.out_val ? static_cast<char*>(p.out_val) + (int64_t)b * r.k * VB : nullptr;
     r.j0 = tile * TILE;
     r.nt = min(TILE, r.n - r.j0);
     r.xo.mode = p.xf_mode;
@@ -1927,20 +1991,21 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
 
 // A row that fits one tile, held whole by this workgroup: the pivot path, and the exact
 // path when it misses.
-template <int NT, int EPT, int KMAX, bool MULTI>
+template <int NT, int EPT, int KMAX, bool MULTI, int VB>
 __device__ __forceinline__ void whole_tile_row(const Params& p, SmemAll<NT, EPT, KMAX, MULTI>& s, const RowCtx& r) {
     if (r.m == 0) {  // empty window: every slot is padding
-        write_padding<NT>(r.oidx, r.oval, 0, r.k);
+        write_padding<NT>(r.oidx, r.ov, 0, r.k);
         return;
     }
+    const char* const row = static_cast<const char*>(p.scores) + r.base * VB;
     uint32_t u[EPT];
-    load_tile<NT, EPT>(u, p.scores + r.base, r.nt);
+    load_tile<NT, EPT, VB>(u, row, r.nt);
     if (p.fast && fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast, [] {})) return;
     if (p.fast) {
         __syncthreads();  // fall back to the exact path
         // (reloaded: kept in registers through the pivot path, the tile would crowd out its
         // later phases)
-        load_tile<NT, EPT>(u, p.scores + r.base, r.nt);
+        load_tile<NT, EPT, VB>(u, row, r.nt);
     }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) u[i] = key_of(u[i]);
@@ -1953,20 +2018,22 @@ __device__ __forceinline__ void whole_tile_row(const Params& p, SmemAll<NT, EPT,
 // hoisted into registers that would stay live across rows), or one workgroup per
 // (row, tile) item (MULTI true; a grid-stride loop over the items, in any order: no item
 // waits for another).
-template <int NT, int EPT, int KMAX, bool MULTI, int MINW>
+// VB: bytes per score (4: float32, 2: binary16 or bfloat16, widened in registers).
+template <int NT, int EPT, int KMAX, bool MULTI, int MINW, int VB>
 __global__ __launch_bounds__(NT, MINW) void topk_ragged_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto& s = *reinterpret_cast<SmemAll<NT, EPT, KMAX, MULTI>*>(smem_raw);
     if constexpr (!MULTI) {
-        whole_tile_row<NT, EPT, KMAX, false>(p, s, row_setup<NT * EPT, false>(p, (int)blockIdx.x, 0));
+        whole_tile_row<NT, EPT, KMAX, false, VB>(p, s, row_setup<NT * EPT, false, VB>(p, (int)blockIdx.x, 0));
     } else {
         const int64_t items = (int64_t)p.B * p.tiles_per_row;
         for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-            const RowCtx r = row_setup<NT * EPT, true>(p, (int)(it / p.tiles_per_row), (int)(it % p.tiles_per_row));
+            const RowCtx r =
+                row_setup<NT * EPT, true, VB>(p, (int)(it / p.tiles_per_row), (int)(it % p.tiles_per_row));
             if (r.tile >= r.ntiles) continue;  // (uniform) the row is shorter than this tile
             __syncthreads();                   // the previous item is done with LDS
-            if (r.ntiles == 1) whole_tile_row<NT, EPT, KMAX, true>(p, s, r);
-            else split_tile<NT, EPT, KMAX>(p, r, s);
+            if (r.ntiles == 1) whole_tile_row<NT, EPT, KMAX, true, VB>(p, s, r);
+            else split_tile<NT, EPT, KMAX, VB>(p, r, s);
         }
     }
 }

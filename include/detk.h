@@ -159,6 +159,32 @@ int detk_topk_ragged_transform(const float* scores, const int32_t* row_starts, c
                                int32_t max_len, int k, const detk_index_transform* transform, int32_t* out_idx,
                                float* out_val, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * 16-bit float scores (detk_topk_ragged_16bit): the same operation on binary16 or bfloat16
+ * bit patterns, ordered by IEEE totalOrder on their 16 bits (NaNs by their bits, -0 below
+ * +0), ties by index; half the score bytes of float32 per element.  The pages list a
+ * 16-bit (fp16) coarse first pass among the deterministic backend's follow-up levers
+ * (SGLang PR #31115, "Speed Tests and Profiling").
+ */
+#define DETK_DTYPE_F32 0
+#define DETK_DTYPE_F16 1
+#define DETK_DTYPE_BF16 2
+
+/*
+ * detk_topk_ragged_16bit -- detk_topk_ragged_transform on 16-bit scores.
+ *   scores   device, B rows of `dtype` (DETK_DTYPE_F16 or DETK_DTYPE_BF16) bit patterns,
+ *            addressed in elements exactly as the float32 entry points address theirs.
+ *   out_val  device uint16[B * k] or NULL: the selected scores' exact 16 bits; padded
+ *            slots hold the format's -inf (0xFC00 binary16, 0xFF80 bfloat16).
+ *   transform, out_idx, workspace, stream: as for detk_topk_ragged_transform (transform
+ *            may be NULL).  detk_workspace_size() gives the same workspace need.
+ * Errors are those of detk_topk_ragged_transform, plus DETK_ERR_INVALID_ARG for another
+ * dtype, found on the host before any launch.
+ */
+int detk_topk_ragged_16bit(const void* scores, int dtype, const int32_t* row_starts, const int32_t* lengths, int B,
+                           int32_t max_len, int k, const detk_index_transform* transform, int32_t* out_idx,
+                           void* out_val, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the per-GPU scratch array behind detk_topk_ragged_noalloc (16 MiB). */
 #define DETK_SCRATCH_BYTES ((size_t)16 << 20)
 

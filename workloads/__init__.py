@@ -228,7 +228,8 @@ def round_to_16bit(x32: np.ndarray, fmt: str) -> np.ndarray:
     the float32 bits after round to nearest even; NaNs stay NaN with their sign, quieted)."""
     x32 = np.ascontiguousarray(x32, dtype=np.float32)
     if fmt == "f16":
-        return x32.astype(np.float16).view(np.uint16)
+        with np.errstate(over="ignore"):  # (beyond 65504 rounds to infinity, as intended)
+            return x32.astype(np.float16).view(np.uint16)
     u = x32.view(np.uint32).astype(np.uint64)
     rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
     nan = np.isnan(x32)
