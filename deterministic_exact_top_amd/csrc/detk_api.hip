@@ -28,16 +28,17 @@ using detk::min_waves;
 using detk::kSingleMaxLen;
 using detk::kSplitTile;
 
-template <int TILE, int KMAX, bool MULTI, int VB = 4>
+template <int TILE, int KMAX, bool MULTI, int VB = 4, bool WIDE = false>
 const void* kernel_ptr() {
-    using S = Shape<TILE, MULTI>;
+    using S = Shape<TILE, MULTI, WIDE>;
     return reinterpret_cast<const void*>(
-        &detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>(), VB>);
+        &detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI, WIDE>(), VB>);
 }
 
-template <int TILE, int KMAX, bool MULTI>
+template <int TILE, int KMAX, bool MULTI, bool WIDE = false>
 constexpr size_t smem_bytes() {
-    return sizeof(SmemAll<Shape<TILE, MULTI>::NT, Shape<TILE, MULTI>::EPT, KMAX, MULTI>);
+    using S = Shape<TILE, MULTI, WIDE>;
+    return sizeof(SmemAll<S::NT, S::EPT, KMAX, MULTI>);
 }
 
 struct DeviceInfo {
@@ -55,11 +56,12 @@ int g_force_path = 0;       // 0 auto, 1 single, 2 multi
 int g_stage_cap = -1;       // -1 default
 int g_multi_tile = 0;       // 0 default
 int g_fast = 1;             // 0 off, 1 on, 2 on with a pivot that always misses
+int g_small = 0;            // 0 by batch size, 1 never the small-batch shapes, 2 always
 
-template <int TILE, int KMAX, bool MULTI, int VB>
+template <int TILE, int KMAX, bool MULTI, int VB, bool WIDE = false>
 hipError_t prepare_kernel() {
-    return hipFuncSetAttribute(kernel_ptr<TILE, KMAX, MULTI, VB>(), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)smem_bytes<TILE, KMAX, MULTI>());
+    return hipFuncSetAttribute(kernel_ptr<TILE, KMAX, MULTI, VB, WIDE>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)smem_bytes<TILE, KMAX, MULTI, WIDE>());
 }
 
 template <int TILE, int VB>
@@ -69,6 +71,10 @@ void prepare_all(hipError_t* e) {
     if ((r = prepare_kernel<TILE, 4096, false, VB>()) != hipSuccess) *e = r;
     if ((r = prepare_kernel<TILE, 2048, true, VB>()) != hipSuccess) *e = r;
     if ((r = prepare_kernel<TILE, 4096, true, VB>()) != hipSuccess) *e = r;
+    if constexpr (TILE < 32768) {
+        if ((r = prepare_kernel<TILE, 2048, false, VB, true>()) != hipSuccess) *e = r;
+        if ((r = prepare_kernel<TILE, 4096, false, VB, true>()) != hipSuccess) *e = r;
+    }
 }
 
 template <int TILE, int KMAX>
@@ -123,6 +129,8 @@ struct Plan {
     int tile = 0;         // elements per workgroup tile
     int kmax = 2048;
     int tiles_per_row = 1;
+    bool wide = false;    // one workgroup per row, small-batch (1024-thread) shape
+    bool small = false;   // no more workgroups than CUs: every wave selects pivot digits
     int grid = 0;
     size_t lds = 0;
     size_t ws_bytes = 0;
@@ -150,7 +158,19 @@ size_t lds_bytes_t(int tile, int kmax) {
     default: return k2 ? smem_bytes<32768, 2048, MULTI>() : smem_bytes<32768, 4096, MULTI>();
     }
 }
-size_t lds_bytes(int tile, int kmax, bool multi) { return multi ? lds_bytes_t<true>(tile, kmax) : lds_bytes_t<false>(tile, kmax); }
+size_t lds_bytes_wide(int tile, int kmax) {
+    const bool k2 = kmax == 2048;
+    switch (tile) {
+    case 4096: return k2 ? smem_bytes<4096, 2048, false, true>() : smem_bytes<4096, 4096, false, true>();
+    case 8192: return k2 ? smem_bytes<8192, 2048, false, true>() : smem_bytes<8192, 4096, false, true>();
+    case 16384: return k2 ? smem_bytes<16384, 2048, false, true>() : smem_bytes<16384, 4096, false, true>();
+    default: return k2 ? smem_bytes<32768, 2048, false, true>() : smem_bytes<32768, 4096, false, true>();
+    }
+}
+size_t lds_bytes(int tile, int kmax, bool multi, bool wide) {
+    if (wide) return lds_bytes_wide(tile, kmax);
+    return multi ? lds_bytes_t<true>(tile, kmax) : lds_bytes_t<false>(tile, kmax);
+}
 
 // Most workgroups launched for the split-row kernel; more items are taken by a grid-stride
 // loop (the items never wait for one another, so any number may be resident).
@@ -181,6 +201,9 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         pl->tiles_per_row = 1;
         pl->grid = B;  // one workgroup per row: the dispatcher balances rows of unequal length
         pl->ws_bytes = 0;
+        // A batch with no more rows than CUs gives every row a CU of its own: then 1024
+        // threads per row shorten the row's serial phases (the latency of a decode step).
+        pl->wide = g_small == 2 || (g_small == 0 && (int64_t)B <= dev.cus);
     } else {
         // 16K-element tiles spread a row over more CUs; when a batch has more of them than
         // the GPU holds at once, 32K-element tiles (half as many workgroups, each ordering
@@ -207,15 +230,18 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         while (data_offset(w) + off > w || (size_t)B * kCtlRowBytes > data_offset(w)) w += 256;
         pl->ws_bytes = w;
     }
-    pl->lds = lds_bytes(pl->tile, pl->kmax, pl->multi);
+    // Every wave selects the pivot digits itself when no more workgroups are launched than
+    // CUs: one barrier fewer per pivot pass, where issue slots are not what limits the call.
+    pl->small = g_small == 2 || (g_small == 0 && (int64_t)pl->grid <= dev.cus);
+    pl->lds = lds_bytes(pl->tile, pl->kmax, pl->multi, pl->wide);
     if (pl->lds > dev.max_lds) return DETK_ERR_UNSUPPORTED;
     return DETK_OK;
 }
 
-template <int TILE, int KMAX, bool MULTI, int VB>
+template <int TILE, int KMAX, bool MULTI, int VB, bool WIDE = false>
 hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
-    using S = Shape<TILE, MULTI>;
-    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI>(), VB>),
+    using S = Shape<TILE, MULTI, WIDE>;
+    hipLaunchKernelGGL((detk::topk_ragged_kernel<S::NT, S::EPT, KMAX, MULTI, min_waves<TILE, KMAX, MULTI, WIDE>(), VB>),
                        dim3(grid), dim3(S::NT), lds, stream, p);
     return hipGetLastError();
 }
@@ -223,6 +249,17 @@ hipError_t launch(const Params& p, int grid, size_t lds, hipStream_t stream) {
 template <int VB>
 hipError_t dispatch_vb(const Plan& pl, const Params& p, hipStream_t stream) {
     const bool k2 = pl.kmax == 2048;
+    if (!pl.multi && pl.wide) {
+        switch (pl.tile) {
+        case 4096: return k2 ? launch<4096, 2048, false, VB, true>(p, pl.grid, pl.lds, stream)
+                             : launch<4096, 4096, false, VB, true>(p, pl.grid, pl.lds, stream);
+        case 8192: return k2 ? launch<8192, 2048, false, VB, true>(p, pl.grid, pl.lds, stream)
+                             : launch<8192, 4096, false, VB, true>(p, pl.grid, pl.lds, stream);
+        case 16384: return k2 ? launch<16384, 2048, false, VB, true>(p, pl.grid, pl.lds, stream)
+                              : launch<16384, 4096, false, VB, true>(p, pl.grid, pl.lds, stream);
+        default: break;  // the 32768-element tile has 1024 threads already
+        }
+    }
     if (!pl.multi) {
         switch (pl.tile) {
         case 4096: return k2 ? launch<4096, 2048, false, VB>(p, pl.grid, pl.lds, stream)
@@ -307,6 +344,7 @@ int run(const void* scores, int dtype, const int32_t* row_starts, const int32_t*
     p.tiles_per_row = pl.tiles_per_row;
     p.stage_cap = g_stage_cap < 0 ? detk::kStageCap : (g_stage_cap > detk::kStageCap ? detk::kStageCap : g_stage_cap);
     p.fast = g_fast;
+    p.small_batch = pl.small ? 1 : 0;
     p.out_idx = out_idx;
     p.out_val = out_val;
     p.val_pad = dtype == DETK_DTYPE_F16 ? 0xFC00u : dtype == DETK_DTYPE_BF16 ? 0xFF80u : detk::kNegInfBits;
@@ -452,6 +490,10 @@ int detk_debug_set(int what, int value) {
     case DETK_DEBUG_FAST:
         if (value < 0 || value > 2) return DETK_ERR_INVALID_ARG;
         g_fast = value;
+        return DETK_OK;
+    case DETK_DEBUG_SMALL_BATCH:
+        if (value < 0 || value > 2) return DETK_ERR_INVALID_ARG;
+        g_small = value;
         return DETK_OK;
     default: return DETK_ERR_INVALID_ARG;
     }

@@ -77,6 +77,8 @@ struct Params {
     int32_t tiles_per_row;      // split-row kernel only
     int32_t stage_cap;          // <= kStageCap
     int32_t fast;               // 1: try the pivot fast path first
+    int32_t small_batch;        // nonzero: no more workgroups than CUs (latency over issue
+                                // slots: every wave selects the pivot digits itself)
     int32_t* out_idx;
     void* out_val;              // nullable: VB-byte values
     uint32_t val_pad;           // the value written in padded slots (-inf of the format)
@@ -670,6 +672,7 @@ struct RowCtx {
     int32_t* oidx;
     ValOut ov;
     IndexOut xo;
+    bool wave_select;  // every wave selects the pivot digits itself (no publishing barrier)
 };
 
 // ----------------------------------------------------------------------------- fast path
@@ -691,6 +694,8 @@ enum : int {
     kCtlLast = 12,      // several workgroups: this tile arrived last
     kCtlRowCgt = 13,    // several workgroups: the row's candidates (last arriver)
     kCtlPool = 15,      // one workgroup: slots claimed in the candidate pool
+    kCtlBinNotMin = 0,  // pivot: max of ~key over the samples in the selected 16-bit bin
+    kCtlBinMax = 14,    // pivot: max of key over the same samples
 };
 
 // Real samples among a tile's nt elements (uniform): slot i * EPT / kSamplesPerLane of
@@ -733,7 +738,11 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 
 // P = the key prefix of the rr-th largest sample, MSB first, one 8-bit digit per pass;
 // a pass runs past the second only while the selected bin still holds more than
-// kRefineAbove samples, so after four passes P is that sample's key itself.  Pass p
+// kRefineAbove samples, so after four passes P is that sample's key itself.  When the
+// bin selected by the second pass holds more than kRefineAbove samples that all have one
+// key (a plateau of equal scores), that key is P at once, as four passes would make it
+// (ctl[kCtlBinNotMin] and ctl[kCtlBinMax], zero on entry, collect the bin's extremes
+// behind one barrier instead of the two passes' four).  Pass p
 // counts into hist + 256 (p % NH), NH regions zeroed beforehand with a barrier behind
 // (with NH < 4 a region is zeroed again, behind one more barrier, before its reuse); no
 // pass waits for the previous one's histogram to be cleared, and every wave then
@@ -744,7 +753,8 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 // publishes it behind one more barrier, instead of every wave repeating the selection.
 template <int NT, int NH, int SPL, class Merge>
 __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[SPL], uint32_t rr, uint32_t* hist,
-                                                 Merge&& merge, int* passes = nullptr, uint32_t* sel = nullptr) {
+                                                 Merge&& merge, uint32_t* ctl, int* passes = nullptr,
+                                                 uint32_t* sel = nullptr) {
     const int tid = opaque_tid();
     uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
     int pass = 0;
@@ -752,6 +762,28 @@ __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[SPL], uint
     for (; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         if (pass >= 2 && cnt <= kRefineAbove) break;  // uniform: bin resolved
+        if (pass == 2) {  // uniform: a crowded 16-bit bin; one key only?
+            uint32_t nmn = 0, mx = 0;
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) {
+                const bool in = (sk[i] >> 16) == prefix;
+                nmn = in ? max(nmn, ~sk[i]) : nmn;
+                mx = in ? max(mx, sk[i]) : mx;
+            }
+            nmn = wave_max(nmn);
+            mx = wave_max(mx);
+            if ((tid & 63) == 0) {
+                __hip_atomic_fetch_max(&ctl[kCtlBinNotMin], nmn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_max(&ctl[kCtlBinMax], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            __syncthreads();
+            const uint32_t lo = ~__builtin_amdgcn_readfirstlane(ctl[kCtlBinNotMin]);
+            if (lo == __builtin_amdgcn_readfirstlane(ctl[kCtlBinMax])) {  // uniform
+                P = lo;
+                pass = 4;
+                break;
+            }
+        }
         uint32_t* h = hist + (pass % NH) * kRadix;
         if (pass >= NH) {  // every wave has selected from this region's previous pass
             if (tid < kRadix) h[tid] = 0;
@@ -1086,6 +1118,31 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     return true;
 }
 
+// Ties at P from one tile's position bitmap, spread over every thread in position order:
+// thread t owns the tile's positions [t EPT, (t + 1) EPT), a field of one bitmap word
+// (word_at(w) reads word w).  The set bits, counted from `first` (ties in earlier tiles),
+// go to slots c_gt + i while i < need, as the index of tile position p0 + bit.  Returns
+// the tile's set bits.  Contains barriers (a block scan over wsum).
+template <int NT, int EPT, class WordAt>
+__device__ __forceinline__ uint32_t emit_ties(WordAt&& word_at, int32_t p0, uint32_t first, uint32_t need,
+                                              uint32_t c_gt, uint32_t vP, const RowCtx& r, uint32_t* wsum) {
+    static_assert(EPT <= 32 && 32 % EPT == 0, "a thread's positions lie in one bitmap word");
+    const int tid = opaque_tid();
+    uint32_t bits = word_at((tid * EPT) >> 5);
+    if constexpr (EPT < 32) bits = (bits >> ((tid * EPT) & 31)) & ((1u << EPT) - 1u);
+    uint32_t tot;
+    uint32_t rr = first + block_excl_scan<NT>((uint32_t)__popc(bits), wsum, &tot);
+    const int32_t pt = p0 + tid * EPT;
+    while (bits && rr < need) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        r.oidx[c_gt + rr] = r.xo((uint32_t)(pt + bit));
+        if (r.ov) r.ov.put(c_gt + rr, vP);
+        ++rr;
+    }
+    return tot;
+}
+
 // Bucket range [L, U]: L is the least sample above P, U the largest sample below
 // key(+inf) (the largest sample when P itself is +inf or +NaN), so neither a pivot on a
 // plateau of equal scores far below the kept keys nor a few +inf / NaN scores stretch
@@ -1134,7 +1191,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         // (fast_mode == 2, a test setting, takes the largest sample: the pivot misses.)
         const uint32_t rr = fast_mode == 2 ? 1u : pivot_rank(nsamp, m, nt);
         if (m < nt && rr < (uint32_t)nsamp) {
-            P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {}, &passes, s.ctl + kCtlSel);
+            P = pivot_passes<NT, 2>(sk, rr, shist, [](int, uint32_t*) {}, s.ctl, &passes,
+                                    r.wave_select ? nullptr : s.ctl + kCtlSel);
         } else if (m == nt && fast_mode != 2) {
             // The whole row is output: pivot on its least key, taken exactly.  No key lies
             // below it, so the keys equal to it are the tail, in index order from the
@@ -1295,34 +1353,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
         return false;
 
     // ------------------------------------------------ ties at P: smallest positions
-    if (ties) {
-        const uint32_t need = (uint32_t)m - c_gt;
-        constexpr int WPT = (BW + NT - 1) / NT;
-        uint32_t tc = 0;
-#pragma unroll
-        for (int q = 0; q < WPT; ++q) {
-            const int w = tid * WPT + q;
-            if (w < BW) tc += (uint32_t)__popc(s.bitmap[w]);
-        }
-        uint32_t tot;
-        uint32_t rr = block_excl_scan<NT>(tc, s.wsum, &tot);
-        const uint32_t vP = bits_of(P);
-#pragma unroll
-        for (int q = 0; q < WPT; ++q) {
-            const int w = tid * WPT + q;
-            if (w < BW) {
-                uint32_t word = s.bitmap[w];
-                while (word && rr < need) {
-                    const int bit = __ffs(word) - 1;
-                    word &= word - 1;
-                    r.oidx[c_gt + rr] = r.xo((uint32_t)(w * 32 + bit));
-                    if (r.ov) r.ov.put(c_gt + rr, vP);
-                    ++rr;
-                }
-                rr += (uint32_t)__popc(word);
-            }
-        }
-    }
+    if (ties)
+        emit_ties<NT, EPT>([&](int w) { return s.bitmap[w]; }, 0, 0u, (uint32_t)m - c_gt, c_gt, bits_of(P), r, s.wsum);
     write_padding<NT>(r.oidx, r.ov, m, r.k);
     return true;
 }
@@ -1431,7 +1463,9 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
         constexpr int nsamp = 4 * SL * NT;
         // (fast == 2, a test setting, aims at the largest sample: the pivot misses.)
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
-        if (rr < (uint32_t)nsamp) P = pivot_passes<NT, 4>(sk, rr, s.bucket, [](int, uint32_t*) {}, nullptr, s.ctl + kCtlSel);
+        if (rr < (uint32_t)nsamp)
+            P = pivot_passes<NT, 4>(sk, rr, s.bucket, [](int, uint32_t*) {}, s.ctl, nullptr,
+                                    r.wave_select ? nullptr : s.ctl + kCtlSel);
         {
             uint32_t lo = 0xFFFFFFFFu;
 #pragma unroll
@@ -1551,35 +1585,13 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     if (ties) {
         const uint32_t need = (uint32_t)m - c_gt;
         const uint32_t vP = bits_of(P);
-        constexpr int WPT = (BW + NT - 1) / NT;
         uint32_t off = 0;  // ties in earlier tiles (uniform)
 #pragma unroll 1
         for (int t = 0; t < ntiles && off < need; ++t) {
             const uint32_t e = ecnt[t];
             if (e == 0) continue;  // uniform: that tile stored no bitmap
             const uint32_t* const gt = p.ws_tie + ((int64_t)b * p.tiles_per_row + t) * BW;
-            uint32_t wv[WPT];
-            uint32_t tc = 0;
-#pragma unroll
-            for (int q = 0; q < WPT; ++q) {
-                const int w = tid * WPT + q;
-                wv[q] = w < BW ? gt[w] : 0u;
-                tc += (uint32_t)__popc(wv[q]);
-            }
-            uint32_t tot;
-            uint32_t rr2 = off + block_excl_scan<NT>(tc, s.wsum, &tot);
-#pragma unroll
-            for (int q = 0; q < WPT; ++q) {
-                uint32_t word = wv[q];
-                const int32_t wpos = t * TILE + (tid * WPT + q) * 32;
-                while (word && rr2 < need) {
-                    const int bit = __ffs(word) - 1;
-                    word &= word - 1;
-                    r.oidx[c_gt + rr2] = r.xo((uint32_t)(wpos + bit));
-                    if (r.ov) r.ov.put(c_gt + rr2, vP);
-                    ++rr2;
-                }
-            }
+            emit_ties<NT, EPT>([&](int w) { return gt[w]; }, t * TILE, off, need, c_gt, vP, r, s.wsum);
             off += e;
             __syncthreads();  // (wsum is scanned again next turn)
         }
@@ -1986,6 +1998,7 @@ __device__ __forceinline__ RowCtx row_setup(const Params& p, int b, int tile) {
     r.xo.ps = p.xf_page;
     r.xo.shift = p.xf_shift;
     r.xo.pt = p.xf_mode == 2 ? p.xf_table + (int64_t)b * p.xf_stride : nullptr;
+    r.wave_select = p.small_batch != 0;
     return r;
 }
 

@@ -243,12 +243,17 @@ int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream)
  *                                  it misses); 0 exact radix path only; 2 pivot forced
  *                                  to miss, so every row starts on the pivot path and
  *                                  falls back.
+ *   what = DETK_DEBUG_SMALL_BATCH: 0 default (a batch with no more workgroups than CUs
+ *                                  takes the small-batch shapes: 1024 threads per
+ *                                  one-workgroup row, pivot digits selected by every
+ *                                  wave); 1 never; 2 always.
  * Returns DETK_OK or DETK_ERR_INVALID_ARG.
  */
 #define DETK_DEBUG_PATH 1
 #define DETK_DEBUG_STAGING_CAP 2
 #define DETK_DEBUG_MULTI_TILE 3
 #define DETK_DEBUG_FAST 4
+#define DETK_DEBUG_SMALL_BATCH 5
 int detk_debug_set(int what, int value);
 
 #ifdef __cplusplus

@@ -55,8 +55,10 @@ def assert_same(gi, gv, oi, ov, what: str) -> None:
 
 
 @contextlib.contextmanager
-def debug_overrides(path=None, stage_cap=None, multi_tile=None, fast=None):
+def debug_overrides(path=None, stage_cap=None, multi_tile=None, fast=None, small=None):
     try:
+        if small is not None:
+            detk.debug_set(detk.DETK_DEBUG_SMALL_BATCH, small)
         if fast is not None:
             detk.debug_set(detk.DETK_DEBUG_FAST, fast)
         if path is not None:
@@ -71,3 +73,4 @@ def debug_overrides(path=None, stage_cap=None, multi_tile=None, fast=None):
         detk.debug_set(detk.DETK_DEBUG_STAGING_CAP, -1)
         detk.debug_set(detk.DETK_DEBUG_MULTI_TILE, 0)
         detk.debug_set(detk.DETK_DEBUG_FAST, 1)
+        detk.debug_set(detk.DETK_DEBUG_SMALL_BATCH, 0)

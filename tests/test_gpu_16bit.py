@@ -75,7 +75,8 @@ SMALL = {
     "specials": _specials,
     "unaligned": _unaligned,
 }
-SHAPES = {"auto": {}, "exact": {"fast": 0}, "pivot_miss": {"fast": 2}, "split4096": {"path": 2, "multi_tile": 4096}}
+SHAPES = {"auto": {}, "exact": {"fast": 0}, "pivot_miss": {"fast": 2}, "split4096": {"path": 2, "multi_tile": 4096},
+          "many_rows": {"small": 1}}
 
 
 @pytest.mark.parametrize("shape", sorted(SHAPES))

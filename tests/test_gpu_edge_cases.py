@@ -48,7 +48,8 @@ def _check(dev, wl, what, **over):
     check_batch(wl.scores.view(np.uint32), wl.row_starts, wl.lengths, wl.max_len, wl.k, gi, gv)
 
 
-SHAPES = {"auto": {}, "single": {"path": 1}, "multi": {"path": 2, "multi_tile": 4096}}
+SHAPES = {"auto": {}, "single": {"path": 1, "small": 1}, "wide": {"path": 1, "small": 2},
+          "multi": {"path": 2, "multi_tile": 4096}}
 
 
 @pytest.mark.parametrize("shape", sorted(SHAPES))
@@ -188,7 +189,7 @@ def test_candidates_crowd_one_wave(dev, shift):
         pw = _wave_positions(n, wave=wave)
         r[pw] += np.float32(shift)
         rows.append(r)
-    _check(dev, _dense(rows, 2048, "crowd"), "candidates crowd one wave (shift %.2f)" % shift, path=1)
+    _check(dev, _dense(rows, 2048, "crowd"), "candidates crowd one wave (shift %.2f)" % shift, path=1, small=1)
 
 
 def test_only_one_wave_has_candidates(dev):
@@ -199,7 +200,7 @@ def test_only_one_wave_has_candidates(dev):
     r = np.zeros(n, np.float32)
     pw = _wave_positions(n, wave=0)
     r[pw] = (np.abs(rng.standard_normal(pw.size)) + 0.01).astype(np.float32)
-    _check(dev, _dense([r, r.copy()], 2048, "one_wave"), "only one wave has candidates", path=1)
+    _check(dev, _dense([r, r.copy()], 2048, "one_wave"), "only one wave has candidates", path=1, small=1)
 
 
 def _bottom_family(rng, fam, n):

@@ -119,25 +119,34 @@ def _small(name):
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
-@pytest.mark.parametrize("shape", ["auto", "single", "single_exact", "single_pivot_miss", "multi4096", "multi8192",
-                                   "multi16384", "multi32768", "multi_exact", "multi_pivot_miss", "single_rescan",
-                                   "multi_rescan", "multi_tinystage"])
+@pytest.mark.parametrize("shape", ["auto", "single", "single_exact", "single_pivot_miss", "wide", "wide_exact",
+                                   "wide_pivot_miss", "wide_rescan", "multi4096", "multi8192", "multi16384",
+                                   "multi32768", "multi_exact", "multi_pivot_miss", "multi_wave_select",
+                                   "multi_block_select", "single_rescan", "multi_rescan", "multi_tinystage"])
 def test_small_workloads(dev, name, shape):
     wl = _small(name)
-    if shape.startswith("single") and wl.max_len > 32768:
+    if (shape.startswith("single") or shape.startswith("wide")) and wl.max_len > 32768:
         pytest.skip("row longer than one workgroup tile")
+    # single*: the many-row shapes (several rows per CU, one wave selects pivot digits);
+    # wide*: the small-batch shapes (1024 threads per row, every wave selects)
     cfg = {
         "auto": {},
-        "single": {"path": 1},
-        "single_exact": {"path": 1, "fast": 0},
-        "single_pivot_miss": {"path": 1, "fast": 2},
+        "single": {"path": 1, "small": 1},
+        "single_exact": {"path": 1, "fast": 0, "small": 1},
+        "single_pivot_miss": {"path": 1, "fast": 2, "small": 1},
+        "wide": {"path": 1, "small": 2},
+        "wide_exact": {"path": 1, "fast": 0, "small": 2},
+        "wide_pivot_miss": {"path": 1, "fast": 2, "small": 2},
+        "wide_rescan": {"path": 1, "stage_cap": 0, "fast": 0, "small": 2},
+        "multi_wave_select": {"path": 2, "multi_tile": 4096, "small": 2},
+        "multi_block_select": {"path": 2, "multi_tile": 4096, "small": 1},
         "multi4096": {"path": 2, "multi_tile": 4096},
         "multi8192": {"path": 2, "multi_tile": 8192},
         "multi16384": {"path": 2, "multi_tile": 16384},
         "multi32768": {"path": 2, "multi_tile": 32768},
         "multi_exact": {"path": 2, "multi_tile": 4096, "fast": 0},
         "multi_pivot_miss": {"path": 2, "multi_tile": 4096, "fast": 2},
-        "single_rescan": {"path": 1, "stage_cap": 0, "fast": 0},
+        "single_rescan": {"path": 1, "stage_cap": 0, "fast": 0, "small": 1},
         "multi_rescan": {"path": 2, "multi_tile": 4096, "stage_cap": 0, "fast": 0},
         "multi_tinystage": {"path": 2, "multi_tile": 4096, "stage_cap": 3, "fast": 0},
     }[shape]

@@ -50,7 +50,8 @@ CASES = {
     "long_offsets": (lambda: W.long_context(B=5, L=100000, k=2048, short_n=1500, name="xf_long"), "offset", 1),
     "narrow_pages7": (lambda: W.narrow_range(B=6, L=70000, k=4096, name="xf_narrow"), "pages", 7),
 }
-SHAPES = {"auto": {}, "exact": {"fast": 0}, "pivot_miss": {"fast": 2}, "split4096": {"path": 2, "multi_tile": 4096}}
+SHAPES = {"auto": {}, "exact": {"fast": 0}, "pivot_miss": {"fast": 2}, "split4096": {"path": 2, "multi_tile": 4096},
+          "many_rows": {"small": 1}}
 
 
 @pytest.mark.parametrize("shape", sorted(SHAPES))
