@@ -249,9 +249,10 @@ def attainable_bandwidth() -> dict:
     }
 
 
-def graph_timing(wl, calls: int = 20) -> dict:
+def graph_timing(wl, calls: int = 20, outputs: bool = False) -> dict:
     """Per-call time with `calls` calls (over rotated input copies) captured in one HIP graph
-    and replayed: no host work between the kernels."""
+    and replayed: no host work between the kernels (the launches are bound once, at
+    capture).  outputs: also return the last replayed call's (out_idx, out_val)."""
     import torch
     import deterministic_exact_top_amd as detk
     dev = torch.device("cuda:0")
@@ -273,7 +274,65 @@ def graph_timing(wl, calls: int = 20) -> dict:
     g.replay()
     torch.cuda.synchronize()
     per = [u / calls for u in event_us(g.replay, 1, torch.cuda.current_stream(dev))]
-    return {"graph_us_per_call": float(np.median(per)), "calls_per_graph": calls, "input_copies": rotate}
+    res = {"graph_us_per_call": float(np.median(per)), "calls_per_graph": calls, "input_copies": rotate}
+    if outputs:
+        res["_outputs"] = (out_i.cpu().numpy(), out_v.cpu().numpy().view(np.uint32))
+    return res
+
+
+def empty_graph_floor(wl, calls: int = 20) -> float:
+    """Per-call time of the same call with every row empty (padding only), replayed from a
+    HIP graph: the launch and the smallest kernel, no host work."""
+    import torch
+    import deterministic_exact_top_amd as detk
+    dev = torch.device("cuda:0")
+    s = torch.zeros(16, device=dev)
+    rs = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+    ln = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+    out_i = torch.empty((wl.B, wl.k), dtype=torch.int32, device=dev)
+    out_v = torch.empty((wl.B, wl.k), dtype=torch.float32, device=dev)
+    ws = detk.new_workspace(wl.B, wl.k, wl.max_len, dev)
+    call = lambda: detk.topk_ragged(s, rs, ln, wl.k, max_len=wl.max_len, out_idx=out_i, out_val=out_v, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            call()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    return float(np.median([u / calls for u in event_us(g.replay, 1, torch.cuda.current_stream(dev))]))
+
+
+DECODE = ("plateau_4x4096", "decode_ragged_64")
+
+
+def decode_latency() -> dict:
+    """The decode-step figure: per-call latency of the small-batch workloads (rows fewer than
+    CUs), calls replayed from a HIP graph, with the small-batch shapes the library picks for
+    them (1024 threads per row, every wave selecting pivot digits) and, for comparison, with
+    the many-row shapes forced (the library's test switch); beside it the same call with
+    every row empty.  The replayed outputs are checked against the oracle."""
+    import deterministic_exact_top_amd as detk
+    import workloads as W
+    out = {}
+    for name in DECODE:
+        wl = W.full(name)
+        small = graph_timing(wl, outputs=True)
+        par = parity_check(wl, small.pop("_outputs"))
+        detk.debug_set(detk.DETK_DEBUG_SMALL_BATCH, 1)
+        try:
+            many = graph_timing(wl)
+        finally:
+            detk.debug_set(detk.DETK_DEBUG_SMALL_BATCH, 0)
+        out[name] = {"B": wl.B, "max_len": wl.max_len, "k": wl.k, "sum_n": wl.sum_n,
+                     "us_per_call": small["graph_us_per_call"],
+                     "us_per_call_many_row_shapes": many["graph_us_per_call"],
+                     "empty_call_us": empty_graph_floor(wl), "input_copies": small["input_copies"],
+                     "parity": {"ok": par["ok"], "gpu_sha256_16": par["gpu_sha256_16"],
+                                "oracle_sha256_16": par["oracle_sha256_16"]}}
+    return out
 
 
 def dispatch_floor(wl) -> dict:
@@ -410,6 +469,8 @@ def main():
                     help="add the bandwidth a plain streaming read and a plain copy reach on this GPU")
     ap.add_argument("--graph", action="store_true", help="add the per-call time with the calls replayed from a HIP graph")
     ap.add_argument("--floor", action="store_true", help="add the per-call time of the same call with every row empty")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step latency of the small-batch workloads (graph replay)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -469,6 +530,10 @@ def main():
         ok_all = m["parity"]["ok"] and m2["parity"]["ok"]
     else:
         ok_all = m["parity"]["ok"]
+    if not args.no_decode and args.dtype == "f32" and args.index_transform == "none":
+        log("timing decode-step latency")
+        result["decode_latency"] = decode_latency()
+        ok_all = ok_all and all(v["parity"]["ok"] for v in result["decode_latency"].values())
     if args.graph:
         log("timing graph replay")
         result["graph"] = graph_timing(wl)

@@ -266,6 +266,73 @@ def to16(wl: Workload, fmt: str) -> Workload16:
                       wl.max_len, wl.k)
 
 
+@dataclasses.dataclass
+class IndexerInputs:
+    """Inputs of the lightning-indexer score for a batch of query rows over one key sequence:
+    q (bfloat16 bits, [B, H, D]), per-query head weights w (float32, [B, H]), keys
+    (bfloat16 bits, [Lk, D]), and each row's key window (key_starts, lengths, max_len)."""
+    name: str
+    q: np.ndarray
+    w: np.ndarray
+    keys: np.ndarray
+    key_starts: np.ndarray
+    lengths: np.ndarray
+    max_len: int
+    k: int
+
+    @property
+    def B(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def D(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def sum_n(self) -> int:
+        return int(np.clip(self.lengths.astype(np.int64), 0, self.max_len).sum())
+
+
+def indexer_causal(Q: int = 8192, ctx: int = 16384, H: int = HEADS, D: int = 128, rho: float = 0.9,
+                   mu: float = -1.0, k: int = 2048, name: str = "indexer_causal") -> IndexerInputs:
+    """Queries and keys whose per-head dot products follow the synthetic indexer model of the
+    "score stats" script (SGLang PR #31115, review thread): the logit of head h against key t
+    is mu + sqrt(rho) c_t + sqrt(1 - rho) z_ht, with c_t a shared relevance factor of the key.
+    Here that model is carried by real vectors: key t = (1, c_t, r_t) with r_t ~ N(0, I / (D - 2)),
+    query head h = (mu, sqrt(rho), sqrt(1 - rho) g_h) with g_h ~ N(0, I), so q.k = mu +
+    sqrt(rho) c_t + sqrt(1 - rho) g_h.r_t (the last term ~ N(0, |r_t|^2), |r_t|^2 ~ 1); all
+    rounded to bfloat16.  Head weights w ~ U(0, 1) / H per query row.  Windows as in the
+    chunked-prefill causal workload: row i covers keys [0, ctx - Q + i] (n_i = ctx - Q + i + 1)."""
+    seed = seed_of(name)
+    kr = row_rng(seed, 0xFFFF)
+    c = kr.standard_normal(ctx)
+    keys = np.empty((ctx, D), np.float32)
+    keys[:, 0] = 1.0
+    keys[:, 1] = c
+    keys[:, 2:] = kr.standard_normal((ctx, D - 2)) / np.sqrt(D - 2)
+    q = np.empty((Q, H, D), np.float32)
+    w = np.empty((Q, H), np.float32)
+    def one(b):
+        rng = row_rng(seed, b)
+        q[b, :, 0] = mu
+        q[b, :, 1] = np.sqrt(rho)
+        q[b, :, 2:] = np.sqrt(1.0 - rho) * rng.standard_normal((H, D - 2))
+        w[b] = (rng.random(H) / H).astype(np.float32)
+    if Q > 8:
+        with _cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, range(Q)))
+    else:
+        for b in range(Q):
+            one(b)
+    lengths = (ctx - Q + 1 + np.arange(Q)).astype(np.int32)
+    return IndexerInputs(name, round_to_16bit(q, "bf16").reshape(Q, H, D), w,
+                         round_to_16bit(keys, "bf16").reshape(ctx, D), np.zeros(Q, np.int32), lengths, ctx, k)
+
+
 FULL = {
     "plateau_4x4096": plateau_abs,
     "decode_ragged_64": decode_ragged,
