@@ -77,6 +77,8 @@ def load_library():
     lib.detk_topk_ragged_noalloc.restype = ctypes.c_int
     lib.detk_status_string.argtypes = [ctypes.c_int]
     lib.detk_status_string.restype = ctypes.c_char_p
+    lib.detk_indexer_scores.argtypes = [vp, vp, vp, i32, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32, vp, vp]
+    lib.detk_indexer_scores.restype = ctypes.c_int
     lib.detk_debug_set.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.detk_read_probe.argtypes = [vp, sz, vp, vp]
     lib.detk_read_probe.restype = ctypes.c_int
@@ -250,3 +252,39 @@ def topk_ragged_noalloc(scores, row_starts, lengths, k: int, max_len: int, out_i
     if st != DETK_OK:
         raise DetkError(st, "detk_topk_ragged_noalloc")
     return out_idx, out_val
+
+
+INDEXER_HEADS = 16
+INDEXER_HEAD_DIM = 128
+
+
+def indexer_scores(q, w, keys, lengths=None, max_len: int | None = None, out=None, stream=None):
+    """detk_indexer_scores: out[b, t] = sum_h w[b, h] * max(0, q[b, h] . keys[t]) for t < n_b.
+
+    q: bfloat16 (or its uint16/int16 bit patterns) CUDA tensor [B, 16, 128]; w: float32 [B, 16];
+    keys: bfloat16 [n_keys, 128]; lengths: int32 [B] or None (every window max_len keys);
+    max_len defaults to n_keys.  Returns out, float32 [B, max_len] (entries past a row's window
+    are left as they were: zero when out is allocated here)."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("keys", keys)):
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bfloat16 (or 16-bit pattern) CUDA tensor" % name)
+    if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 CUDA tensor")
+    if q.dim() != 3 or w.dim() != 2 or keys.dim() != 2:
+        raise ValueError("q is [B, heads, head_dim], w [B, heads], keys [n_keys, head_dim]")
+    B, H, D = (int(x) for x in q.shape)
+    n_keys = int(keys.shape[0])
+    if max_len is None:
+        max_len = n_keys
+    if lengths is not None and (lengths.dtype != torch.int32 or not lengths.is_cuda):
+        raise ValueError("lengths must be an int32 CUDA tensor")
+    if out is None:
+        out = torch.zeros((B, max_len), dtype=torch.float32, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lib.detk_indexer_scores(_ptr(q), _ptr(w), _ptr(keys), int(n_keys), _ptr(lengths), B, H, D, int(max_len),
+                                 _ptr(out), ctypes.c_void_p(s.cuda_stream))
+    if st != DETK_OK:
+        raise DetkError(st, "detk_indexer_scores")
+    return out

@@ -10,8 +10,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 # the host API and one translation unit per tile size's kernels, compiled in parallel
 SOURCES = [os.path.join(CSRC, n) for n in ("detk_api.hip", "inst_4096.hip", "inst_8192.hip", "inst_16384.hip",
-                                           "inst_32768.hip")]
+                                           "inst_32768.hip", "indexer.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, "topk_device.hpp"), os.path.join(CSRC, "kernels.hpp"),
+                  os.path.join(CSRC, "indexer.hpp"),
                   os.path.join(ROOT, "include", "detk.h")]
 OUT = os.path.join(HERE, "libdetk.so")
 

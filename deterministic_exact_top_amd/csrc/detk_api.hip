@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "../../include/detk.h"
+#include "indexer.hpp"
 #include "kernels.hpp"
 
 // Workspace of detk_topk_ragged_noalloc: one array per GPU the library runs on, held until
@@ -470,6 +471,36 @@ int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream_
     hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream_ptr),
                        reinterpret_cast<const uint4*>(data), n16, out);
     return hipGetLastError() == hipSuccess ? DETK_OK : DETK_ERR_HIP;
+}
+
+int detk_indexer_scores(const void* q, const float* w, const void* keys, int32_t n_keys, const int32_t* lengths,
+                        int B, int heads, int head_dim, int32_t max_len, float* out, void* stream) {
+    if (B < 0 || max_len < 0 || n_keys < 0) return DETK_ERR_INVALID_ARG;
+    if (heads != detk_ix::kHeads || head_dim != detk_ix::kHeadDim) return DETK_ERR_UNSUPPORTED;
+    if (max_len > n_keys) return DETK_ERR_INVALID_ARG;  // every window lies inside the keys
+    if (B == 0 || max_len == 0) return DETK_OK;
+    if (!q || !w || !keys || !out) return DETK_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(keys)) & 15u)
+        return DETK_ERR_INVALID_ARG;  // 16-byte loads
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return DETK_ERR_HIP;
+    DeviceInfo dev;
+    const int st = device_info(device, &dev);
+    if (st != DETK_OK) return st;
+    if (!dev.gfx950) return DETK_ERR_UNSUPPORTED;
+    detk_ix::IxParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.w = w;
+    p.keys = static_cast<const uint16_t*>(keys);
+    p.lengths = lengths;
+    p.B = B;
+    p.max_len = max_len;
+    p.n_keys = n_keys;
+    p.chunks = (max_len + detk_ix::kChunk - 1) / detk_ix::kChunk;
+    p.out = out;
+    const hipError_t e = detk_ix::launch_indexer(p, reinterpret_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidValue) return DETK_ERR_UNSUPPORTED;  // grid beyond 2^31 - 1 workgroups
+    return e == hipSuccess ? DETK_OK : DETK_ERR_HIP;
 }
 
 int detk_debug_set(int what, int value) {

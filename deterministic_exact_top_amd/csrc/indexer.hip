@@ -1,0 +1,170 @@
+// indexer.hip -- the lightning-indexer score producer on the matrix cores (gfx950).
+//
+// SGLang PR #31115, review thread: the DSA lightning-indexer score of a query against a
+// key is a sum over the indexer heads of ReLU-ed per-head dot products, weighted per head:
+//     score[b, t] = sum_h w[b, h] * max(0, q[b, h, :] . k[t, :]),   t < n_b,
+// which puts every key whose heads all score non-positive on exactly 0.0 -- the plateau
+// the top-k selector is built to resolve.  Per query this is a [H x D] x [D x n] product
+// followed by a weighted ReLU reduction over H, so it runs on the MFMA units
+// (v_mfma_f32_16x16x32_bf16: bfloat16 operands, float32 accumulation) with the ReLU and the
+// head reduction fused into the epilogue: the per-head logits never leave registers, and
+// only the [B, max_len] float32 scores are written.
+//
+// Work split: a 256-thread workgroup (4 waves) takes 16 query rows (4 per wave) and one
+// chunk of kChunk keys, walked in blocks of kKeyBlock keys.  A block's keys are staged in
+// LDS (padded rows, double-buffered: the next block's loads are in flight during this
+// block's MFMAs) and shared by the 16 queries; each wave keeps its queries' q fragments in
+// registers for the whole chunk.  Per block and wave: 4 queries x 4 key groups of 16 x
+// D / 32 steps MFMAs.  MFMA operand layout (16x16x32): lane l holds A[l % 16][8 (l / 16) + j]
+// and B[8 (l / 16) + j][l % 16] (j < 8), and C[4 (l / 16) + i][l % 16] (i < 4); here
+// A = the query's heads x head dims, B = head dims x 16 keys, so C holds four heads of one
+// key per lane.  The epilogue sums a lane's four heads (w_h * max(0, c_h)), then the four
+// lane groups by two fixed exchanges, so every lane holds the same bits whatever the
+// schedule.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "indexer.hpp"
+
+namespace detk_ix {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = kHeadDim;               // head dimension (contraction length)
+constexpr int kH = kHeads;                 // heads (the MFMA's 16 rows)
+constexpr int kSteps = kD / 32;            // MFMA steps over the head dimension
+constexpr int kQPerWave = 4;
+constexpr int kWaves = 4;
+constexpr int kQPerGroup = kQPerWave * kWaves;  // query rows per workgroup
+constexpr int kKeyBlock = 64;              // keys per staged block (4 groups of 16)
+constexpr int kRowBytes = kD * 2 + 16;     // LDS bytes per staged key row (16 bytes of padding)
+constexpr int kChunksPerThread = kKeyBlock * kD * 2 / 16 / 256;  // 16-byte loads per thread per block
+static_assert(kH == 16, "one 16-row MFMA tile of heads");
+static_assert(kD % 32 == 0 && kChunksPerThread * 256 * 16 == kKeyBlock * kD * 2, "whole 16-byte loads");
+
+constexpr int32_t kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9-family data format
+
+__device__ __forceinline__ int32_t row_len(const IxParams& p, int64_t b) {
+    if (b >= p.B) return 0;
+    const int32_t len = p.lengths ? p.lengths[b] : p.max_len;
+    return min(max(len, 0), p.max_len);
+}
+
+__global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
+    __shared__ __align__(16) unsigned char stage[2][kKeyBlock * kRowBytes];
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t group = (int64_t)blockIdx.x / p.chunks;
+    const int chunk = (int)((int64_t)blockIdx.x % p.chunks);
+    const int64_t q0 = group * kQPerGroup;
+
+    // The workgroup's key range: its chunk, cut at the longest window of its rows.
+    int32_t nmax = 0;
+    for (int j = 0; j < kQPerGroup; ++j) nmax = max(nmax, row_len(p, q0 + j));
+    const int32_t k_begin = chunk * kChunk;
+    const int32_t k_end = min(k_begin + kChunk, nmax);
+    if (k_begin >= k_end) return;  // uniform: no row of the group reaches this chunk
+
+    // This wave's rows: q fragments (rows past the batch are zero) and head weights.
+    int32_t nq[kQPerWave];
+    int64_t qi[kQPerWave];
+    bf16x8 a[kQPerWave][kSteps];
+    f32x4 wv[kQPerWave];
+#pragma unroll
+    for (int j = 0; j < kQPerWave; ++j) {
+        qi[j] = q0 + wave * kQPerWave + j;
+        nq[j] = row_len(p, qi[j]);
+        const bool live = qi[j] < p.B;
+        const uint16_t* const qrow = p.q + (qi[j] * kH + (lane & 15)) * kD + 8 * (lane >> 4);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const uint4 v = live ? *reinterpret_cast<const uint4*>(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
+            a[j][s] = __builtin_bit_cast(bf16x8, v);
+        }
+        wv[j] = live ? *reinterpret_cast<const f32x4*>(p.w + qi[j] * kH + 4 * (lane >> 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Key blocks: 16-byte loads through a buffer resource over the key rows (rows past
+    // n_keys read as zero, so a block never reads outside the keys).
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.keys), (short)0, (int)min<int64_t>((int64_t)p.n_keys * kD * 2, 0x7FFFFFFF), kBufferWord3);
+    uint4 kr[kChunksPerThread];
+    auto load_block = [&](int32_t kb) {
+#pragma unroll
+        for (int i = 0; i < kChunksPerThread; ++i) {
+            const int c = tid + 256 * i;  // 16-byte chunk: row c / (kD / 8), column c % (kD / 8)
+            const int row = c / (kD / 8), col = c % (kD / 8);
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (row * kD + col * 8) * 2, kb * kD * 2, 0);
+            kr[i] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
+    auto stage_block = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kChunksPerThread; ++i) {
+            const int c = tid + 256 * i;
+            const int row = c / (kD / 8), col = c % (kD / 8);
+            *reinterpret_cast<uint4*>(stage[buf] + row * kRowBytes + col * 16) = kr[i];
+        }
+    };
+
+    load_block(k_begin);
+    stage_block(0);
+    __syncthreads();
+    int it = 0;
+    for (int32_t kb = k_begin; kb < k_end; kb += kKeyBlock, ++it) {
+        const int buf = it & 1;
+        const bool more = kb + kKeyBlock < k_end;  // uniform
+        if (more) load_block(kb + kKeyBlock);      // (in flight during the MFMAs)
+
+        f32x4 acc[kQPerWave][4];
+#pragma unroll
+        for (int j = 0; j < kQPerWave; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const bf16x8 bk = *reinterpret_cast<const bf16x8*>(stage[buf] + (16 * g + (lane & 15)) * kRowBytes +
+                                                                   (32 * s + 8 * (lane >> 4)) * 2);
+#pragma unroll
+                for (int j = 0; j < kQPerWave; ++j)
+                    acc[j][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][s], bk, acc[j][g], 0, 0, 0);
+            }
+        }
+
+        // Epilogue: lane l holds heads 4 (l / 16) .. + 3 of key 16 g + l % 16.
+#pragma unroll
+        for (int j = 0; j < kQPerWave; ++j) {
+            float r[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float part = wv[j][0] * fmaxf(acc[j][g][0], 0.f);
+                part += wv[j][1] * fmaxf(acc[j][g][1], 0.f);
+                part += wv[j][2] * fmaxf(acc[j][g][2], 0.f);
+                part += wv[j][3] * fmaxf(acc[j][g][3], 0.f);
+                part += __shfl_xor(part, 16);
+                part += __shfl_xor(part, 32);
+                r[g] = part;
+            }
+            // lane l stores key kb + l: group l / 16, column l % 16 (one 256-byte store)
+            const int lg = lane >> 4;
+            const float v = lg == 0 ? r[0] : lg == 1 ? r[1] : lg == 2 ? r[2] : r[3];
+            const int32_t t = kb + lane;
+            if (t < nq[j]) p.out[qi[j] * p.max_len + t] = v;
+        }
+        if (more) stage_block(buf ^ 1);  // (nobody reads that buffer until the barrier)
+        __syncthreads();
+    }
+}
+
+hipError_t launch_indexer(const IxParams& p, hipStream_t stream) {
+    const int64_t groups = ((int64_t)p.B + kQPerGroup - 1) / kQPerGroup;
+    const int64_t grid = groups * p.chunks;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(indexer_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace detk_ix

@@ -209,6 +209,31 @@ int detk_topk_ragged_noalloc(const float* scores, const int32_t* row_starts, con
                              int32_t max_len, int k, int32_t* out_idx, float* out_val, void* stream);
 
 /*
+ * detk_indexer_scores -- the score producer upstream of the selection: the DSA
+ * lightning-indexer score (SGLang PR #31115, review thread: a sum over the indexer heads
+ * of ReLU-ed per-head dot products, weighted per head, which is why keys whose heads all
+ * score non-positive sit on exactly 0.0), for B query rows over one key sequence:
+ *     out[b * max_len + t] = sum_h w[b * heads + h] *
+ *                            max(0, sum_d q[(b * heads + h) * head_dim + d] * keys[t * head_dim + d])
+ * for t < n_b = clamp(lengths[b], 0, max_len) (lengths NULL: n_b = max_len): row b's window
+ * is keys[0, n_b), as in chunked causal prefill.  Entries t >= n_b of a row are not written.
+ *   q     device, bfloat16 bit patterns, [B][heads][head_dim], 16-byte aligned
+ *   w     device, float32, [B][heads], 16-byte aligned
+ *   keys  device, bfloat16 bit patterns, [n_keys][head_dim], 16-byte aligned
+ *   out   device, float32, [B][max_len] -- the layout detk_topk_ragged reads with
+ *         row_starts NULL (row b at b * max_len), so the two calls chain on one stream
+ * Products are exact (bfloat16 x bfloat16 fits float32) and sums are float32 on the matrix
+ * cores, in a fixed order: the same inputs give the same bits on every call.  The sums'
+ * order is not the oracle's, so results agree with the exact value within the float32
+ * forward error bound (D + H + 8) 2^-24 sum_h |w_h| sum_d |q_hd k_td|.
+ * Supported shape: heads = 16, head_dim = 128 (else DETK_ERR_UNSUPPORTED).  max_len must
+ * not exceed n_keys (DETK_ERR_INVALID_ARG), pointers must be non-NULL and aligned when
+ * B > 0 and max_len > 0.  Allocates nothing, never synchronizes; ordered on `stream`.
+ */
+int detk_indexer_scores(const void* q, const float* w, const void* keys, int32_t n_keys, const int32_t* lengths,
+                        int B, int heads, int head_dim, int32_t max_len, float* out, void* stream);
+
+/*
  * detk_status_string -- human-readable text for a status code, naming the condition
  * that produced it (static storage; "unknown detk status" for other values).  The pages'
  * backend replaces bare asserts with actionable errors (SGLang PR #31115, hardening

@@ -84,3 +84,18 @@ def test_workspace_size_refusal_is_size_max(lib):
     assert lib.detk_workspace_size(0, 4, 16, -5) == size_max
     assert lib.detk_workspace_size(0, 4, 4097, 100) == size_max
     assert lib.detk_workspace_size(-1, 4, 16, 100) == size_max
+
+
+def test_indexer_scores_argument_errors(lib):
+    """The indexer producer's shape and window checks come before any device call."""
+    vp = ctypes.c_void_p
+    fake = vp(256)  # never dereferenced: every call below is refused (or empty) on the host
+    f = lib.detk_indexer_scores
+    assert f(fake, fake, fake, 100, None, 4, 8, 128, 100, fake, None) == detk.DETK_ERR_UNSUPPORTED   # 8 heads
+    assert f(fake, fake, fake, 100, None, 4, 16, 64, 100, fake, None) == detk.DETK_ERR_UNSUPPORTED   # head dim 64
+    assert f(fake, fake, fake, 100, None, 4, 16, 128, 101, fake, None) == detk.DETK_ERR_INVALID_ARG  # past the keys
+    assert f(fake, fake, fake, 100, None, -1, 16, 128, 100, fake, None) == detk.DETK_ERR_INVALID_ARG
+    assert f(None, None, None, 100, None, 0, 16, 128, 100, None, None) == detk.DETK_OK              # empty batch
+    assert f(None, None, None, 100, None, 4, 16, 128, 0, None, None) == detk.DETK_OK                # empty windows
+    assert f(None, fake, fake, 100, None, 4, 16, 128, 100, fake, None) == detk.DETK_ERR_INVALID_ARG  # q NULL
+    assert f(vp(258), fake, fake, 100, None, 4, 16, 128, 100, fake, None) == detk.DETK_ERR_INVALID_ARG  # misaligned
