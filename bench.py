@@ -305,6 +305,79 @@ def empty_graph_floor(wl, calls: int = 20) -> float:
     return float(np.median([u / calls for u in event_us(g.replay, 1, torch.cuda.current_stream(dev))]))
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bfloat16 matrix peak
+
+
+def indexer_measure(steps: int, warmup: int) -> dict:
+    """The score producer upstream of the selection (detk_indexer_scores) on the chunked-
+    prefill shape: 8192 query rows over 16,384 keys, 16 heads of 128, causal windows.  Times
+    `steps` producer calls after `warmup` (HIP events on the call's stream) and the same
+    number of producer + selection pairs; checks 8 sampled rows' scores against the oracle
+    within its float32 bound and the selection of every row against the oracle's selection
+    over the GPU's scores, bit for bit."""
+    import torch
+    import oracle
+    from oracle import indexer as OI
+    import deterministic_exact_top_amd as detk
+    import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    inp = W.indexer_causal(Q=8192, ctx=16384)
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev)
+    w = torch.from_numpy(inp.w).to(dev)
+    kk = torch.from_numpy(inp.keys.view(np.int16)).to(dev)
+    ln = torch.from_numpy(inp.lengths).to(dev)
+    out = torch.zeros((inp.B, inp.max_len), dtype=torch.float32, device=dev)
+    oi = torch.empty((inp.B, inp.k), dtype=torch.int32, device=dev)
+    ov = torch.empty((inp.B, inp.k), dtype=torch.float32, device=dev)
+    ws = detk.new_workspace(inp.B, inp.k, inp.max_len, dev)
+    prod = lambda: detk.indexer_scores(q, w, kk, ln, inp.max_len, out=out, stream=stream)
+    pair = lambda: (prod(), detk.topk_ragged(out.view(-1), None, ln, inp.k, max_len=inp.max_len, out_idx=oi,
+                                             out_val=ov, workspace=ws, stream=stream))
+    for _ in range(warmup):
+        pair()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record(stream)
+    for _ in range(steps):
+        prod()
+    e[1].record(stream)
+    for _ in range(steps):
+        pair()
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    prod_us = e[0].elapsed_time(e[1]) * 1e3 / steps
+    pair_us = e[1].elapsed_time(e[2]) * 1e3 / steps
+    flops = 2.0 * inp.H * inp.D * inp.sum_n
+    tflops = flops / (prod_us * 1e-6) / 1e12
+    # parity
+    host = out.cpu().numpy()
+    rows = [0, 1, 1000, 4095, 4096, 6000, 8190, 8191]
+    sub = W.IndexerInputs(inp.name, inp.q[rows], inp.w[rows], inp.keys, inp.key_starts[rows], inp.lengths[rows],
+                          inp.max_len, inp.k)
+    exact = OI.scores(sub.q, sub.w, sub.keys, sub.lengths, sub.max_len)
+    bound = OI.error_bound(sub.q, sub.w, sub.keys, sub.lengths, sub.max_len)
+    within = all(bool(np.all(np.abs(host[b, :inp.lengths[b]].astype(np.float64) - exact[i, :inp.lengths[b]])
+                              <= bound[i, :inp.lengths[b]])) for i, b in enumerate(rows))
+    ri, rv = oracle.topk_ragged(host.reshape(-1), None, inp.lengths, inp.k, inp.max_len, B=inp.B,
+                                threads=cpu_threads())
+    sel_ok = bool(np.array_equal(oi.cpu().numpy(), ri)) and bool(np.array_equal(ov.cpu().numpy().view(np.uint32), rv))
+    bytes_ = inp.q.nbytes + inp.w.nbytes + inp.keys.nbytes + 4 * inp.sum_n
+    return {
+        "workload": "indexer_causal_8192x16384_h16_d128", "B": inp.B, "n_keys": inp.max_len, "heads": inp.H,
+        "head_dim": inp.D, "k": inp.k, "sum_n": inp.sum_n, "steps": steps, "warmup": warmup,
+        "producer_us": prod_us, "producer_plus_selection_us": pair_us,
+        "zero_fraction": float(np.mean(host[0, :inp.lengths[0]] == 0.0)),
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
+                     "note": "2 H D sum(n) flops per call (the [H x D] x [D x n] products; the ReLU and head "
+                             "sum are not counted), bfloat16 dense peak"},
+        "parity": {"ok": within and sel_ok, "scores_rows_checked": len(rows), "scores_within_bound": within,
+                   "selection_rows_checked": inp.B, "selection_bit_exact": sel_ok},
+    }
+
+
 DECODE = ("plateau_4x4096", "decode_ragged_64")
 
 
@@ -469,6 +542,11 @@ def main():
                     help="add the bandwidth a plain streaming read and a plain copy reach on this GPU")
     ap.add_argument("--graph", action="store_true", help="add the per-call time with the calls replayed from a HIP graph")
     ap.add_argument("--floor", action="store_true", help="add the per-call time of the same call with every row empty")
+    ap.add_argument("--force-exact", action="store_true",
+                    help="time the exact radix path every row takes when the sampled pivot misses (the "
+                         "library's test switch; the worst case of a call)")
+    ap.add_argument("--no-indexer", action="store_true",
+                    help="skip the indexer-score producer (matrix cores) measured upstream of the selection")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step latency of the small-batch workloads (graph replay)")
     args = ap.parse_args()
@@ -482,6 +560,9 @@ def main():
         return
 
     import workloads as W
+    if args.force_exact:
+        import deterministic_exact_top_amd as detk
+        detk.debug_set(detk.DETK_DEBUG_FAST, 0)
     log("generating %s" % args.workload)
     wl = W.full(args.workload)
     if args.dtype != "f32":
@@ -506,6 +587,7 @@ def main():
         "config": {
             "workload": wl.name, "B": wl.B, "max_len": wl.max_len, "k": wl.k, "sum_n": wl.sum_n,
             "input_copies_rotated": m["rotate"], "parallelism": "none (1 GPU)",
+            "path": "exact radix path forced on every row (worst case)" if args.force_exact else "default",
             "index_transform": args.index_transform if args.index_transform == "none" else
             "%s%s" % (args.index_transform, " (page size %d)" % args.page_size if args.index_transform == "page_table" else ""),
         },
@@ -530,6 +612,10 @@ def main():
         ok_all = m["parity"]["ok"] and m2["parity"]["ok"]
     else:
         ok_all = m["parity"]["ok"]
+    if not args.no_indexer and args.dtype == "f32" and args.index_transform == "none":
+        log("timing the indexer-score producer")
+        result["indexer"] = indexer_measure(max(args.steps, 20), max(args.warmup, 5))
+        ok_all = ok_all and result["indexer"]["parity"]["ok"]
     if not args.no_decode and args.dtype == "f32" and args.index_transform == "none":
         log("timing decode-step latency")
         result["decode_latency"] = decode_latency()

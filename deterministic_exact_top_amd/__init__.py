@@ -51,10 +51,16 @@ def library_path() -> str:
 
 
 def load_library():
-    """Load libdetk.so (raises if it has not been built)."""
+    """Load libdetk.so (raises if it has not been built).
+
+    torch is imported first: its wheel carries its own HIP runtime under the soname the
+    library links against, so whichever is loaded first serves both.  Loaded after the
+    library, torch would bring a second runtime, and calls given torch's streams would be
+    lost in the library's runtime without an error."""
     global _lib
     if _lib is not None:
         return _lib
+    import torch  # noqa: F401  (the HIP runtime the library must share)
     path = library_path()
     if not os.path.exists(path):
         raise RuntimeError("libdetk.so is missing at %s; build it with "
