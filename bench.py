@@ -56,11 +56,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+SELECTION_SOURCES = ("detk_api.hip", "topk_device.hpp", "kernels.hpp")
+INDEXER_SOURCES = ("indexer.hip", "indexer.hpp")
+
+
+def kernel_source_sha(names=SELECTION_SOURCES) -> str:
     """Hash of the kernel sources with comments and whitespace taken out, so that a
     comment edit does not mark counters taken on the same code as stale."""
     h = hashlib.sha256()
-    for name in ("detk_api.hip", "topk_device.hpp", "kernels.hpp"):
+    for name in names:
         with open(os.path.join(ROOT, "deterministic_exact_top_amd", "csrc", name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -203,13 +207,13 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     }
 
 
-def traffic_for(workload, algo_bytes):
+def traffic_for(workload, algo_bytes, sources=SELECTION_SOURCES):
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -369,10 +373,12 @@ def indexer_measure(steps: int, warmup: int) -> dict:
         "producer_us": prod_us, "producer_plus_selection_us": pair_us,
         "zero_fraction": float(np.mean(host[0, :inp.lengths[0]] == 0.0)),
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic_for("indexer_causal_8192x16384_h16_d128", bytes_, INDEXER_SOURCES),
                      "algorithmic_flops": flops, "algorithmic_bytes": bytes_,
                      "note": "2 H D sum(n) flops per call (the [H x D] x [D x n] products; the ReLU and head "
-                             "sum are not counted), bfloat16 dense peak"},
+                             "sum are not counted), bfloat16 dense peak; traffic: HBM bytes per launch from "
+                             "FETCH_SIZE and WRITE_SIZE"},
         "parity": {"ok": within and sel_ok, "scores_rows_checked": len(rows), "scores_within_bound": within,
                    "selection_rows_checked": inp.B, "selection_bit_exact": sel_ok},
     }
