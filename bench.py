@@ -505,7 +505,8 @@ def measure(wl, steps, warmup, rotate, transform_kind="none", page_size=64) -> d
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic_for(wl.name, algo),
+            # (counters are stored for the plain call: none for a fused index transform)
+            "traffic": traffic_for(wl.name, algo) if transform_kind == "none" else None,
             "algorithmic_bytes_per_launch": algo,
             "avg_launch_us": per_round_us[0],
             "min_launch_us": float(np.min(launch_ms)) * 1e3,

@@ -12,15 +12,17 @@
 //
 // Work split: a 256-thread workgroup (4 waves) takes 16 query rows (4 per wave) and one
 // chunk of kChunk keys, walked in blocks of kKeyBlock keys.  A block's keys are staged in
-// LDS (padded rows, double-buffered: the next block's loads are in flight during this
-// block's MFMAs) and shared by the 16 queries; each wave keeps its queries' q fragments in
+// LDS (padded rows, double-buffered; the loads run two blocks ahead, in registers, so each
+// block's HBM/L2 latency hides behind two blocks of MFMAs) and shared by the 16 queries; each wave keeps its queries' q fragments in
 // registers for the whole chunk.  Per block and wave: 4 queries x 4 key groups of 16 x
 // D / 32 steps MFMAs.  MFMA operand layout (16x16x32): lane l holds A[l % 16][8 (l / 16) + j]
 // and B[8 (l / 16) + j][l % 16] (j < 8), and C[4 (l / 16) + i][l % 16] (i < 4); here
 // A = the query's heads x head dims, B = head dims x 16 keys, so C holds four heads of one
-// key per lane.  The epilogue sums a lane's four heads (w_h * max(0, c_h)), then the four
-// lane groups by two fixed exchanges, so every lane holds the same bits whatever the
-// schedule.
+// key per lane.  The epilogue sums a lane's four heads (w_h * max(0, c_h)) for each of its
+// query's four key groups, then reduces over the four 16-lane rows and transposes at once
+// with three row swaps (v_permlane16_swap, v_permlane32_swap: no LDS traffic), leaving in
+// row r the totals of key group r -- the 64 consecutive keys of the block, one per lane, in
+// a fixed order of additions, so the bits do not depend on the schedule.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,12 +40,22 @@ constexpr int kQPerWave = 4;
 constexpr int kWaves = 4;
 constexpr int kQPerGroup = kQPerWave * kWaves;  // query rows per workgroup
 constexpr int kKeyBlock = 64;              // keys per staged block (4 groups of 16)
-constexpr int kRowBytes = kD * 2 + 16;     // LDS bytes per staged key row (16 bytes of padding)
+constexpr int kGroups = kKeyBlock / 16;
+// LDS bytes per staged key row: 32 bytes of padding keep the B-fragment reads free of bank
+// conflicts (16 bytes left one 4-cycle conflict per read; none measured with 32)
+constexpr int kRowBytes = kD * 2 + 32;
 constexpr int kChunksPerThread = kKeyBlock * kD * 2 / 16 / 256;  // 16-byte loads per thread per block
 static_assert(kH == 16, "one 16-row MFMA tile of heads");
 static_assert(kD % 32 == 0 && kChunksPerThread * 256 * 16 == kKeyBlock * kD * 2, "whole 16-byte loads");
 
 constexpr int32_t kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9-family data format
+
+// max(0, x) on the bits: negative patterns become +0.0 (finite inputs assumed: a NaN logit
+// has no defined place in the score).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 
 __device__ __forceinline__ int32_t row_len(const IxParams& p, int64_t b) {
     if (b >= p.B) return 0;
@@ -88,73 +100,90 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
     // n_keys read as zero, so a block never reads outside the keys).
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(p.keys), (short)0, (int)min<int64_t>((int64_t)p.n_keys * kD * 2, 0x7FFFFFFF), kBufferWord3);
-    uint4 kr[kChunksPerThread];
-    auto load_block = [&](int32_t kb) {
+    auto load_block = [&](int32_t kb, uint4 (&dst)[kChunksPerThread]) {
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {
             const int c = tid + 256 * i;  // 16-byte chunk: row c / (kD / 8), column c % (kD / 8)
             const int row = c / (kD / 8), col = c % (kD / 8);
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (row * kD + col * 8) * 2, kb * kD * 2, 0);
-            kr[i] = make_uint4(v[0], v[1], v[2], v[3]);
+            dst[i] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
-    auto stage_block = [&](int buf) {
+    auto stage_block = [&](int buf, const uint4 (&src)[kChunksPerThread]) {
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {
             const int c = tid + 256 * i;
             const int row = c / (kD / 8), col = c % (kD / 8);
-            *reinterpret_cast<uint4*>(stage[buf] + row * kRowBytes + col * 16) = kr[i];
+            *reinterpret_cast<uint4*>(stage[buf] + row * kRowBytes + col * 16) = src[i];
         }
     };
 
-    load_block(k_begin);
-    stage_block(0);
-    __syncthreads();
-    int it = 0;
-    for (int32_t kb = k_begin; kb < k_end; kb += kKeyBlock, ++it) {
-        const int buf = it & 1;
-        const bool more = kb + kKeyBlock < k_end;  // uniform
-        if (more) load_block(kb + kKeyBlock);      // (in flight during the MFMAs)
+    // One block: MFMAs over the staged keys of `buf`, the epilogue, then the next block's
+    // keys (in `next`, loaded a block earlier) staged into the other buffer.  `ahead`
+    // receives the keys of the block after that, loaded while this block computes.
+    auto block = [&](int32_t kb, int buf, uint4 (&next)[kChunksPerThread], uint4 (&ahead)[kChunksPerThread]) {
+        const bool more = kb + kKeyBlock < k_end;        // uniform
+        const bool more2 = kb + 2 * kKeyBlock < k_end;   // uniform
+        if (more2) load_block(kb + 2 * kKeyBlock, ahead);  // (in flight during two blocks)
 
-        f32x4 acc[kQPerWave][4];
+        f32x4 acc[kQPerWave][kGroups];
 #pragma unroll
         for (int j = 0; j < kQPerWave; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int g = 0; g < kGroups; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < kGroups; ++g) {
                 const bf16x8 bk = *reinterpret_cast<const bf16x8*>(stage[buf] + (16 * g + (lane & 15)) * kRowBytes +
-                                                                   (32 * s + 8 * (lane >> 4)) * 2);
+                                                                   (4 * s + (lane >> 4)) * 16);
 #pragma unroll
                 for (int j = 0; j < kQPerWave; ++j)
                     acc[j][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][s], bk, acc[j][g], 0, 0, 0);
             }
         }
 
-        // Epilogue: lane l holds heads 4 (l / 16) .. + 3 of key 16 g + l % 16.
+        // Epilogue: lane l holds heads 4 (l / 16) .. + 3 of key 16 g + l % 16; each quarter of
+        // 64 keys (groups 4 h .. 4 h + 3) is reduced and stored on its own.
 #pragma unroll
-        for (int j = 0; j < kQPerWave; ++j) {
-            float r[4];
+        for (int j = 0; j < kQPerWave; ++j)
+#pragma unroll
+        for (int h = 0; h < kGroups / 4; ++h) {
+            uint32_t part[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                float part = wv[j][0] * fmaxf(acc[j][g][0], 0.f);
-                part += wv[j][1] * fmaxf(acc[j][g][1], 0.f);
-                part += wv[j][2] * fmaxf(acc[j][g][2], 0.f);
-                part += wv[j][3] * fmaxf(acc[j][g][3], 0.f);
-                part += __shfl_xor(part, 16);
-                part += __shfl_xor(part, 32);
-                r[g] = part;
+                float x = wv[j][0] * relu(acc[j][4 * h + g][0]);
+                x += wv[j][1] * relu(acc[j][4 * h + g][1]);
+                x += wv[j][2] * relu(acc[j][4 * h + g][2]);
+                x += wv[j][3] * relu(acc[j][4 * h + g][3]);
+                part[g] = as_u(x);
             }
-            // lane l stores key kb + l: group l / 16, column l % 16 (one 256-byte store)
-            const int lg = lane >> 4;
-            const float v = lg == 0 ? r[0] : lg == 1 ? r[1] : lg == 2 ? r[2] : r[3];
-            const int32_t t = kb + lane;
+            // rows (0, 1) and (2, 3) exchange: even rows sum groups 0 and 2 over the pair,
+            // odd rows groups 1 and 3; then rows (0, 1) and (2, 3) exchange halves: row r
+            // holds the total of group r.
+            const auto x01 = __builtin_amdgcn_permlane16_swap(part[0], part[1], false, false);
+            const auto x23 = __builtin_amdgcn_permlane16_swap(part[2], part[3], false, false);
+            const float s01 = as_f(x01[0]) + as_f(x01[1]);
+            const float s23 = as_f(x23[0]) + as_f(x23[1]);
+            const auto y = __builtin_amdgcn_permlane32_swap(as_u(s01), as_u(s23), false, false);
+            const float v = as_f(y[0]) + as_f(y[1]);
+            // lane l stores key kb + 64 h + l: group l / 16, column l % 16 (one 256-byte store)
+            const int32_t t = kb + 64 * h + lane;
             if (t < nq[j]) p.out[qi[j] * p.max_len + t] = v;
         }
-        if (more) stage_block(buf ^ 1);  // (nobody reads that buffer until the barrier)
+        if (more) stage_block(buf ^ 1, next);  // (nobody reads that buffer until the barrier)
         __syncthreads();
+    };
+
+    uint4 kA[kChunksPerThread], kB[kChunksPerThread];
+    load_block(k_begin, kA);
+    stage_block(0, kA);
+    if (k_begin + kKeyBlock < k_end) load_block(k_begin + kKeyBlock, kA);
+    __syncthreads();
+    // (two blocks per turn, so the two register sets keep fixed names)
+    for (int32_t kb = k_begin; kb < k_end; kb += 2 * kKeyBlock) {
+        block(kb, 0, kA, kB);
+        if (kb + kKeyBlock < k_end) block(kb + kKeyBlock, 1, kB, kA);
     }
 }
 
