@@ -521,16 +521,6 @@ __device__ __forceinline__ uint32_t wave_select_digit(const uint32_t* hist, uint
     return __builtin_amdgcn_readlane(d, src);
 }
 
-// Orders one wave's LDS accesses: its earlier LDS writes are seen by its later LDS reads,
-// in any of its lanes.  LDS serves a wave's instructions in issue order, so this only has
-// to keep the compiler from moving accesses across it.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    asm volatile("" ::: "memory");
-}
-
 // A plain LDS array of composites, with PairList's accessors.
 struct U64List {
     uint64_t* a;
@@ -538,21 +528,89 @@ struct U64List {
     __device__ __forceinline__ void set_composite(uint32_t i, uint64_t c) const { a[i] = c; }
 };
 
+// x of lane ^ S: S = 1, 2, 8 one DPP move (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_ror:8), S = 4 two (row_half_mirror gives lane ^ 7, then quad_perm [3,2,1,0] lane ^ 3),
+// S = 16, 32 a row swap (v_permlane16_swap / v_permlane32_swap of x with itself: each lane's
+// partner value lands in one of the two results).  No LDS traffic.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+    if constexpr (S == 1) return dpp<0xB1, 0xF, false>(x, x);
+    else if constexpr (S == 2) return dpp<0x4E, 0xF, false>(x, x);
+    else if constexpr (S == 4) {
+        const uint32_t m = dpp<0x141, 0xF, false>(x, x);
+        return dpp<0x1B, 0xF, false>(m, m);
+    } else if constexpr (S == 8) return dpp<0x128, 0xF, false>(x, x);
+    else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(S == 32, "strides within a wave");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+template <int S>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x, int lane) {
+    return ((uint64_t)lane_xor<S>((uint32_t)(x >> 32), lane) << 32) | lane_xor<S>((uint32_t)x, lane);
+}
+
+// Bitonic compare-exchange stages on registers: a wave holds an aligned block of 128
+// elements, lane l elements e0 = block + l (v0) and e0 + 64 (v1).  A pair (lo, lo + s) of
+// merge `size` keeps the larger composite at lo when lo & size == 0 (descending), else the
+// smaller.  Stride 64 pairs a lane's own two elements; smaller strides pair lanes l, l ^ s.
+template <int S>
+__device__ __forceinline__ void reg_stage(uint64_t& v0, uint64_t& v1, int e0, int lane, int size) {
+    const uint64_t p0 = lane_xor64<S>(v0, lane), p1 = lane_xor64<S>(v1, lane);
+    const bool lo = (lane & S) == 0;
+    const bool m0 = ((e0 & size) == 0) == lo;  // this lane keeps the larger of the pair
+    const bool m1 = (((e0 + 64) & size) == 0) == lo;
+    // (one compare each: composites are unique, and equal pairs are padding zeros)
+    v0 = (v0 > p0) == m0 ? v0 : p0;
+    v1 = (v1 > p1) == m1 ? v1 : p1;
+}
+__device__ __forceinline__ void reg_merge(uint64_t& v0, uint64_t& v1, int e0, int lane, int size) {
+    if (size > 64) {  // stride 64: within the lane
+        const bool m = (e0 & size) == 0;
+        const uint64_t hi = max(v0, v1), lo = min(v0, v1);
+        v0 = m ? hi : lo;
+        v1 = m ? lo : hi;
+    }
+    if (size > 32) reg_stage<32>(v0, v1, e0, lane, size);
+    if (size > 16) reg_stage<16>(v0, v1, e0, lane, size);
+    if (size > 8) reg_stage<8>(v0, v1, e0, lane, size);
+    if (size > 4) reg_stage<4>(v0, v1, e0, lane, size);
+    if (size > 2) reg_stage<2>(v0, v1, e0, lane, size);
+    reg_stage<1>(v0, v1, e0, lane, size);
+}
+
 // Descending bitonic sort of the composites of A[0..count) (count <= KMAX), padded to a
 // power of two P with composite 0, which no real element has (~pos != 0).
-// Pairs of a stage with stride s lie in aligned blocks of 2s elements, and thread i takes
-// the pair starting at 2i - (i mod s).  For s <= 64 the 64 threads of a wave (i in an
-// aligned run of 64, in every turn of the NT-strided loop) therefore cover one aligned
-// block of 128 elements that no other wave touches: such stages need only wave_lds_sync,
-// and a workgroup barrier is taken only where the next stage crosses waves.
+// Every stage of stride <= 64 runs in registers (reg_merge): each wave takes aligned
+// 128-element blocks, and the merges of sizes 2 .. 128 run in one pass over a block (loaded
+// and stored once).  A merge of size >= 256 first takes its stages of stride >= 128 through
+// LDS (thread i takes the pair starting at 2i - (i mod stride), a workgroup barrier after
+// each), then one register pass for strides 64 .. 1.  For 2048 entries: 10 LDS stages
+// instead of 66.  Elements past P are never paired with ones below it (merges stay within
+// aligned blocks of their size <= P), so a block's lanes past P only hold zeros.
 template <int NT, class List>
 __device__ __forceinline__ void bitonic_desc(const List& A, int count) {
-    static_assert(NT % 64 == 0, "whole waves");
+    static_assert(NT % 64 == 0 && NT >= 128, "whole waves");
     const int tid = opaque_tid();
+    const int lane = tid & 63, wave = tid >> 6;
     int P = 1;
     while (P < count) P <<= 1;
     for (int i = count + tid; i < P; i += NT) A.set_composite(i, 0);
     __syncthreads();
+    auto reg_pass = [&](int size_lo, int size_hi) {
+        for (int blk = wave; blk * 128 < P; blk += NT / 64) {
+            const int e0 = blk * 128 + lane;
+            uint64_t v0 = e0 < P ? A.composite(e0) : 0ull;
+            uint64_t v1 = e0 + 64 < P ? A.composite(e0 + 64) : 0ull;
+            for (int size = size_lo; size <= size_hi; size <<= 1) reg_merge(v0, v1, e0, lane, size);
+            if (e0 < P) A.set_composite(e0, v0);
+            if (e0 + 64 < P) A.set_composite(e0 + 64, v1);
+        }
+    };
     auto stage = [&](int size, int stride) {
         for (int i = tid; i < (P >> 1); i += NT) {
             const int lo = 2 * i - (i & (stride - 1));
@@ -565,18 +623,16 @@ __device__ __forceinline__ void bitonic_desc(const List& A, int count) {
             }
         }
     };
-    for (int size = 2; size <= P; size <<= 1) {
-        int stride = size >> 1;
-        for (; stride >= 128; stride >>= 1) {
+    reg_pass(2, P < 128 ? P : 128);
+    for (int size = 256; size <= P; size <<= 1) {
+        __syncthreads();
+        for (int stride = size >> 1; stride >= 128; stride >>= 1) {
             stage(size, stride);
             __syncthreads();
         }
-        for (; stride > 0; stride >>= 1) {
-            stage(size, stride);
-            wave_lds_sync();
-        }
-        if (size >= 128 || size == P) __syncthreads();  // the next stage (stride = size) crosses waves, or done
+        reg_pass(size, size);
     }
+    __syncthreads();
 }
 
 // The same on a plain array of composites.
