@@ -478,6 +478,8 @@ int detk_indexer_scores(const void* q, const float* w, const void* keys, int32_t
     if (B < 0 || max_len < 0 || n_keys < 0) return DETK_ERR_INVALID_ARG;
     if (heads != detk_ix::kHeads || head_dim != detk_ix::kHeadDim) return DETK_ERR_UNSUPPORTED;
     if (max_len > n_keys) return DETK_ERR_INVALID_ARG;  // every window lies inside the keys
+    // the key rows are read through one buffer resource: at most 2^31 - 1 bytes of keys
+    if ((int64_t)n_keys * detk_ix::kHeadDim * 2 > 0x7FFFFFFF) return DETK_ERR_UNSUPPORTED;
     if (B == 0 || max_len == 0) return DETK_OK;
     if (!q || !w || !keys || !out) return DETK_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(keys)) & 15u)

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
     // Key blocks: 16-byte loads through a buffer resource over the key rows (rows past
     // n_keys read as zero, so a block never reads outside the keys).
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.keys), (short)0, (int)min<int64_t>((int64_t)p.n_keys * kD * 2, 0x7FFFFFFF), kBufferWord3);
+        const_cast<uint16_t*>(p.keys), (short)0, p.n_keys * kD * 2, kBufferWord3);  // (host: < 2^31 bytes)
     auto load_block = [&](int32_t kb, uint4 (&dst)[kChunksPerThread]) {
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {

@@ -227,7 +227,8 @@ int detk_topk_ragged_noalloc(const float* scores, const int32_t* row_starts, con
  * order is not the oracle's, so results agree with the exact value within the float32
  * forward error bound (D + H + 8) 2^-24 sum_h |w_h| sum_d |q_hd k_td|.
  * q, w and keys must be finite (a NaN or infinite operand leaves the scores it reaches
- * unspecified).  Supported shape: heads = 16, head_dim = 128 (else DETK_ERR_UNSUPPORTED).  max_len must
+ * unspecified).  Supported shape: heads = 16, head_dim = 128, and at most 8,388,607 key
+ * rows (2^31 - 1 bytes of keys) (else DETK_ERR_UNSUPPORTED).  max_len must
  * not exceed n_keys (DETK_ERR_INVALID_ARG), pointers must be non-NULL and aligned when
  * B > 0 and max_len > 0.  Allocates nothing, never synchronizes; ordered on `stream`.
  */

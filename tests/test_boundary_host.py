@@ -99,3 +99,5 @@ def test_indexer_scores_argument_errors(lib):
     assert f(None, None, None, 100, None, 4, 16, 128, 0, None, None) == detk.DETK_OK                # empty windows
     assert f(None, fake, fake, 100, None, 4, 16, 128, 100, fake, None) == detk.DETK_ERR_INVALID_ARG  # q NULL
     assert f(vp(258), fake, fake, 100, None, 4, 16, 128, 100, fake, None) == detk.DETK_ERR_INVALID_ARG  # misaligned
+    big = (2 ** 31) // 256  # 8,388,608 key rows: 2^31 bytes, one past the envelope
+    assert f(fake, fake, fake, big, None, 4, 16, 128, 100, fake, None) == detk.DETK_ERR_UNSUPPORTED
