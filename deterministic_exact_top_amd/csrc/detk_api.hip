@@ -498,9 +498,10 @@ int detk_indexer_scores(const void* q, const float* w, const void* keys, int32_t
     p.B = B;
     p.max_len = max_len;
     p.n_keys = n_keys;
-    p.chunks = (max_len + detk_ix::kChunk - 1) / detk_ix::kChunk;
+    p.chunk = 0;   // (chosen by launch_indexer)
+    p.chunks = 0;
     p.out = out;
-    const hipError_t e = detk_ix::launch_indexer(p, reinterpret_cast<hipStream_t>(stream));
+    const hipError_t e = detk_ix::launch_indexer(p, dev.cus, reinterpret_cast<hipStream_t>(stream));
     if (e == hipErrorInvalidValue) return DETK_ERR_UNSUPPORTED;  // grid beyond 2^31 - 1 workgroups
     return e == hipSuccess ? DETK_OK : DETK_ERR_HIP;
 }

@@ -11,7 +11,7 @@
 // only the [B, max_len] float32 scores are written.
 //
 // Work split: a 256-thread workgroup (4 waves) takes 16 query rows (4 per wave) and one
-// chunk of kChunk keys, walked in blocks of kKeyBlock keys.  A block's keys are staged in
+// chunk of keys (1024 .. 16384, chosen per launch), walked in blocks of kKeyBlock keys.  A block's keys are staged in
 // LDS (padded rows, double-buffered; the loads run two blocks ahead, in registers, so each
 // block's HBM/L2 latency hides behind two blocks of MFMAs) and shared by the 16 queries; each wave keeps its queries' q fragments in
 // registers for the whole chunk.  Per block and wave: 4 queries x 4 key groups of 16 x
@@ -73,8 +73,8 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
     // The workgroup's key range: its chunk, cut at the longest window of its rows.
     int32_t nmax = 0;
     for (int j = 0; j < kQPerGroup; ++j) nmax = max(nmax, row_len(p, q0 + j));
-    const int32_t k_begin = chunk * kChunk;
-    const int32_t k_end = min(k_begin + kChunk, nmax);
+    const int32_t k_begin = chunk * p.chunk;
+    const int32_t k_end = min(k_begin + p.chunk, nmax);
     if (k_begin >= k_end) return;  // uniform: no row of the group reaches this chunk
 
     // This wave's rows: q fragments (rows past the batch are zero) and head weights.
@@ -187,8 +187,14 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
     }
 }
 
-hipError_t launch_indexer(const IxParams& p, hipStream_t stream) {
+hipError_t launch_indexer(IxParams p, int cus, hipStream_t stream) {
     const int64_t groups = ((int64_t)p.B + kQPerGroup - 1) / kQPerGroup;
+    // Larger chunks measured faster on the 8192 x 16384 prefill shape (1024: 467 us, 2048:
+    // 436, 4096: 423-439, 8192: 423-430, 16384: 410-414), as long as the grid fills the GPU.
+    int32_t chunk = kMaxChunk;
+    while (chunk > kMinChunk && groups * (((int64_t)p.max_len + chunk - 1) / chunk) < 2 * (int64_t)cus) chunk >>= 1;
+    p.chunk = chunk;
+    p.chunks = (int32_t)(((int64_t)p.max_len + chunk - 1) / chunk);
     const int64_t grid = groups * p.chunks;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
