@@ -63,10 +63,14 @@ def _with_lengths(inp, lengths, name):
 
 
 CASES = {
-    # 40 rows (not a multiple of 16) over 3000 keys (two chunks of 2048, a ragged last block)
+    # 40 rows (not a multiple of 16) over 3000 keys (at this batch size the launch takes
+    # 1024-key chunks: three per row, a ragged last block)
     "causal_40x3000": lambda: W.indexer_causal(Q=40, ctx=3000, name="ix_a"),
     "causal_5x70": lambda: W.indexer_causal(Q=5, ctx=70, name="ix_b"),
-    # windows at and around block (64) and chunk (2048) edges, empty and clamped rows
+    # one 16-row group over 20,000 keys: the launch takes 1024-key chunks, 20 per row
+    "causal_8x20000": lambda: W.indexer_causal(Q=8, ctx=20000, name="ix_g"),
+    # windows at and around block (64) and chunk (1024 here; 2048 and 4096 for larger batches)
+    # edges, empty and clamped rows
     "edges": lambda: _with_lengths(W.indexer_causal(Q=20, ctx=4200, name="ix_c"),
                                    [0, -5, 1, 63, 64, 65, 2047, 2048, 2049, 4095, 4096, 4097, 4199, 4200, 9999,
                                     128, 130, 2, 3000, 4100], "ix_edges"),
@@ -158,3 +162,41 @@ def test_refusals(dev):
     with pytest.raises(detk.DetkError) as e:
         detk.indexer_scores(qm, w, k, ln)
     assert e.value.status == detk.DETK_ERR_INVALID_ARG
+
+
+def test_graph_replay_of_producer_and_selection(dev):
+    """Both calls captured in one HIP graph (torch.cuda.graph), replayed on new inputs copied
+    into the captured buffers; every replay must equal an eager run on the same inputs."""
+    import torch
+    mk = lambda i: W.indexer_causal(Q=48, ctx=2600, k=512, name="ix_graph_%d" % i)
+    inps = [mk(i) for i in range(3)]
+    q, w, kk, ln = _dev(inps[0], dev)
+    scores = torch.zeros((inps[0].B, inps[0].max_len), dtype=torch.float32, device=dev)
+    oi = torch.empty((inps[0].B, 512), dtype=torch.int32, device=dev)
+    ov = torch.empty((inps[0].B, 512), dtype=torch.float32, device=dev)
+    ws = detk.new_workspace(inps[0].B, 512, inps[0].max_len, dev)
+    def pair():
+        detk.indexer_scores(q, w, kk, ln, inps[0].max_len, out=scores)
+        detk.topk_ragged(scores.view(-1), None, ln, 512, max_len=inps[0].max_len, out_idx=oi, out_val=ov,
+                         workspace=ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pair()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pair()
+    torch.cuda.synchronize()
+    for inp in inps:
+        q2, w2, k2, _ = _dev(inp, dev)
+        q.copy_(q2); w.copy_(w2); kk.copy_(k2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (scores.cpu().numpy().copy(), oi.cpu().numpy().copy(), ov.cpu().numpy().copy())
+        pair()  # eager, same buffers
+        torch.cuda.synchronize()
+        assert got[0].view(np.uint32).tobytes() == scores.cpu().numpy().view(np.uint32).tobytes()
+        assert np.array_equal(got[1], oi.cpu().numpy())
+        assert got[2].view(np.uint32).tobytes() == ov.cpu().numpy().view(np.uint32).tobytes()
