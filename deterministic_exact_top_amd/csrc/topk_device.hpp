@@ -352,13 +352,20 @@ struct FastSmem {
                                               // candidate has been read into registers);
                                               // while choosing P, its first 2 KiB hold two
                                               // sample-digit histograms
+        struct {
+            uint64_t past_S[SCAP + rank_pad<true>()];
+            uint64_t other[kBucketLimit];  // a plateau bucket's composites of other keys
+            uint32_t bits[BWORDS];         //   and the positions holding its key
+        } plateau;
     };
-    uint32_t ctl[16];             // control words, kCtl* below
+    static constexpr int CTL_WORDS = 24;
+    uint32_t ctl[CTL_WORDS];      // control words, kCtl* below
     uint32_t wsum[32];
     uint32_t bitmap[BWORDS];      // positions with key == P
     uint32_t bucket[kBuckets / 2 + 2];  // 16-bit bucket counters, cursors and ends, two per
                                         // word; then a zero (the end above the top bucket)
     static_assert((CCAP * 4) % 256 == 0, "candidate arrays on 256-byte boundaries");
+    static_assert(sizeof(plateau) <= sizeof(cand), "the plateau arrays fit past S");
     static_assert(sizeof(uint64_t) * SCAP >= sizeof(uint32_t) * 2 * kRadix, "S holds the sample histograms");
 };
 
@@ -752,6 +759,12 @@ enum : int {
     kCtlPool = 15,      // one workgroup: slots claimed in the candidate pool
     kCtlBinNotMin = 0,  // pivot: max of ~key over the samples in the selected 16-bit bin
     kCtlBinMax = 14,    // pivot: max of key over the same samples
+    // one workgroup (FastSmem only): a plateau bucket
+    kCtlPFirst = 16,    // [16..17] as one 64-bit word: max of (~position << 32 | key) over the
+                        //   long bucket, i.e. its first element in position order and that key
+    kCtlLongN = 18,     // buckets longer than the ranking limit
+    kCtlPOther = 19,    // the bucket's composites of other keys
+    kCtlPCount = 20,    // (its keys above the plateau key) << 16 | (those equal to it)
 };
 
 // Real samples among a tile's nt elements (uniform): slot i * EPT / kSamplesPerLane of
@@ -967,8 +980,9 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // barrier behind); otherwise the bucket array is zero (a barrier behind) and counted here.
 // Every candidate is read into registers before the first barrier in here, so S may
 // overlay the memory src reads.
-// ctl[kCtlBt..kCtlMaxBucket] are zero on entry (kCtlMaxBucket becomes a flag: some bucket
-// is longer than the limit).
+// ctl[kCtlBt..kCtlMaxBucket] are zero on entry (kCtlMaxBucket becomes one more than the
+// highest bucket longer than the limit, 0 when there is none); so are ctl[kCtlPFirst..
+// kCtlPCount] when PBW > 0.  Only kept buckets (at or above the threshold) count as long.
 // scattered() runs once the kept composites are in S, past the last point of returning
 // false.
 // LIMITED: returns false, having emitted nothing, when more than SCAP candidates are
@@ -980,12 +994,29 @@ __device__ __forceinline__ void bucket_count(uint32_t* bucket, uint32_t bk) {
 // SCAP + rank_pad<LIMITED>() entries (those past the kept ones are cleared here).
 // sort_long (LIMITED only): when a bucket is too long but at most SORT_MAX candidates are
 // kept, sort them instead of returning false (a row output whole keeps at most KMAX).
-template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, class Src, class Valid, class Live, class Map,
-          class Emit, class Scattered>
+// PBW > 0 (LIMITED only; positions are a tile's, below 32 PBW): a plateau bucket.  When
+// exactly one kept bucket is longer than the limit, its key X is that of its first element
+// in position order, and at most kBucketLimit of its elements have another key, those go
+// to pl->other and are ranked among themselves (an element below X also passes all of
+// X's); the elements of key X are not ranked: they take slots pl->base .. in position
+// order, the caller emitting them from the bitmap pl->bits (PBW words) with pl->need of
+// them inside the output.  Every key gives the same output; X a majority key makes the
+// bucket cheap.  pl->on says whether this happened.
+struct PlateauBucket {
+    uint64_t* other;  // kBucketLimit composites
+    uint32_t* bits;   // position bitmap
+    bool on;
+    uint32_t key, base, need;
+};
+template <int NT, int SCAP, int CPT, bool LIMITED, bool COUNTED, int PBW, class Src, class Valid, class Live,
+          class Map, class Emit, class Scattered>
 __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint32_t* wsum, uint32_t* ctl, Src&& src,
                                             Valid&& valid, Live&& live, uint32_t c_gt, uint32_t m, bool ties,
                                             const Map& bucket_of, const IndexOut& xo, Emit&& emit,
-                                            Scattered&& scattered, bool sort_long = false) {
+                                            Scattered&& scattered, bool sort_long = false,
+                                            PlateauBucket* pl = nullptr) {
+    static_assert(PBW == 0 || LIMITED, "plateau buckets only where positions are a tile's");
+    if constexpr (PBW > 0) pl->on = false;
     constexpr int BPT = kBuckets / NT;  // buckets per thread in the scan
     static_assert(BPT % 2 == 0, "threads own whole words of bucket counters");
     const int tid = opaque_tid();
@@ -1052,7 +1083,17 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
         uint32_t ov = 0;
 #pragma unroll
         for (int i = 0; i < WPT; ++i) ov |= cw[i] + BIAS;
-        if (ov & 0x80008000u) ctl[kCtlMaxBucket] = 1u;  // (any lane; all store the same)
+        if (ov & 0x80008000u) {  // rare: which buckets (word w0 + i: bit 15 bucket 2 (w0 + i), bit 31 the next)
+            uint32_t top = 0, nlong = 0;
+#pragma unroll
+            for (int i = 0; i < WPT; ++i) {
+                const uint32_t x = cw[i] + BIAS;
+                if (x & 0x8000u) top = max(top, 2u * (uint32_t)(w0 + i) + 1u), ++nlong;
+                if (x & 0x80000000u) top = max(top, 2u * (uint32_t)(w0 + i) + 2u), ++nlong;
+            }
+            __hip_atomic_fetch_max(&ctl[kCtlMaxBucket], top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if constexpr (PBW > 0) lds_add(&ctl[kCtlLongN], nlong);
+        }
     }
     uint32_t total;
     const uint32_t run0 = block_excl_scan<NT>(tsum, wsum + 16, &total);
@@ -1083,11 +1124,16 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     __syncthreads();
     const uint32_t bt = ties ? 0u : ctl[kCtlBt];
     const uint32_t kept = ties ? c_gt : ctl[kCtlKept];
-    const bool too_long = ctl[kCtlMaxBucket] != 0u;
+    const uint32_t long_top = ctl[kCtlMaxBucket];  // highest long bucket + 1
+    const bool too_long = long_top > bt;            // some kept bucket is long
+    // A plateau bucket (see above) is looked at once the composites are in S: exactly one
+    // long kept bucket.
+    bool plateau = false;  // uniform
+    if constexpr (PBW > 0) plateau = too_long && ctl[kCtlLongN] == 1u;
     // (the bitonic sort pads to a power of two, which must fit S)
     constexpr uint32_t SORT_MAX = pow2_floor((uint32_t)(SCAP + rank_pad<LIMITED>()));
-    const bool sort_all = too_long && (!LIMITED || (sort_long && kept <= SORT_MAX));  // uniform
-    if (LIMITED && (kept > (uint32_t)SCAP || (too_long && !sort_all))) return false;  // uniform
+    bool sort_all = too_long && !plateau && (!LIMITED || (sort_long && kept <= SORT_MAX));  // uniform
+    if (LIMITED && (kept > (uint32_t)SCAP || (too_long && !plateau && !sort_all))) return false;  // uniform
 
     // ---- scatter kept candidates by bucket, two per lane at a time (claim both, then write).
     // A candidate that is not kept claims nothing: its claim word stays all ones, whose
@@ -1119,6 +1165,49 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     }
     for (int i = tid; i < rank_pad<LIMITED>(); i += NT) S[kept + i] = 0;  // kept <= SCAP here
     __syncthreads();
+    const uint16_t* const b16 = reinterpret_cast<const uint16_t*>(bucket);
+    if constexpr (PBW > 0) {
+        if (plateau) {  // uniform: the long bucket's key X and its other composites
+            const uint32_t pb = long_top - 1u;
+            const uint32_t q0 = b16[pb + 1], q1 = b16[pb];  // its slots in S
+            for (int w = tid; w < PBW; w += NT) pl->bits[w] = 0u;  // (S's tail: the candidates are in S)
+            uint64_t f = 0;  // (one atomic per wave: same-address LDS atomics serialise)
+            for (uint32_t q = q0 + tid; q < q1; q += NT) {
+                const uint64_t c = S[q];
+                f = max(f, (c << 32) | (c >> 32));
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) f = max(f, (uint64_t)__shfl_xor((unsigned long long)f, o));
+            if (lane == 0 && f)
+                __hip_atomic_fetch_max(reinterpret_cast<uint64_t*>(&ctl[kCtlPFirst]), f, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            __syncthreads();
+            const uint32_t px = __builtin_amdgcn_readfirstlane(ctl[kCtlPFirst]);  // (the low word: the key)
+            uint32_t cnt = 0;  // (above X) << 16 | (equal to X), this thread's
+            for (uint32_t q = q0 + tid; q < q1; q += NT) {
+                const uint64_t c = S[q];
+                const uint32_t kx = (uint32_t)(c >> 32), pos = ~(uint32_t)c;
+                if (kx == px) {
+                    __hip_atomic_fetch_or(&pl->bits[pos >> 5], 1u << (pos & 31u), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+                    cnt += 1u;
+                } else {
+                    const uint32_t o = __hip_atomic_fetch_add(&ctl[kCtlPOther], 1u, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_WORKGROUP);
+                    if (o < (uint32_t)kBucketLimit) pl->other[o] = c;
+                    if (kx > px) cnt += 1u << 16;
+                }
+            }
+            cnt = wave_incl_scan(cnt);  // (both halves stay below 2^16: at most SCAP in the bucket)
+            if (lane == 63 && cnt) lds_add(&ctl[kCtlPCount], cnt);
+            __syncthreads();
+            if (ctl[kCtlPOther] > (uint32_t)kBucketLimit) {  // uniform: X is not the bucket's one key
+                plateau = false;
+                sort_all = sort_long && kept <= SORT_MAX;
+                if (!sort_all) return false;  // (nothing emitted yet)
+            }
+        }
+    }
     scattered();  // past the point of falling back: the caller may reuse its registers
 
     if (sort_all) {  // uniform
@@ -1133,44 +1222,72 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
     // RUNR elements at once: it counts the larger composites among the lmax entries from
     // its bucket's start, lmax being the wave's longest bucket; entries past its bucket's
     // end belong to lower buckets or the zero padding, so every lane compares them all.
-    const uint16_t* const b16 = reinterpret_cast<const uint16_t*>(bucket);
     constexpr int RUNR = 2;
     const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)(tid & ~63));  // (scalar: a uniform loop exit)
-    for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
-        if (q0 + wbase >= kept) break;  // nothing left for this wave
-        uint64_t cc[RUNR];
-        uint32_t st[RUNR], rank[RUNR];
-        int32_t ox[RUNR];  // the index written for the element (a page-table load is issued here,
-                           // so its latency hides behind the comparisons)
-        uint32_t lmax = 0;
-#pragma unroll
-        for (int i = 0; i < RUNR; ++i) {
-            const uint32_t q = q0 + i * NT + tid;
-            const bool in = q < kept;
-            cc[i] = S[min(q, kept)];  // S[kept] is zero: no branch around the read
-            ox[i] = in ? xo(~(uint32_t)cc[i]) : 0;
-            const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
-            const uint32_t en = min((uint32_t)b16[bk], kept);
-            const uint32_t s0 = b16[bk + 1];
-            st[i] = in ? s0 : 0u;
-            lmax = max(lmax, in && en > s0 ? en - s0 : 0u);
-            rank[i] = 0;
-        }
-        lmax = wave_max(lmax);
-        for (uint32_t f = 0; f < lmax; f += kRankUnroll) {
+    // SKIP: the plateau bucket's elements are placed apart (not ranked here)
+    auto rank_kept = [&](auto skip_tag) {
+        constexpr bool SKIP = decltype(skip_tag)::value;
+        const uint32_t pb = SKIP ? long_top - 1u : 0u;
+        for (uint32_t q0 = 0; q0 < kept; q0 += RUNR * NT) {
+            if (q0 + wbase >= kept) break;  // nothing left for this wave
+            uint64_t cc[RUNR];
+            uint32_t st[RUNR], rank[RUNR];
+            int32_t ox[RUNR];  // the index written for the element (a page-table load is issued here,
+                               // so its latency hides behind the comparisons)
+            bool in[RUNR];
+            uint32_t lmax = 0;
 #pragma unroll
             for (int i = 0; i < RUNR; ++i) {
-                const uint64_t* const o = S + st[i] + f;
+                const uint32_t q = q0 + i * NT + tid;
+                cc[i] = S[min(q, kept)];  // S[kept] is zero: no branch around the read
+                const uint32_t bk = bucket_of((uint32_t)(cc[i] >> 32));
+                in[i] = q < kept && (!SKIP || bk != pb);
+                ox[i] = in[i] ? xo(~(uint32_t)cc[i]) : 0;
+                const uint32_t en = min((uint32_t)b16[bk], kept);
+                const uint32_t s0 = b16[bk + 1];
+                st[i] = in[i] ? s0 : 0u;
+                lmax = max(lmax, in[i] && en > s0 ? en - s0 : 0u);
+                rank[i] = 0;
+            }
+            lmax = wave_max(lmax);
+            for (uint32_t f = 0; f < lmax; f += kRankUnroll) {
 #pragma unroll
-                for (int u = 0; u < kRankUnroll; ++u) rank[i] += o[u] > cc[i] ? 1u : 0u;
+                for (int i = 0; i < RUNR; ++i) {
+                    const uint64_t* const o = S + st[i] + f;
+#pragma unroll
+                    for (int u = 0; u < kRankUnroll; ++u) rank[i] += o[u] > cc[i] ? 1u : 0u;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RUNR; ++i) {
+                const uint32_t slot = st[i] + rank[i];
+                if (in[i] && slot < mlim) emit(slot, ox[i], bits_of((uint32_t)(cc[i] >> 32)));
             }
         }
-#pragma unroll
-        for (int i = 0; i < RUNR; ++i) {
-            const uint32_t slot = st[i] + rank[i];
-            if (q0 + i * NT + tid < kept && slot < mlim) emit(slot, ox[i], bits_of((uint32_t)(cc[i] >> 32)));
+    };
+    if constexpr (PBW > 0) {
+        if (plateau) {  // uniform
+            rank_kept(std::true_type{});
+            // the bucket's other keys, ranked among themselves; those below X also pass X's
+            const uint32_t base = b16[long_top];  // the bucket's first slot (end of the one above)
+            const uint32_t px = ctl[kCtlPFirst], pcount = ctl[kCtlPCount], pother = ctl[kCtlPOther];
+            const uint32_t n_eq = pcount & 0xFFFFu, n_gt = pcount >> 16;
+            for (uint32_t t = tid; t < pother; t += NT) {
+                const uint64_t y = pl->other[t];
+                uint32_t rk = (uint32_t)(y >> 32) < px ? n_eq : 0u;
+                for (uint32_t j = 0; j < pother; ++j) rk += pl->other[j] > y ? 1u : 0u;
+                const uint32_t slot = base + rk;
+                if (slot < mlim) emit(slot, xo(~(uint32_t)y), bits_of((uint32_t)(y >> 32)));
+            }
+            const uint32_t b0 = base + n_gt;  // X's first slot
+            pl->on = true;
+            pl->key = px;
+            pl->base = b0;
+            pl->need = b0 < mlim ? min(n_eq, mlim - b0) : 0u;
+            return true;
         }
     }
+    rank_kept(std::false_type{});
     return true;
 }
 
@@ -1178,10 +1295,15 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
 // thread t owns the tile's positions [t EPT, (t + 1) EPT), a field of one bitmap word
 // (word_at(w) reads word w).  The set bits, counted from `first` (ties in earlier tiles),
 // go to slots c_gt + i while i < need, as the index of tile position p0 + bit.  Returns
-// the tile's set bits.  Contains barriers (a block scan over wsum).
+// the tile's set bits.  The positions are first listed in LDS (`stage`, at least need
+// words, free from the first barrier in here to the caller's next one), so that the
+// output stores run over consecutive slots: written straight from the bitmap fields,
+// neighbouring lanes would store a field's length apart.  Contains barriers (a block
+// scan over wsum, then the list).
 template <int NT, int EPT, class WordAt>
 __device__ __forceinline__ uint32_t emit_ties(WordAt&& word_at, int32_t p0, uint32_t first, uint32_t need,
-                                              uint32_t c_gt, uint32_t vP, const RowCtx& r, uint32_t* wsum) {
+                                              uint32_t c_gt, uint32_t vP, const RowCtx& r, uint32_t* wsum,
+                                              uint32_t* stage) {
     static_assert(EPT <= 32 && 32 % EPT == 0, "a thread's positions lie in one bitmap word");
     const int tid = opaque_tid();
     uint32_t bits = word_at((tid * EPT) >> 5);
@@ -1192,9 +1314,15 @@ __device__ __forceinline__ uint32_t emit_ties(WordAt&& word_at, int32_t p0, uint
     while (bits && rr < need) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1;
-        r.oidx[c_gt + rr] = r.xo((uint32_t)(pt + bit));
-        if (r.ov) r.ov.put(c_gt + rr, vP);
+        stage[rr - first] = (uint32_t)(pt + bit);
         ++rr;
+    }
+    const uint32_t cnt = first < need ? min(tot, need - first) : 0u;  // (uniform)
+    __syncthreads();
+    for (uint32_t i = tid; i < cnt; i += NT) {
+        const uint32_t slot = c_gt + first + i;
+        r.oidx[slot] = r.xo(stage[i]);
+        if (r.ov) r.ov.put(slot, vP);
     }
     return tot;
 }
@@ -1212,7 +1340,9 @@ __device__ __forceinline__ void bucket_range(uint32_t P, uint32_t lo, uint32_t s
 // Pivot path of a row that fits one workgroup (raw bits in u[], dead after the write pass).
 // Returns false, with LDS left dirty, when the row needs the exact path.  scattered() runs
 // once the row can no longer fall back.
-template <int NT, int EPT, int KMAX, class Scattered>
+// PLATEAU: a long kept bucket of one key is placed by position (bucket_rank's plateau
+// bucket) instead of sending the row to the sort or the exact path.
+template <int NT, int EPT, int KMAX, bool PLATEAU, class Scattered>
 __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMAX>& s, const uint32_t (&u)[EPT],
                                           int fast_mode, Scattered&& scattered) {
     using FS = FastSmem<NT, EPT, KMAX>;
@@ -1227,7 +1357,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     uint32_t* const shist = reinterpret_cast<uint32_t*>(s.S);  // sample histograms (the list's LDS is free until the write pass)
     block_zero<NT, 2 * kRadix>(shist);
     block_zero<NT, kBuckets / 2>(s.bucket);
-    if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
+    if (tid < FS::CTL_WORDS) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot
     uint32_t sk[kSamplesPerLane];
@@ -1389,7 +1519,8 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     // tid + NT i)
     constexpr int RC = (int)(R / 64), PC = (int)((POOL + NT - 1) / NT);
     const uint32_t c_w = o - base;  // this wave's region entries (scalar)
-    if (!bucket_rank<NT, FS::SCAP, RC + PC, true, false>(
+    PlateauBucket pl{s.plateau.other, s.plateau.bits};
+    if (!bucket_rank<NT, FS::SCAP, RC + PC, true, false, PLATEAU ? FS::BWORDS : 0>(
             s.bucket, s.S, s.wsum, s.ctl,
             [&](int i) {
                 const uint32_t q = i < RC ? base + (uint32_t)(lane + 64 * i) : NW * R + (uint32_t)(tid + (i - RC) * NT);
@@ -1405,12 +1536,18 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
                 store_at(r.oidx, slot, idx);
                 if (r.ov) r.ov.put(slot, bits);
             },
-            scattered, m == nt))
+            scattered, m == nt, &pl))
         return false;
+    if (pl.on) {  // uniform: a plateau bucket's key, in position order
+        emit_ties<NT, EPT>([&](int w) { return s.plateau.bits[w]; }, 0, 0u, pl.need, pl.base, bits_of(pl.key), r,
+                           s.wsum, reinterpret_cast<uint32_t*>(s.S));
+        __syncthreads();  // (wsum is scanned through again below)
+    }
 
     // ------------------------------------------------ ties at P: smallest positions
     if (ties)
-        emit_ties<NT, EPT>([&](int w) { return s.bitmap[w]; }, 0, 0u, (uint32_t)m - c_gt, c_gt, bits_of(P), r, s.wsum);
+        emit_ties<NT, EPT>([&](int w) { return s.bitmap[w]; }, 0, 0u, (uint32_t)m - c_gt, c_gt, bits_of(P), r, s.wsum,
+                           reinterpret_cast<uint32_t*>(s.S));
     write_padding<NT>(r.oidx, r.ov, m, r.k);
     return true;
 }
@@ -1492,9 +1629,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
 
     if (p.fast) {
         uint32_t sk[4 * SL];
-        load_row_samples<NT, SL, VB>(sk, row, n);  // (issued first: the pivot needs them first)
-        uint32_t u[EPT];
-        load_tile<NT, EPT, VB>(u, row + (size_t)j0 * VB, nt);
+        load_row_samples<NT, SL, VB>(sk, row, n);
 
         // ------------------------------------------------ pivot from the row's samples
         block_zero<NT, 4 * kRadix>(s.bucket);  // the sample-digit histograms
@@ -1516,6 +1651,12 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
                 __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
+        // The tile's loads are issued only past that barrier (which they cannot cross), so
+        // the wait before it is for the samples alone -- the tile load takes one of two code
+        // paths, and past that branch the compiler would wait for every load outstanding --
+        // and they complete behind the pivot passes.
+        uint32_t u[EPT];
+        load_tile<NT, EPT, VB>(u, row + (size_t)j0 * VB, nt);
         constexpr int nsamp = 4 * SL * NT;
         // (fast == 2, a test setting, aims at the largest sample: the pivot misses.)
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
@@ -1627,7 +1768,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     uint32_t L, U;
     bucket_range(P, s.ctl[kCtlLo], s.ctl[kCtlSmaxAll], s.ctl[kCtlSmaxFin], &L, &U);
     const uint2* const gc = p.ws_cand + (int64_t)b * CAP;
-    bucket_rank<NT, SS::SCAP, (SS::SCAP + NT - 1) / NT, false, false>(
+    bucket_rank<NT, SS::SCAP, (SS::SCAP + NT - 1) / NT, false, false, 0>(
         s.bucket, s.S, s.wsum, s.ctl, [&](int i) { return gc[tid + i * NT]; },
         [&](int i) { return (uint32_t)(tid + i * NT) < c_gt; }, [&](int i) { return (uint32_t)(i * NT) < c_gt; },
         c_gt, (uint32_t)m, ties, BucketMapT<true>(L, U), r.xo,
@@ -1647,7 +1788,8 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
             const uint32_t e = ecnt[t];
             if (e == 0) continue;  // uniform: that tile stored no bitmap
             const uint32_t* const gt = p.ws_tie + ((int64_t)b * p.tiles_per_row + t) * BW;
-            emit_ties<NT, EPT>([&](int w) { return gt[w]; }, t * TILE, off, need, c_gt, vP, r, s.wsum);
+            emit_ties<NT, EPT>([&](int w) { return gt[w]; }, t * TILE, off, need, c_gt, vP, r, s.wsum,
+                               reinterpret_cast<uint32_t*>(s.S));
             off += e;
             __syncthreads();  // (wsum is scanned again next turn)
         }
@@ -2069,7 +2211,13 @@ __device__ __forceinline__ void whole_tile_row(const Params& p, SmemAll<NT, EPT,
     const char* const row = static_cast<const char*>(p.scores) + r.base * VB;
     uint32_t u[EPT];
     load_tile<NT, EPT, VB>(u, row, r.nt);
-    if (p.fast && fast_tile<NT, EPT, KMAX>(r, s.fast, u, p.fast, [] {})) return;
+    // (The plateau bucket is compiled into the kernels of 1024-thread workgroups -- small
+    // batches, 32K-element rows -- and of split rows, where one slow row sets the time of
+    // the call.  The many-row kernels leave it out: among thousands of rows a plateau row
+    // costs only its own workgroup, while the extra code measured 1.2 % slower on the
+    // prefill batch.)
+    constexpr bool PLATEAU = MULTI || NT == 1024;
+    if (p.fast && fast_tile<NT, EPT, KMAX, PLATEAU>(r, s.fast, u, p.fast, [] {})) return;
     if (p.fast) {
         __syncthreads();  // fall back to the exact path
         // (reloaded: kept in registers through the pivot path, the tile would crowd out its

@@ -246,3 +246,60 @@ def test_whole_row_outputs_k4096(dev, shape):
     rows = [_bottom_family(rng, f, n) for f, n in (("zero_plateau", 4096), ("neg_inf_plateau", 3000),
                                                     ("neg_nan_bottom", 4095), ("unique_min", 1))]
     _check(dev, _dense(rows, 4096, "whole_k4096"), "whole-row outputs k=4096/%s" % shape, **SHAPES[shape])
+
+
+def _plateau_family(rng, fam, n):
+    """Rows where one key fills a long run of a kept bucket (the rest of the bucket: a few
+    neighbouring keys)."""
+    def with_neighbours(r, x, count):
+        u = r.view(np.uint32)
+        pos = rng.choice(n, size=count, replace=False)
+        near = np.array([x], np.float32).view(np.uint32)[0] + rng.integers(-3, 4, count).astype(np.int64)
+        u[pos] = near.astype(np.uint32)
+        return r
+    if fam == "zero_above_specials":  # whole row: +0.0 on 80 %, specials and negatives below it
+        r = W.relu_sum_mixture(rng, n, 0.8)
+        r[rng.random(n) < 0.05] = np.float32(-1.5)
+        u = r.view(np.uint32)
+        u[rng.choice(n, 6, replace=False)] = np.array([0x80000000, 0x00000001, 0xFFC00000, 0xFF800000,
+                                                        0x80000001, 0x7FC00000], np.uint32)
+        return r
+    if fam == "one_above_gauss":  # whole row: 1.0 on 60 %, keys within 3 ulps of it on a few
+        r = rng.standard_normal(n).astype(np.float32)
+        r[rng.random(n) < 0.6] = np.float32(1.0)
+        return with_neighbours(r, 1.0, 20)
+    if fam == "minority_first":  # the first position holds a rare key of the long bucket
+        r = W.relu_sum_mixture(rng, n, 0.8)
+        r[rng.random(n) < 0.05] = np.float32(-1.0)
+        r.view(np.uint32)[0] = np.uint32(0x00000001)
+        return r
+    if fam == "two_zeros":  # +0.0 and -0.0 share the bucket half and half
+        r = W.relu_sum_mixture(rng, n, 0.8)
+        z = np.flatnonzero(r == 0)
+        r[z[rng.random(z.size) < 0.5]] = np.float32(-0.0)
+        r[rng.random(n) < 0.05] = np.float32(-2.0)
+        return r
+    if fam == "kept_plateau":  # longer than k: a plateau of 1,500 at 3.0 inside the top k
+        r = rng.standard_normal(n).astype(np.float32)
+        r[rng.choice(n, 1500, replace=False)] = np.float32(3.0)
+        return with_neighbours(r, 3.0, 12)
+    # longer than k: the plateau straddles the k-th place (its key is the pivot)
+    r = rng.standard_normal(n).astype(np.float32)
+    r[rng.choice(n, 3000, replace=False)] = np.float32(3.0)
+    return r
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+@pytest.mark.parametrize("fam", ["zero_above_specials", "one_above_gauss", "minority_first", "two_zeros",
+                                 "kept_plateau", "straddling_plateau"])
+def test_plateau_buckets(dev, shape, fam):
+    """One key repeated on a long run of a kept bucket: those elements are placed by position
+    instead of ranked, the bucket's other keys ranked among themselves around them (or, when
+    the bucket's first element has a rare key or two keys share it, the sort or the exact path
+    takes the row).  Whole rows from 300 to k, and rows longer than k with the plateau inside
+    or straddling the top k."""
+    rng = np.random.default_rng(len(fam) * 17 + len(shape))
+    whole = fam not in ("kept_plateau", "straddling_plateau")
+    ns = (300, 1500, 2047, 2048) if whole else (4000, 9000, 16000)
+    rows = [_plateau_family(rng, fam, n) for n in ns]
+    _check(dev, _dense(rows, 2048, "plateau_" + fam), "plateau bucket %s/%s" % (fam, shape), **SHAPES[shape])
