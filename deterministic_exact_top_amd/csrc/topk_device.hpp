@@ -53,7 +53,7 @@ constexpr int kRankUnroll = 4;                  // composites compared per turn 
 // lower buckets' composites or these, all smaller than its own, so it needs no bound.
 template <bool LIMITED>
 constexpr int rank_pad() { return (LIMITED ? kBucketLimit : kBucketLimitRow) + kRankUnroll; }
-static_assert(kBuckets / 2 >= 4 * 256, "the packed bucket array doubles as the sample histograms");
+static_assert(kBuckets / 2 >= 5 * 256, "the packed bucket array doubles as the sample histograms");
 constexpr uint32_t pow2_floor(uint32_t x) { return x < 2 ? x : 2 * pow2_floor(x / 2); }
 constexpr int kSamplesPerLane = 2;           // fast path: pivot samples per lane
 constexpr uint32_t kNegInfBits = 0xFF800000u;
@@ -820,10 +820,13 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 // over the row's tiles otherwise).  Every wave, and every workgroup of a row, takes the
 // same decisions.  With sel (three LDS words), wave 0 alone selects each digit and
 // publishes it behind one more barrier, instead of every wave repeating the selection.
-template <int NT, int NH, int SPL, class Merge>
+// FLOOR: the first pass counts only the samples at or above `floor`, a bin boundary
+// known to lie at or below the rr-th largest sample (the ranks from the top, and so the
+// pivot, are those of all the samples).
+template <int NT, int NH, bool FLOOR = false, int SPL, class Merge>
 __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[SPL], uint32_t rr, uint32_t* hist,
                                                  Merge&& merge, uint32_t* ctl, int* passes = nullptr,
-                                                 uint32_t* sel = nullptr) {
+                                                 uint32_t* sel = nullptr, uint32_t floor = 0) {
     const int tid = opaque_tid();
     uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
     int pass = 0;
@@ -862,7 +865,8 @@ __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[SPL], uint
         // and same-address LDS atomics serialise)
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-            if (pass == 0 || (sk[i] >> (shift + 8)) == prefix) hist_add(h, (sk[i] >> shift) & 0xFFu);
+            if (pass == 0 ? (!FLOOR || sk[i] >= floor) : (sk[i] >> (shift + 8)) == prefix)
+                hist_add(h, (sk[i] >> shift) & 0xFFu);
         __syncthreads();
         merge(pass, h);
         uint32_t above, d;
@@ -1632,7 +1636,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
         load_row_samples<NT, SL, VB>(sk, row, n);
 
         // ------------------------------------------------ pivot from the row's samples
-        block_zero<NT, 4 * kRadix>(s.bucket);  // the sample-digit histograms
+        block_zero<NT, 5 * kRadix>(s.bucket);  // the sample-digit histograms, and the lane maxima's
         if (tid < 16) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 #pragma unroll
         for (int i = 0; i < 4 * SL; ++i) sk[i] = key_of(sk[i]);
@@ -1660,9 +1664,26 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
         constexpr int nsamp = 4 * SL * NT;
         // (fast == 2, a test setting, aims at the largest sample: the pivot misses.)
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
-        if (rr < (uint32_t)nsamp)
-            P = pivot_passes<NT, 4>(sk, rr, s.bucket, [](int, uint32_t*) {}, s.ctl, nullptr,
-                                    r.wave_select ? nullptr : s.ctl + kCtlSel);
+        if (rr < (uint32_t)nsamp) {
+            // The rr-th largest lane maximum is at most the rr-th largest sample (were it
+            // larger, rr lanes would each hold a larger sample), so no sample below its
+            // first-digit bin decides the pivot.  One count of the lane maxima (one atomic
+            // per lane instead of one per sample) lets the first pass skip those samples:
+            // for a long row with a small k, nearly all of them.
+            uint32_t floor = 0;
+            if (rr <= (uint32_t)NT) {
+                uint32_t lm = 0;
+#pragma unroll
+                for (int i = 0; i < 4 * SL; ++i) lm = max(lm, sk[i]);
+                uint32_t* const hm = s.bucket + 4 * kRadix;
+                hist_add(hm, lm >> 24);
+                __syncthreads();
+                uint32_t above, cnt;
+                floor = wave_select_digit(hm, rr, &above, &cnt) << 24;
+            }
+            P = pivot_passes<NT, 4, true>(sk, rr, s.bucket, [](int, uint32_t*) {}, s.ctl, nullptr,
+                                          r.wave_select ? nullptr : s.ctl + kCtlSel, floor);
+        }
         {
             uint32_t lo = 0xFFFFFFFFu;
 #pragma unroll
