@@ -616,6 +616,16 @@ def main():
             "ms_per_step": m2["ms_per_step"], "rows_per_s": wl2.B / (m2["ms_per_step"] * 1e-3),
             "roofline": m2["roofline"], "rounds": m2["rounds"], "parity": m2["parity"],
         }
+        if args.dtype == "f32" and args.index_transform == "none":
+            # the same calls captured once in a HIP graph and replayed (no host work between
+            # the kernels), beside the same call with every row empty
+            log("timing %s from a graph" % SECONDARY)
+            gr = graph_timing(wl2, outputs=True)
+            par = parity_check(wl2, gr.pop("_outputs"))
+            gr["parity_ok"] = bool(par["ok"])
+            gr["empty_call_us"] = empty_graph_floor(wl2)
+            result["secondary"]["graph_replay"] = gr
+            m2["parity"]["ok"] = m2["parity"]["ok"] and gr["parity_ok"]
         ok_all = m["parity"]["ok"] and m2["parity"]["ok"]
     else:
         ok_all = m["parity"]["ok"]

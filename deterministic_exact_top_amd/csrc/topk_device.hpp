@@ -49,6 +49,7 @@ constexpr int kBucketLimit = 128;               // fast path: largest bucket ran
 constexpr int kBucketLimitRow = 512;            // the same, ordering a split row's candidates
 constexpr int kKeptSlack = 96;                  // fast path: kept candidates past KMAX that fit S
 constexpr int kRankUnroll = 4;                  // composites compared per turn of the ranking loop
+constexpr int kDirectTies = 64;                 // ties stored straight from the bitmap (more go through LDS)
 // Zero composites past the kept ones: a ranking loop running past a bucket's end reads
 // lower buckets' composites or these, all smaller than its own, so it needs no bound.
 template <bool LIMITED>
@@ -1299,11 +1300,11 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
 // thread t owns the tile's positions [t EPT, (t + 1) EPT), a field of one bitmap word
 // (word_at(w) reads word w).  The set bits, counted from `first` (ties in earlier tiles),
 // go to slots c_gt + i while i < need, as the index of tile position p0 + bit.  Returns
-// the tile's set bits.  The positions are first listed in LDS (`stage`, at least need
-// words, free from the first barrier in here to the caller's next one), so that the
-// output stores run over consecutive slots: written straight from the bitmap fields,
-// neighbouring lanes would store a field's length apart.  Contains barriers (a block
-// scan over wsum, then the list).
+// the tile's set bits.  Beyond kDirectTies of them, the positions are first listed in LDS
+// (`stage`, at least need words, free from the first barrier in here to the caller's next
+// one), so that the output stores run over consecutive slots: written straight from the
+// bitmap fields, neighbouring lanes would store a field's length apart.  Contains
+// barriers (a block scan over wsum, then the list when there is one).
 template <int NT, int EPT, class WordAt>
 __device__ __forceinline__ uint32_t emit_ties(WordAt&& word_at, int32_t p0, uint32_t first, uint32_t need,
                                               uint32_t c_gt, uint32_t vP, const RowCtx& r, uint32_t* wsum,
@@ -1315,13 +1316,23 @@ __device__ __forceinline__ uint32_t emit_ties(WordAt&& word_at, int32_t p0, uint
     uint32_t tot;
     uint32_t rr = first + block_excl_scan<NT>((uint32_t)__popc(bits), wsum, &tot);
     const int32_t pt = p0 + tid * EPT;
+    const uint32_t cnt = first < need ? min(tot, need - first) : 0u;  // (uniform)
+    if (cnt <= (uint32_t)kDirectTies) {  // uniform: a few stores, straight from the fields
+        while (bits && rr < need) {
+            const int bit = __ffs(bits) - 1;
+            bits &= bits - 1;
+            r.oidx[c_gt + rr] = r.xo((uint32_t)(pt + bit));
+            if (r.ov) r.ov.put(c_gt + rr, vP);
+            ++rr;
+        }
+        return tot;
+    }
     while (bits && rr < need) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1;
         stage[rr - first] = (uint32_t)(pt + bit);
         ++rr;
     }
-    const uint32_t cnt = first < need ? min(tot, need - first) : 0u;  // (uniform)
     __syncthreads();
     for (uint32_t i = tid; i < cnt; i += NT) {
         const uint32_t slot = c_gt + first + i;
@@ -1634,6 +1645,8 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     if (p.fast) {
         uint32_t sk[4 * SL];
         load_row_samples<NT, SL, VB>(sk, row, n);
+        uint32_t u_early[EPT];
+        if constexpr (EPT >= 32) load_tile<NT, EPT, VB>(u_early, row + (size_t)j0 * VB, nt);
 
         // ------------------------------------------------ pivot from the row's samples
         block_zero<NT, 5 * kRadix>(s.bucket);  // the sample-digit histograms, and the lane maxima's
@@ -1660,7 +1673,11 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
         // paths, and past that branch the compiler would wait for every load outstanding --
         // and they complete behind the pivot passes.
         uint32_t u[EPT];
-        load_tile<NT, EPT, VB>(u, row + (size_t)j0 * VB, nt);
+        if constexpr (EPT < 32) load_tile<NT, EPT, VB>(u, row + (size_t)j0 * VB, nt);
+        else {
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) u[i] = u_early[i];
+        }
         constexpr int nsamp = 4 * SL * NT;
         // (fast == 2, a test setting, aims at the largest sample: the pivot misses.)
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
@@ -1671,7 +1688,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
             // per lane instead of one per sample) lets the first pass skip those samples:
             // for a long row with a small k, nearly all of them.
             uint32_t floor = 0;
-            if (rr <= (uint32_t)NT) {
+            if (rr <= (uint32_t)NT / 4) {
                 uint32_t lm = 0;
 #pragma unroll
                 for (int i = 0; i < 4 * SL; ++i) lm = max(lm, sk[i]);
