@@ -49,7 +49,6 @@ constexpr int kBucketLimit = 128;               // fast path: largest bucket ran
 constexpr int kBucketLimitRow = 512;            // the same, ordering a split row's candidates
 constexpr int kKeptSlack = 96;                  // fast path: kept candidates past KMAX that fit S
 constexpr int kRankUnroll = 4;                  // composites compared per turn of the ranking loop
-constexpr int kDirectTies = 64;                 // ties stored straight from the bitmap (more go through LDS)
 // Zero composites past the kept ones: a ranking loop running past a bucket's end reads
 // lower buckets' composites or these, all smaller than its own, so it needs no bound.
 template <bool LIMITED>
@@ -1300,11 +1299,11 @@ __device__ __forceinline__ bool bucket_rank(uint32_t* bucket, uint64_t* S, uint3
 // thread t owns the tile's positions [t EPT, (t + 1) EPT), a field of one bitmap word
 // (word_at(w) reads word w).  The set bits, counted from `first` (ties in earlier tiles),
 // go to slots c_gt + i while i < need, as the index of tile position p0 + bit.  Returns
-// the tile's set bits.  Beyond kDirectTies of them, the positions are first listed in LDS
-// (`stage`, at least need words, free from the first barrier in here to the caller's next
-// one), so that the output stores run over consecutive slots: written straight from the
-// bitmap fields, neighbouring lanes would store a field's length apart.  Contains
-// barriers (a block scan over wsum, then the list when there is one).
+// the tile's set bits.  The positions are first listed in LDS (`stage`, at least need
+// words, free from the first barrier in here to the caller's next one), so that the
+// output stores run over consecutive slots: written straight from the bitmap fields,
+// neighbouring lanes would store a field's length apart.  Contains barriers (a block
+// scan over wsum, then the list).
 template <int NT, int EPT, class WordAt>
 __device__ __forceinline__ uint32_t emit_ties(WordAt&& word_at, int32_t p0, uint32_t first, uint32_t need,
                                               uint32_t c_gt, uint32_t vP, const RowCtx& r, uint32_t* wsum,
@@ -1316,23 +1315,13 @@ __device__ __forceinline__ uint32_t emit_ties(WordAt&& word_at, int32_t p0, uint
     uint32_t tot;
     uint32_t rr = first + block_excl_scan<NT>((uint32_t)__popc(bits), wsum, &tot);
     const int32_t pt = p0 + tid * EPT;
-    const uint32_t cnt = first < need ? min(tot, need - first) : 0u;  // (uniform)
-    if (cnt <= (uint32_t)kDirectTies) {  // uniform: a few stores, straight from the fields
-        while (bits && rr < need) {
-            const int bit = __ffs(bits) - 1;
-            bits &= bits - 1;
-            r.oidx[c_gt + rr] = r.xo((uint32_t)(pt + bit));
-            if (r.ov) r.ov.put(c_gt + rr, vP);
-            ++rr;
-        }
-        return tot;
-    }
     while (bits && rr < need) {
         const int bit = __ffs(bits) - 1;
         bits &= bits - 1;
         stage[rr - first] = (uint32_t)(pt + bit);
         ++rr;
     }
+    const uint32_t cnt = first < need ? min(tot, need - first) : 0u;  // (uniform)
     __syncthreads();
     for (uint32_t i = tid; i < cnt; i += NT) {
         const uint32_t slot = c_gt + first + i;
@@ -1645,6 +1634,9 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
     if (p.fast) {
         uint32_t sk[4 * SL];
         load_row_samples<NT, SL, VB>(sk, row, n);
+        // A 32K-element tile's loads go out with the samples: that tile serves batches that
+        // fill the GPU, where the HBM stream matters more than one tile's latency (the pivot
+        // then waits for all of them, see below).
         uint32_t u_early[EPT];
         if constexpr (EPT >= 32) load_tile<NT, EPT, VB>(u_early, row + (size_t)j0 * VB, nt);
 
@@ -1668,7 +1660,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
                 __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
-        // The tile's loads are issued only past that barrier (which they cannot cross), so
+        // Smaller tiles issue their loads only past that barrier (which they cannot cross), so
         // the wait before it is for the samples alone -- the tile load takes one of two code
         // paths, and past that branch the compiler would wait for every load outstanding --
         // and they complete behind the pivot passes.
@@ -1686,7 +1678,8 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
             // larger, rr lanes would each hold a larger sample), so no sample below its
             // first-digit bin decides the pivot.  One count of the lane maxima (one atomic
             // per lane instead of one per sample) lets the first pass skip those samples:
-            // for a long row with a small k, nearly all of them.
+            // for a long row with a small k, nearly all of them.  (With rr past a quarter of
+            // the lanes the floor would filter little and cost a pass.)
             uint32_t floor = 0;
             if (rr <= (uint32_t)NT / 4) {
                 uint32_t lm = 0;
