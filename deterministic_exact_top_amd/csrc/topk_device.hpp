@@ -48,7 +48,7 @@ constexpr int kBucketBits = 12;
 constexpr int kBucketLimit = 128;               // fast path: largest bucket ranked by comparisons
 constexpr int kBucketLimitRow = 512;            // the same, ordering a split row's candidates
 constexpr int kKeptSlack = 96;                  // fast path: kept candidates past KMAX that fit S
-constexpr int kRankUnroll = 4;                  // composites compared per turn of the ranking loop
+constexpr int kRankUnroll = 3;                  // composites compared per turn of the ranking loop
 // Zero composites past the kept ones: a ranking loop running past a bucket's end reads
 // lower buckets' composites or these, all smaller than its own, so it needs no bound.
 template <bool LIMITED>
