@@ -5,6 +5,7 @@
 // enqueues the kernels on the caller's stream.  No allocation, no synchronisation,
 // no device readback: a call can be captured into a HIP graph.
 #include <hip/hip_runtime.h>
+#include <cmath>
 
 #include <mutex>
 #include <string.h>
@@ -132,6 +133,7 @@ struct Plan {
     int tiles_per_row = 1;
     bool wide = false;    // one workgroup per row, small-batch (1024-thread) shape
     bool small = false;   // no more workgroups than CUs: every wave selects pivot digits
+    bool half = false;    // split rows: half the row samples
     int grid = 0;
     size_t lds = 0;
     size_t ws_bytes = 0;
@@ -218,6 +220,15 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         pl->grid = (int)(items < kMaxSplitGrid ? items : kMaxSplitGrid);
         // Data regions, from the start of the data area (see data_offset()).
         const size_t cap = pl->kmax == 2048 ? detk::cand_cap<2048>() : detk::cand_cap<4096>();
+        // Half the row samples when, even with them, the longest row's candidates stay
+        // within the list by four standard deviations: the pivot passes cost half as much.
+        // (Pivot at the r-th largest of s samples, r = e + 3.5 sqrt(e) + 4, e = s m / n:
+        // about r n / s keys above it, give or take n sqrt(r) / s.)
+        {
+            const double s = detk::kSplitSamples / 2, n = (double)max_len, m = (double)(k < max_len ? k : max_len);
+            const double e = s * m / n, r = e + 3.5 * std::sqrt(e) + 4.0;
+            pl->half = r * n / s + 4.0 * n * std::sqrt(r) / s <= (double)cap;
+        }
         size_t off = 0;
         pl->off_ecnt = off;
         off = align256(off + (size_t)B * (size_t)tpr * 4);
@@ -346,6 +357,7 @@ int run(const void* scores, int dtype, const int32_t* row_starts, const int32_t*
     p.stage_cap = g_stage_cap < 0 ? detk::kStageCap : (g_stage_cap > detk::kStageCap ? detk::kStageCap : g_stage_cap);
     p.fast = g_fast;
     p.small_batch = pl.small ? 1 : 0;
+    p.split_half = pl.half ? 1 : 0;
     p.out_idx = out_idx;
     p.out_val = out_val;
     p.val_pad = dtype == DETK_DTYPE_F16 ? 0xFC00u : dtype == DETK_DTYPE_BF16 ? 0xFF80u : detk::kNegInfBits;

@@ -79,6 +79,7 @@ struct Params {
     int32_t fast;               // 1: try the pivot fast path first
     int32_t small_batch;        // nonzero: no more workgroups than CUs (latency over issue
                                 // slots: every wave selects the pivot digits itself)
+    int32_t split_half;         // split-row kernel: nonzero, half the row samples (kSplitSamples / 2)
     int32_t* out_idx;
     void* out_val;              // nullable: VB-byte values
     uint32_t val_pad;           // the value written in padded slots (-inf of the format)
@@ -823,10 +824,12 @@ __device__ __forceinline__ uint32_t pivot_rank(int nsamp, int32_t m, int32_t n) 
 // FLOOR: the first pass counts only the samples at or above `floor`, a bin boundary
 // known to lie at or below the rr-th largest sample (the ranks from the top, and so the
 // pivot, are those of all the samples).
+// spl (uniform): the samples that count are sk[0 .. spl); the rest hold key 0 and are
+// skipped by the histograms.
 template <int NT, int NH, bool FLOOR = false, int SPL, class Merge>
 __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[SPL], uint32_t rr, uint32_t* hist,
                                                  Merge&& merge, uint32_t* ctl, int* passes = nullptr,
-                                                 uint32_t* sel = nullptr, uint32_t floor = 0) {
+                                                 uint32_t* sel = nullptr, uint32_t floor = 0, int spl = SPL) {
     const int tid = opaque_tid();
     uint32_t prefix = 0, r_rem = rr, P = 0, cnt = 0xFFFFFFFFu;
     int pass = 0;
@@ -865,7 +868,7 @@ __device__ __forceinline__ uint32_t pivot_passes(const uint32_t (&sk)[SPL], uint
         // and same-address LDS atomics serialise)
 #pragma unroll
         for (int i = 0; i < SPL; ++i)
-            if (pass == 0 ? (!FLOOR || sk[i] >= floor) : (sk[i] >> (shift + 8)) == prefix)
+            if (i < spl && (pass == 0 ? (!FLOOR || sk[i] >= floor) : (sk[i] >> (shift + 8)) == prefix))
                 hist_add(h, (sk[i] >> shift) & 0xFFu);
         __syncthreads();
         merge(pass, h);
@@ -1565,8 +1568,9 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
 // group is group floor(q * G / (SL * NT)), q = g * NT + t, of the G = (n - a0) / 4 whole
 // groups (a row shorter than 4 * SL * NT elements repeats some, which only weakens the
 // pivot estimate).
+// sl (<= SL, uniform): groups per lane actually sampled; the others hold the least key.
 template <int NT, int SL, int VB>
-__device__ __forceinline__ void load_row_samples(uint32_t (&sk)[4 * SL], const char* row, int32_t n) {
+__device__ __forceinline__ void load_row_samples(uint32_t (&sk)[4 * SL], const char* row, int32_t n, int sl) {
     // a0: elements before the first (4 * VB)-byte boundary (rows start VB-byte aligned)
     const uint32_t a0 = ((4u * VB - (uint32_t)((uintptr_t)row & (4u * VB - 1u))) & (4u * VB - 1u)) / VB;
     const char* base = row + (size_t)a0 * VB;
@@ -1580,8 +1584,12 @@ __device__ __forceinline__ void load_row_samples(uint32_t (&sk)[4 * SL], const c
     const uint32_t tid = (uint32_t)opaque_tid();
 #pragma unroll
     for (int g = 0; g < SL; ++g) {
+        if (g >= sl) {  // uniform: bits whose key is 0, below every sample (they rank last)
+            sk[4 * g + 0] = sk[4 * g + 1] = sk[4 * g + 2] = sk[4 * g + 3] = VB == 4 ? 0xFFFFFFFFu : 0xFFFF0000u;
+            continue;
+        }
         const uint32_t q = (uint32_t)g * NT + tid;
-        const uint32_t grp = (uint32_t)(((uint64_t)q * groups) / (uint64_t)(SL * NT));
+        const uint32_t grp = (uint32_t)(((uint64_t)q * groups) / ((uint64_t)sl * NT));
         if constexpr (VB == 4) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, grp * 16u, 0, 0);
             sk[4 * g + 0] = v[0];
@@ -1633,7 +1641,9 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
 
     if (p.fast) {
         uint32_t sk[4 * SL];
-        load_row_samples<NT, SL, VB>(sk, row, n);
+        const int sl = p.split_half ? SL / 2 : SL;  // (uniform)
+        static_assert(SL % 2 == 0, "the samples halve");
+        load_row_samples<NT, SL, VB>(sk, row, n, sl);
         // A 32K-element tile's loads go out with the samples: that tile serves batches that
         // fill the GPU, where the HBM stream matters more than one tile's latency (the pivot
         // then waits for all of them, see below).
@@ -1670,7 +1680,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
 #pragma unroll
             for (int i = 0; i < EPT; ++i) u[i] = u_early[i];
         }
-        constexpr int nsamp = 4 * SL * NT;
+        const int nsamp = 4 * sl * NT;
         // (fast == 2, a test setting, aims at the largest sample: the pivot misses.)
         const uint32_t rr = p.fast == 2 ? 1u : pivot_rank(nsamp, m, n);
         if (rr < (uint32_t)nsamp) {
@@ -1692,7 +1702,7 @@ __device__ __forceinline__ void split_tile(const Params& p, const RowCtx& r, Sme
                 floor = wave_select_digit(hm, rr, &above, &cnt) << 24;
             }
             P = pivot_passes<NT, 4, true>(sk, rr, s.bucket, [](int, uint32_t*) {}, s.ctl, nullptr,
-                                          r.wave_select ? nullptr : s.ctl + kCtlSel, floor);
+                                          r.wave_select ? nullptr : s.ctl + kCtlSel, floor, 4 * sl);
         }
         {
             uint32_t lo = 0xFFFFFFFFu;
