@@ -55,7 +55,13 @@ template <bool LIMITED>
 constexpr int rank_pad() { return (LIMITED ? kBucketLimit : kBucketLimitRow) + kRankUnroll; }
 static_assert(kBuckets / 2 >= 5 * 256, "the packed bucket array doubles as the sample histograms");
 constexpr uint32_t pow2_floor(uint32_t x) { return x < 2 ? x : 2 * pow2_floor(x / 2); }
-constexpr int kSamplesPerLane = 2;           // fast path: pivot samples per lane
+// Fast path: pivot samples per lane.  Two, except where a lane holds no more than 8
+// elements (the 1024-thread shapes of 4K and 8K rows): there two per lane would sample a
+// half or a quarter of the row, and one keeps the candidates' excess small (3.5 sqrt(m n /
+// s) + 4 n / s for s samples) at half the histogram work.  (A 4096-row decode batch: 9.8 ->
+// 9.2 us.  One per lane on the 16K prefill tile overflows the candidate list.)
+template <int EPT>
+constexpr int samples_per_lane() { return EPT <= 8 ? 1 : 2; }
 constexpr uint32_t kNegInfBits = 0xFF800000u;
 // Per-row control words of the split-row path (a row spread over several workgroups).
 // They are zero when a call starts, and the row's last arriving workgroup sets them back
@@ -227,7 +233,8 @@ __device__ __forceinline__ uint32_t claim_slot(bool pred, uint32_t* counter) {
 // the pivot samples, PART 1 the others, PART 2 all of them (sample groups issued first).
 template <int NT, int EPT>
 constexpr bool sample_group(int v) {
-    return v % (EPT / 4 >= kSamplesPerLane ? EPT / 4 / kSamplesPerLane : 1) == 0;
+    constexpr int SPL = samples_per_lane<EPT>();
+    return v % (EPT / 4 >= SPL ? EPT / 4 / SPL : 1) == 0;
 }
 
 template <int NT, int EPT, int PART, int VB>
@@ -768,29 +775,32 @@ enum : int {
     kCtlPCount = 20,    // (its keys above the plateau key) << 16 | (those equal to it)
 };
 
-// Real samples among a tile's nt elements (uniform): slot i * EPT / kSamplesPerLane of
-// each lane, for the lanes whose slot lies inside the tile.
+// Real samples among a tile's nt elements (uniform): slot i * EPT / SPL of each lane
+// (SPL = samples_per_lane), for the lanes whose slot lies inside the tile.
 template <int NT, int EPT>
 __device__ __forceinline__ int tile_samples(int32_t nt) {
+    constexpr int SPL = samples_per_lane<EPT>();
     int ns = 0;
 #pragma unroll
-    for (int i = 0; i < kSamplesPerLane; ++i) {
-        const int slot = i * (EPT / kSamplesPerLane);
+    for (int i = 0; i < SPL; ++i) {
+        const int slot = i * (EPT / SPL);
         const int lim = nt - (slot / 4) * NT * 4 - slot % 4;
         ns += min(max((lim + 3) / 4, 0), NT);
     }
     return ns;
 }
 
-// This lane's samples: register slots i * EPT / kSamplesPerLane (the groups load_tile
-// issues first).  Slots past the tile give key 0, the least key, which never outranks a
-// real sample at the ranks asked for.
+// This lane's samples: register slots i * EPT / SPL (the groups load_tile issues first).
+// Slots past the tile give key 0, the least key, which never outranks a real sample at
+// the ranks asked for.
 template <int NT, int EPT>
-__device__ __forceinline__ void take_samples(const uint32_t (&u)[EPT], int32_t nt, uint32_t (&sk)[kSamplesPerLane]) {
+__device__ __forceinline__ void take_samples(const uint32_t (&u)[EPT], int32_t nt,
+                                             uint32_t (&sk)[samples_per_lane<EPT>()]) {
+    constexpr int SPL = samples_per_lane<EPT>();
     const int t4 = opaque_tid() * 4;
 #pragma unroll
-    for (int i = 0; i < kSamplesPerLane; ++i) {
-        const int slot = i * (EPT / kSamplesPerLane);
+    for (int i = 0; i < SPL; ++i) {
+        const int slot = i * (EPT / SPL);
         sk[i] = t4 + ((slot / 4) * NT * 4 + slot % 4) < nt ? key_of(u[slot]) : 0u;
     }
 }
@@ -1367,13 +1377,14 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     if (tid < FS::CTL_WORDS) s.ctl[tid] = tid == kCtlLo ? 0xFFFFFFFFu : 0u;
 
     // ------------------------------------------------ sample -> pivot
-    uint32_t sk[kSamplesPerLane];
+    constexpr int SPL = samples_per_lane<EPT>();
+    uint32_t sk[SPL];
     take_samples<NT, EPT>(u, nt, sk);
     const int nsamp = tile_samples<NT, EPT>(nt);
     {
         uint32_t sf = 0;  // largest sample below key(+inf)
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
+        for (int i = 0; i < SPL; ++i) sf = sk[i] < kKeyPosInf ? max(sf, sk[i]) : sf;
         sf = wave_max(sf);
         __syncthreads();
         if (lane == 0) __hip_atomic_fetch_max(&s.ctl[kCtlSmaxFin], sf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1402,7 +1413,7 @@ __device__ __forceinline__ bool fast_tile(const RowCtx& r, FastSmem<NT, EPT, KMA
     if (need_lo) {
         uint32_t lo = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
+        for (int i = 0; i < SPL; ++i) lo = sk[i] > P ? min(lo, sk[i]) : lo;
         lo = wave_min(lo);
         if (lane == 0) __hip_atomic_fetch_min(&s.ctl[kCtlLo], lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
