@@ -10,19 +10,22 @@
 // head reduction fused into the epilogue: the per-head logits never leave registers, and
 // only the [B, max_len] float32 scores are written.
 //
-// Work split: a 256-thread workgroup (4 waves) takes 16 query rows (4 per wave) and one
-// chunk of keys (1024 .. 16384, chosen per launch), walked in blocks of kKeyBlock keys.  A block's keys are staged in
-// LDS (padded rows, double-buffered; the loads run two blocks ahead, in registers, so each
-// block's HBM/L2 latency hides behind two blocks of MFMAs) and shared by the 16 queries; each wave keeps its queries' q fragments in
-// registers for the whole chunk.  Per block and wave: 4 queries x 4 key groups of 16 x
-// D / 32 steps MFMAs.  MFMA operand layout (16x16x32): lane l holds A[l % 16][8 (l / 16) + j]
-// and B[8 (l / 16) + j][l % 16] (j < 8), and C[4 (l / 16) + i][l % 16] (i < 4); here
-// A = the query's heads x head dims, B = head dims x 16 keys, so C holds four heads of one
-// key per lane.  The epilogue sums a lane's four heads (w_h * max(0, c_h)) for each of its
-// query's four key groups, then reduces over the four 16-lane rows and transposes at once
-// with three row swaps (v_permlane16_swap, v_permlane32_swap: no LDS traffic), leaving in
-// row r the totals of key group r -- the 64 consecutive keys of the block, one per lane, in
-// a fixed order of additions, so the bits do not depend on the schedule.
+// Work split: a 512-thread workgroup (8 waves) takes 16 query rows (2 per wave) and one
+// chunk of keys (1024 .. 16384, chosen per launch), walked in blocks of kKeyBlock keys.  A
+// block's keys are staged in LDS (padded rows, double-buffered; the loads run two blocks
+// ahead, in registers, so each block's HBM/L2 latency hides behind two blocks of MFMAs)
+// and shared by the 16 queries; each wave keeps its queries' q fragments in registers for
+// the whole chunk.  Per block and wave: 2 queries x 4 key groups of 16 x D / 32 steps
+// MFMAs.  (Two queries per wave leave 126 VGPRs, four waves per SIMD; four per wave needed
+// 244, two waves per SIMD, and ran 2-3 % slower.)  MFMA operand layout (16x16x32): lane l
+// holds A[l % 16][8 (l / 16) + j] and B[8 (l / 16) + j][l % 16] (j < 8), and
+// C[4 (l / 16) + i][l % 16] (i < 4); here A = the query's heads x head dims, B = head dims
+// x 16 keys, so C holds four heads of one key per lane.  The epilogue sums a lane's four
+// heads (w_h * max(0, c_h)) for each of its query's four key groups, then reduces over the
+// four 16-lane rows and transposes at once with three row swaps (v_permlane16_swap,
+// v_permlane32_swap: no LDS traffic), leaving in row r the totals of key group r -- the 64
+// consecutive keys of the block, one per lane, in a fixed order of additions, so the bits
+// do not depend on the schedule.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,17 +39,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = kHeadDim;               // head dimension (contraction length)
 constexpr int kH = kHeads;                 // heads (the MFMA's 16 rows)
 constexpr int kSteps = kD / 32;            // MFMA steps over the head dimension
-constexpr int kQPerWave = 4;
-constexpr int kWaves = 4;
+constexpr int kQPerWave = 2;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kQPerGroup = kQPerWave * kWaves;  // query rows per workgroup
 constexpr int kKeyBlock = 64;              // keys per staged block (4 groups of 16)
 constexpr int kGroups = kKeyBlock / 16;
 // LDS bytes per staged key row: 32 bytes of padding keep the B-fragment reads free of bank
 // conflicts (16 bytes left one 4-cycle conflict per read; none measured with 32)
 constexpr int kRowBytes = kD * 2 + 32;
-constexpr int kChunksPerThread = kKeyBlock * kD * 2 / 16 / 256;  // 16-byte loads per thread per block
+constexpr int kChunksPerThread = kKeyBlock * kD * 2 / 16 / kThreads;  // 16-byte loads per thread per block
 static_assert(kH == 16, "one 16-row MFMA tile of heads");
-static_assert(kD % 32 == 0 && kChunksPerThread * 256 * 16 == kKeyBlock * kD * 2, "whole 16-byte loads");
+static_assert(kD % 32 == 0 && kChunksPerThread * kThreads * 16 == kKeyBlock * kD * 2, "whole 16-byte loads");
 
 constexpr int32_t kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9-family data format
 
@@ -63,7 +67,7 @@ __device__ __forceinline__ int32_t row_len(const IxParams& p, int64_t b) {
     return min(max(len, 0), p.max_len);
 }
 
-__global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
+__global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IxParams p) {
     __shared__ __align__(16) unsigned char stage[2][kKeyBlock * kRowBytes];
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t group = (int64_t)blockIdx.x / p.chunks;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
     auto load_block = [&](int32_t kb, uint4 (&dst)[kChunksPerThread]) {
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {
-            const int c = tid + 256 * i;  // 16-byte chunk: row c / (kD / 8), column c % (kD / 8)
+            const int c = tid + kThreads * i;  // 16-byte chunk: row c / (kD / 8), column c % (kD / 8)
             const int row = c / (kD / 8), col = c % (kD / 8);
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(krs, (row * kD + col * 8) * 2, kb * kD * 2, 0);
             dst[i] = make_uint4(v[0], v[1], v[2], v[3]);
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(IxParams p) {
     auto stage_block = [&](int buf, const uint4 (&src)[kChunksPerThread]) {
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {
-            const int c = tid + 256 * i;
+            const int c = tid + kThreads * i;
             const int row = c / (kD / 8), col = c % (kD / 8);
             *reinterpret_cast<uint4*>(stage[buf] + row * kRowBytes + col * 16) = src[i];
         }
@@ -198,7 +202,7 @@ hipError_t launch_indexer(IxParams p, int cus, hipStream_t stream) {
     const int64_t grid = groups * p.chunks;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(indexer_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(indexer_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
