@@ -27,6 +27,7 @@ DETK_WORKSPACE_UNSUPPORTED = (1 << 64) - 1  # SIZE_MAX: the configuration cannot
 DETK_SCRATCH_BYTES = 16 << 20  # the per-GPU scratch array behind topk_ragged_noalloc
 DETK_OK, DETK_ERR_INVALID_ARG, DETK_ERR_UNSUPPORTED, DETK_ERR_WORKSPACE, DETK_ERR_HIP = range(5)
 DETK_DEBUG_PATH, DETK_DEBUG_STAGING_CAP, DETK_DEBUG_MULTI_TILE, DETK_DEBUG_FAST, DETK_DEBUG_SMALL_BATCH = 1, 2, 3, 4, 5
+DETK_DEBUG_SPLIT_SAMPLES = 6
 DETK_INDEX_LOCAL, DETK_INDEX_OFFSET, DETK_INDEX_PAGE_TABLE = 0, 1, 2
 DETK_DTYPE_F32, DETK_DTYPE_F16, DETK_DTYPE_BF16 = 0, 1, 2
 

@@ -59,6 +59,7 @@ int g_stage_cap = -1;       // -1 default
 int g_multi_tile = 0;       // 0 default
 int g_fast = 1;             // 0 off, 1 on, 2 on with a pivot that always misses
 int g_small = 0;            // 0 by batch size, 1 never the small-batch shapes, 2 always
+int g_split_samples = 0;    // split rows: 0 by the candidate list's room, 1 always 8192, 2 always 4096
 
 template <int TILE, int KMAX, bool MULTI, int VB, bool WIDE = false>
 hipError_t prepare_kernel() {
@@ -227,7 +228,8 @@ int make_plan(const DeviceInfo& dev, int B, int k, int32_t max_len, Plan* pl) {
         {
             const double s = detk::kSplitSamples / 2, n = (double)max_len, m = (double)(k < max_len ? k : max_len);
             const double e = s * m / n, r = e + 3.5 * std::sqrt(e) + 4.0;
-            pl->half = r * n / s + 4.0 * n * std::sqrt(r) / s <= (double)cap;
+            pl->half = g_split_samples == 2 ||
+                       (g_split_samples == 0 && r * n / s + 4.0 * n * std::sqrt(r) / s <= (double)cap);
         }
         size_t off = 0;
         pl->off_ecnt = off;
@@ -540,6 +542,10 @@ int detk_debug_set(int what, int value) {
     case DETK_DEBUG_SMALL_BATCH:
         if (value < 0 || value > 2) return DETK_ERR_INVALID_ARG;
         g_small = value;
+        return DETK_OK;
+    case DETK_DEBUG_SPLIT_SAMPLES:
+        if (value < 0 || value > 2) return DETK_ERR_INVALID_ARG;
+        g_split_samples = value;
         return DETK_OK;
     default: return DETK_ERR_INVALID_ARG;
     }

@@ -274,6 +274,9 @@ int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream)
  *                                  takes the small-batch shapes: 1024 threads per
  *                                  one-workgroup row, pivot digits selected by every
  *                                  wave); 1 never; 2 always.
+ *   what = DETK_DEBUG_SPLIT_SAMPLES: 0 default (rows split over workgroups take 4096
+ *                                  samples when the candidate list has room for the
+ *                                  longest row, else 8192); 1 always 8192; 2 always 4096.
  * Returns DETK_OK or DETK_ERR_INVALID_ARG.
  */
 #define DETK_DEBUG_PATH 1
@@ -281,6 +284,7 @@ int detk_read_probe(const void* data, size_t bytes, uint32_t* out, void* stream)
 #define DETK_DEBUG_MULTI_TILE 3
 #define DETK_DEBUG_FAST 4
 #define DETK_DEBUG_SMALL_BATCH 5
+#define DETK_DEBUG_SPLIT_SAMPLES 6
 int detk_debug_set(int what, int value);
 
 #ifdef __cplusplus

@@ -55,8 +55,10 @@ def assert_same(gi, gv, oi, ov, what: str) -> None:
 
 
 @contextlib.contextmanager
-def debug_overrides(path=None, stage_cap=None, multi_tile=None, fast=None, small=None):
+def debug_overrides(path=None, stage_cap=None, multi_tile=None, fast=None, small=None, split_samples=None):
     try:
+        if split_samples is not None:
+            detk.debug_set(detk.DETK_DEBUG_SPLIT_SAMPLES, split_samples)
         if small is not None:
             detk.debug_set(detk.DETK_DEBUG_SMALL_BATCH, small)
         if fast is not None:
@@ -74,3 +76,4 @@ def debug_overrides(path=None, stage_cap=None, multi_tile=None, fast=None, small
         detk.debug_set(detk.DETK_DEBUG_MULTI_TILE, 0)
         detk.debug_set(detk.DETK_DEBUG_FAST, 1)
         detk.debug_set(detk.DETK_DEBUG_SMALL_BATCH, 0)
+        detk.debug_set(detk.DETK_DEBUG_SPLIT_SAMPLES, 0)

@@ -303,3 +303,29 @@ def test_plateau_buckets(dev, shape, fam):
     ns = (300, 1500, 2047, 2048) if whole else (4000, 9000, 16000)
     rows = [_plateau_family(rng, fam, n) for n in ns]
     _check(dev, _dense(rows, 2048, "plateau_" + fam), "plateau bucket %s/%s" % (fam, shape), **SHAPES[shape])
+
+@pytest.mark.parametrize("samples", [1, 2])
+@pytest.mark.parametrize("fam", ["mixture", "plateau_top", "negative", "nan_heavy", "narrow"])
+def test_split_row_sample_counts(dev, samples, fam):
+    """Rows split over workgroups with 8192 (1) or 4096 (2) row samples forced, whatever the
+    candidate list's room: the pivot only steers, so both give the oracle's output, also
+    where the smaller sample overflows the list and the row falls back."""
+    rng = np.random.default_rng(len(fam) * 7 + samples)
+    def row(n):
+        if fam == "mixture":
+            return W.relu_sum_mixture(rng, n, 0.6)
+        if fam == "plateau_top":  # a long run of the top key
+            r = rng.standard_normal(n).astype(np.float32)
+            r[rng.choice(n, 3000, replace=False)] = np.float32(5.0)
+            return r
+        if fam == "negative":
+            return (-np.abs(rng.standard_normal(n)) - 1.0).astype(np.float32)
+        if fam == "nan_heavy":
+            r = rng.standard_normal(n).astype(np.float32)
+            r.view(np.uint32)[rng.random(n) < 0.01] = np.uint32(0x7FC00001)
+            return r
+        u = (np.uint32(0x3F800000) | rng.integers(0, 8192, n).astype(np.uint32))
+        return u.view(np.float32)
+    rows = [row(n) for n in (40000, 70000, 150000)]
+    _check(dev, _dense(rows, 2048, "split_samples_" + fam), "split-row samples %d/%s" % (samples, fam),
+           split_samples=samples)
