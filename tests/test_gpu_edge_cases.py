@@ -279,6 +279,17 @@ def _plateau_family(rng, fam, n):
         r[z[rng.random(z.size) < 0.5]] = np.float32(-0.0)
         r[rng.random(n) < 0.05] = np.float32(-2.0)
         return r
+    if fam in ("others_at_limit", "others_past_limit"):  # whole row: X = 1.0 with exactly 128
+        # (or 129) keys within 3 ulps of it but not equal, the ranking limit of the others
+        r = np.full(n, np.float32(1.0), np.float32)
+        cnt = 128 if fam == "others_at_limit" else 129
+        pos = 1 + rng.choice(n - 1, size=cnt + 2, replace=False)  # position 0 keeps X
+        u = r.view(np.uint32)
+        step = rng.integers(1, 4, cnt) * rng.choice(np.array([-1, 1]), cnt)
+        u[pos[:cnt]] = (np.int64(0x3F800000) + step).astype(np.uint32)
+        r[pos[cnt]] = np.float32(-100.0)
+        r[pos[cnt + 1]] = np.float32(100.0)
+        return r
     if fam == "kept_plateau":  # longer than k: a plateau of 1,500 at 3.0 inside the top k
         r = rng.standard_normal(n).astype(np.float32)
         r[rng.choice(n, 1500, replace=False)] = np.float32(3.0)
@@ -291,7 +302,7 @@ def _plateau_family(rng, fam, n):
 
 @pytest.mark.parametrize("shape", sorted(SHAPES))
 @pytest.mark.parametrize("fam", ["zero_above_specials", "one_above_gauss", "minority_first", "two_zeros",
-                                 "kept_plateau", "straddling_plateau"])
+                                 "others_at_limit", "others_past_limit", "kept_plateau", "straddling_plateau"])
 def test_plateau_buckets(dev, shape, fam):
     """One key repeated on a long run of a kept bucket: those elements are placed by position
     instead of ranked, the bucket's other keys ranked among themselves around them (or, when
@@ -301,6 +312,8 @@ def test_plateau_buckets(dev, shape, fam):
     rng = np.random.default_rng(len(fam) * 17 + len(shape))
     whole = fam not in ("kept_plateau", "straddling_plateau")
     ns = (300, 1500, 2047, 2048) if whole else (4000, 9000, 16000)
+    if fam.startswith("others_"):
+        ns = (1500, 2048)
     rows = [_plateau_family(rng, fam, n) for n in ns]
     _check(dev, _dense(rows, 2048, "plateau_" + fam), "plateau bucket %s/%s" % (fam, shape), **SHAPES[shape])
 
