@@ -94,6 +94,34 @@ def test_scores_within_bound(dev, case):
         assert np.all(np.isnan(got[b, n:])), (case, b)
 
 
+# Batches whose launch takes the middle key-chunk sizes (the chunk halves from 16384 while
+# fewer than 512 workgroups would fill the GPU's 256 CUs twice; a workgroup serves 16 query
+# rows): 65, 129 and 257 row groups over 16,384 keys take 2048-, 4096- and 8192-key chunks,
+# each with a partial last group.
+CHUNK_CASES = {"chunk2048_1030": 1030, "chunk4096_2050": 2050, "chunk8192_4100": 4100}
+
+
+@pytest.mark.parametrize("case", sorted(CHUNK_CASES))
+def test_middle_chunk_sizes(dev, case):
+    import torch
+    B = CHUNK_CASES[case]
+    inp = W.indexer_causal(Q=B, ctx=16384, name="ix_" + case)
+    rows = sorted(set([0, 1, 15, 16, B // 2, (B // 16) * 16 - 1, (B // 16) * 16, B - 2, B - 1]
+                      + list(np.linspace(0, B - 1, 6).astype(int))))
+    log("indexer scores %s: B=%d max_len=%d, %d sampled rows" % (case, B, inp.max_len, len(rows)))
+    q, w, k, ln = _dev(inp, dev)
+    out = torch.full((inp.B, inp.max_len), float("nan"), device=dev)
+    detk.indexer_scores(q, w, k, ln, inp.max_len, out=out)
+    torch.cuda.synchronize()
+    got = out[torch.tensor(rows, device=dev)].cpu().numpy()
+    full = np.full((inp.B, inp.max_len), np.nan, np.float32)
+    full[rows] = got
+    _check_scores(inp, full, rows, case)
+    for b in rows:
+        n = int(min(max(int(inp.lengths[b]), 0), inp.max_len))
+        assert np.all(np.isnan(full[b, n:])), (case, b)
+
+
 def test_default_windows_and_repeat_bits(dev):
     import torch
     inp = W.indexer_causal(Q=33, ctx=2500, name="ix_d")
